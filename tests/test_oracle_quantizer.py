@@ -1,0 +1,134 @@
+"""Pins for the oracle's quantizers and packed format (CPU only).
+
+Each test checks the oracle against something other than its own formula:
+values printed on the pages, closed forms, or brute force.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import asym_params, asym_quantize, sym_params, sym_quantize
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_worked_example_int8_symmetric_codes():
+    """Worked example 1 of "Quantization (INT8, INT4, GPTQ)"."""
+    ex = _load("worked_example_int8_symmetric.json")
+    w = np.array(ex["w"])
+    s, _ = sym_params(np.max(np.abs(w)), ex["bits"])
+    assert s == pytest.approx(ex["scale_exact_num"] / ex["scale_exact_den"], rel=1e-15)
+    assert round(float(s), 5) == ex["scale_printed"]
+    q, what = sym_quantize(w, s, ex["bits"])
+    assert q.astype(int).tolist() == ex["q"]
+    # the page's w/s line is printed to one decimal (truncated)
+    np.testing.assert_allclose(w / s, ex["w_over_s_printed"], atol=0.1)
+    # the printed dequantized values use the rounded scale
+    _, what_printed = sym_quantize(w, ex["scale_printed"], ex["bits"])
+    half_ulp = 0.5 * 10.0 ** -np.array(ex["w_hat_printed_decimals"]) + 1e-12
+    assert np.all(np.abs(what_printed - ex["w_hat_printed"]) <= half_ulp)
+    # "≈" error line: within the page's rounding of the exact-scale errors
+    np.testing.assert_allclose(np.abs(w - what), ex["abs_err_printed_approx"], atol=5e-4)
+
+
+def test_worked_example_through_unsigned_storage():
+    """Symmetric codes stored unsigned with offset 2ᵇ⁻¹ give the same values."""
+    ex = _load("worked_example_int8_symmetric.json")
+    w = np.array(ex["w"])
+    s, z = sym_params(np.max(np.abs(w)), 8)
+    _, qu, what = asym_quantize(w, s, z, 8)
+    assert (qu - z).astype(int).tolist() == ex["q"]
+    np.testing.assert_allclose(what, s * np.array(ex["q"]), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_affine_endpoints_closed_form(bits):
+    """Deriving the scale and zero-point: x_min = s(q_min − z), x_max = s(q_max − z)
+    when −x_min/s is an integer; the extremes map to codes 0 and 2ᵇ−1."""
+    maxq = (1 << bits) - 1
+    for z0 in [0, 1, maxq // 2, maxq]:
+        step = 0.0078125  # power of two: every quantity below is exact
+        mn, mx = -z0 * step, (maxq - z0) * step
+        s, z, zraw = asym_params(mn, mx, bits)
+        assert s == step and z == z0 and zraw == z0
+        assert mn == s * (0 - z) and mx == s * (maxq - z)
+        _, q, what = asym_quantize(np.array([mn, mx]), s, z, bits)
+        assert q.tolist() == [0, maxq]
+        assert what.tolist() == [mn, mx]
+
+
+@pytest.mark.parametrize("c", [0.37, -0.21, 0.0])
+def test_constant_group_reconstructs_exactly(c):
+    for bits in (3, 4):
+        s, z, _ = asym_params(c, c, bits)
+        _, q, what = asym_quantize(np.array([c, c]), s, z, bits)
+        assert np.all(what == c)
+        assert 0 <= z <= (1 << bits) - 1
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_rounding_is_nearest_grid_point(bits, rng):
+    """Brute force over the whole grid: the code chosen is the nearest grid
+    point (ties aside), z inside the round, clamped at the edges."""
+    maxq = (1 << bits) - 1
+    for _ in range(50):
+        w = rng.normal(size=32) * rng.uniform(0.01, 1)
+        s, z, _ = asym_params(w.min(), w.max(), bits)
+        v, q, what = asym_quantize(w, s, z, bits)
+        grid = s * (np.arange(maxq + 1) - z)
+        best = np.argmin(np.abs(w[:, None] - grid[None, :]), axis=1)
+        assert np.array_equal(q.astype(int), best)
+        inside = (q > 0) & (q < maxq)
+        assert np.all(np.abs(w - what)[inside] <= s / 2 * (1 + 1e-12))
+
+
+def test_zero_is_representable_and_zero_point_rounded(rng):
+    """'The zero-point must itself be a valid integer so that 0 maps exactly.'"""
+    for bits in (3, 4):
+        for _ in range(20):
+            w = rng.normal(size=64)
+            s, z, _ = asym_params(w.min(), w.max(), bits)
+            assert z == np.round(z)
+            _, _, what0 = asym_quantize(np.array([0.0]), s, z, bits)
+            assert what0[0] == 0.0
+
+
+def test_rtn_grouped_matches_per_group_brute_force(rng):
+    W = rng.normal(size=(6, 300)) * 0.02
+    q, S, Z, what = oracle.rtn_grouped(W, 4, 128)
+    assert S.shape == (6, 3)
+    for gi, (c0, c1) in enumerate([(0, 128), (128, 256), (256, 300)]):
+        blk = W[:, c0:c1]
+        np.testing.assert_allclose(S[:, gi], (blk.max(1) - blk.min(1)) / 15, rtol=1e-15)
+        grid = S[:, gi:gi + 1, None] * (np.arange(16)[None, None, :] - Z[:, gi:gi + 1, None])
+        best = np.argmin(np.abs(blk[:, :, None] - grid), axis=2)
+        assert np.array_equal(q[:, c0:c1], best)
+
+
+def test_pack_known_words():
+    """Eight 4-bit codes per 32-bit word, column 8k+i in nibble i."""
+    q = np.array([[0, 1, 2, 3, 4, 5, 6, 7, 15, 0, 0, 0, 0, 0, 0, 9, 3]], dtype=np.uint8)
+    w = oracle.pack_codes(q)
+    assert w.shape == (1, 3)
+    assert int(w[0, 0]) == 0x76543210
+    assert int(w[0, 1]) == 0x9000000F
+    assert int(w[0, 2]) == 0x3
+
+
+def test_pack_roundtrip(rng):
+    for d in (1, 7, 8, 9, 129, 4096):
+        q = rng.integers(0, 16, size=(5, d)).astype(np.uint8)
+        assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(q), d), q)
+
+
+def test_bit_rate_matches_page():
+    ex = _load("bit_rate.json")
+    assert oracle.bits_per_weight(ex["bits"], ex["group_size"]) == ex["bits_per_weight"]
