@@ -1,0 +1,174 @@
+"""Shared pieces of the GPU parity tests: run the HIP path through the C ABI
+and compare it with the fp64 oracle on the same seeded inputs.
+
+Acceptance (per the target statement of this path):
+  * H and U within 1e-3 relative Frobenius error;
+  * codes: follow-mode comparison (the oracle re-runs its sweep, adopting the
+    GPU's code or zero-point wherever they differ, and classifies each
+    adoption) -- no hard flips, and at least 99.9 % of codes identical; a flip
+    is allowed only where the oracle's pre-round value lies within 1e-4 code
+    units of the rounding boundary between the two codes;
+  * scales within 1e-5 relative (max over groups);
+  * layer output error ‖WX − ŴX‖²_F within 1 % of the oracle's.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import oracle
+import synth
+
+H_TOL = 1e-3
+U_TOL = 1e-3
+TIE_TOL = 1e-4
+MIN_IDENTICAL = 0.999
+SCALE_TOL = 1e-5
+LOSS_TOL = 0.01
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def gq():
+    import post_weight_quantization_16_amd as m
+    return m
+
+
+def to_dev(arr, dtype: str):
+    torch = torch_mod()
+    arr = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.float16)
+    else:
+        t = torch.from_numpy(arr.astype(np.float32, copy=False))
+    return t.cuda()
+
+
+def rel_fro(a, b) -> float:
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+def params_of(wl: synth.Workload, **kw):
+    g = gq()
+    d = dict(bits=wl.bits, group_size=wl.group_size, block_size=wl.block_size,
+             percdamp=wl.percdamp, act_order=wl.act_order, sym=wl.sym)
+    d.update(kw)
+    return g.GPTQParams(**d), oracle.Params(**d)
+
+
+def run_gpu(W, w_dtype, X, x_dtype, gparams, H_in=None, U_in=None, perm_in=None):
+    """Run the three calls; returns numpy copies of every output.
+
+    H_in (fp64 numpy) replaces the GPU Hessian when given (stage isolation);
+    U_in (+ perm_in) replaces the GPU prepare output for the sweep.
+    """
+    torch = torch_mod()
+    g = gq()
+    Wd = to_dev(W, w_dtype)
+    m, d = W.shape
+    out = {}
+    if H_in is None:
+        H = torch.zeros(d, d, dtype=torch.float32, device="cuda")
+        g.hessian_accumulate(H, to_dev(X, x_dtype))
+        torch.cuda.synchronize()
+        out["H"] = H.cpu().numpy().astype(np.float64)
+    else:
+        H = torch.from_numpy(H_in.astype(np.float32)).cuda()
+        out["H"] = H_in
+    if U_in is None:
+        prep = g.prepare_hinv(H, gparams)
+        out["Hd"] = H.cpu().numpy().astype(np.float64)
+    else:
+        U = torch.from_numpy(np.ascontiguousarray(U_in, dtype=np.float32)).cuda()
+        pm = perm_in if perm_in is not None else np.arange(d)
+        prep = g.Prepared(U, torch.from_numpy(pm.astype(np.int32)).cuda(),
+                          torch.zeros(d, dtype=torch.uint8, device="cuda"))
+    q = g.quantize_layer(Wd, prep, gparams)
+    torch.cuda.synchronize()
+    out.update(
+        U=prep.U.cpu().numpy().astype(np.float64), perm=prep.perm.cpu().numpy().astype(np.int64),
+        dead=prep.dead.cpu().numpy().astype(bool),
+        qweight=q.qweight.cpu().numpy().view(np.uint32), scales=q.scales.cpu().numpy(),
+        zeros=q.zeros.cpu().numpy(), what=q.W_hat.cpu().numpy().astype(np.float64),
+        g_idx=q.g_idx.cpu().numpy(), row_loss=q.row_loss.cpu().numpy())
+    if gparams.bits <= 4:
+        out["codes"] = oracle.unpack_codes(out["qweight"], d)
+    else:
+        w = out["qweight"]
+        c = np.zeros((m, w.shape[1] * 4), np.uint8)
+        for i in range(4):
+            c[:, i::4] = (w >> np.uint32(8 * i)) & np.uint32(0xFF)
+        out["codes"] = c[:, :d]
+    return out
+
+
+def check_perm(gpu_perm, H_exact, dead_tol=1e-5):
+    """The GPU's act-order must be a descending order of the exact diagonal up
+    to fp32 rounding of near-equal entries; returns #positions differing from
+    the oracle's own order."""
+    d = H_exact.shape[0]
+    assert sorted(gpu_perm.tolist()) == list(range(d)), "perm is not a permutation"
+    diag = np.diag(oracle.dead_fix(H_exact)[0])
+    dp = diag[gpu_perm]
+    viol = dp[1:] > dp[:-1] * (1 + dead_tol) + 1e-30
+    assert not np.any(viol), f"perm breaks descending order at {np.nonzero(viol)[0][:5]}"
+    own = oracle.act_order_perm(diag)
+    return int(np.sum(own != gpu_perm))
+
+
+def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, check_u=True,
+                  perm_follow=True):
+    """Full comparison; returns a dict of measured figures and asserts the bar."""
+    t0 = time.time()
+    rep = {"label": label}
+    d = W.shape[1]
+    if check_h:
+        rep["H_rel"] = rel_fro(gpu["H"], H_exact)
+        assert rep["H_rel"] <= H_TOL, rep
+        assert np.array_equal(gpu["H"], gpu["H"].T), "H is not exactly symmetric"
+    perm = None
+    if oparams.act_order:
+        rep["perm_diff_positions"] = check_perm(gpu["perm"], H_exact)
+        perm = gpu["perm"] if perm_follow else None
+    ora = oracle.gptq_layer(W, H_exact, oparams, w_dtype=w_dtype, perm=perm,
+                            follow={"q": gpu["codes"], "z": gpu["zeros"].astype(np.float64)},
+                            tie_tol=TIE_TOL)
+    if check_u:
+        rep["U_rel"] = rel_fro(gpu["U"], ora["U"])
+        assert rep["U_rel"] <= U_TOL, rep
+    r = ora["report"]
+    rep.update(code_allowed=r.code_allowed, code_hard=r.code_hard, zero_allowed=r.zero_allowed,
+               zero_hard=r.zero_hard, frac_identical=r.frac_codes_identical,
+               max_tie_dist=r.max_tie_dist)
+    rep["free_run_identical"] = float(np.mean(
+        oracle.gptq_layer(W, H_exact, oparams, w_dtype=w_dtype, perm=perm)["q"] == gpu["codes"]))
+    assert r.ok, (rep, r.hard_examples[:5])
+    assert r.frac_codes_identical >= MIN_IDENTICAL, rep
+    s_rel = np.abs(gpu["scales"] - ora["s"]) / np.abs(ora["s"])
+    rep["scale_rel_max"] = float(s_rel.max())
+    assert rep["scale_rel_max"] <= SCALE_TOL, rep
+    assert np.array_equal(gpu["zeros"], ora["z"].astype(np.uint8))
+    e_gpu = oracle.layer_error(ora["W"], gpu["what"], H_exact)
+    e_ora = oracle.layer_error(ora["W"], ora["what"], H_exact)
+    rep["layer_err_gpu"], rep["layer_err_oracle"] = e_gpu, e_ora
+    rep["layer_err_rel"] = abs(e_gpu - e_ora) / e_ora
+    assert rep["layer_err_rel"] <= LOSS_TOL, rep
+    assert np.array_equal(gpu["g_idx"], ora["g_idx"])
+    assert np.array_equal(gpu["dead"], ora["dead"]) or not check_u
+    rep["what_max_abs_diff"] = float(np.max(np.abs(gpu["what"] - ora["what"])))
+    rep["row_loss_rel"] = float(np.max(np.abs(gpu["row_loss"] - ora["row_loss"]) /
+                                       np.maximum(ora["row_loss"], 1e-30)))
+    rep["oracle_s"] = round(time.time() - t0, 2)
+    log("PARITY", rep)
+    return rep
