@@ -48,8 +48,12 @@ inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 // tri: 0 full, 1 only n <= m is written (lower), 2 only n >= m (upper); tiles
 // entirely outside the triangle are skipped.  k_last: K of the last batch
 // (split-K over one long dimension), or K when all batches are equal.
+// k_from_n: op(B) is lower triangular (B(k,n) = 0 for k < n), so a tile at
+// column n0 starts its K loop at n0.  k_to_m: op(A) is lower triangular
+// (A(m,k) = 0 for k > m), so a tile at row m0 stops at m0 + 128.
 struct GemmArgs {
   int M, N, K, k_last, batch;
+  int k_from_n, k_to_m;
   float alpha, beta;
   const float* A; int64_t lda, strideA; bool trans_a;
   const float* B; int64_t ldb, strideB; bool trans_b;

@@ -16,6 +16,7 @@ constexpr int LDS_STRIDE = TM + 32;  // row k+1 lands 32 banks after row k
 
 struct KArgs {
   int M, N, K, k_last;
+  int k_from_n, k_to_m;
   float alpha, beta;
   const float* A; int64_t lda, strideA;
   const float* B; int64_t ldb, strideB;
@@ -84,7 +85,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g) {
   if (g.tri == 1 && n0 > m0 + TM - 1) return;
   if (g.tri == 2 && n0 + TN - 1 < m0) return;
   const int z = blockIdx.z;
-  const int K = (z == (int)gridDim.z - 1) ? g.k_last : g.K;
+  const int Kz = (z == (int)gridDim.z - 1) ? g.k_last : g.K;
+  const int kbeg = g.k_from_n ? (n0 / TK) * TK : 0;
+  const int K = g.k_to_m ? min(Kz, m0 + TM) : Kz;
   const float* A = g.A + (int64_t)z * g.strideA;
   const float* B = g.B + (int64_t)z * g.strideB;
   float* C = g.C + (int64_t)z * g.strideC;
@@ -110,13 +113,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   f32x4 ra[2], rb[2];
-  load_chunk<TA>(Ab, g.lda, mvalid, 0, K, t, g.vec_a, ra);
-  load_chunk<!TB>(Bb, g.ldb, nvalid, 0, K, t, g.vec_b, rb);
+  load_chunk<TA>(Ab, g.lda, mvalid, kbeg, K, t, g.vec_a, ra);
+  load_chunk<!TB>(Bb, g.ldb, nvalid, kbeg, K, t, g.vec_b, rb);
   store_chunk<TA>(As, t, ra);
   store_chunk<!TB>(Bs, t, rb);
   __syncthreads();
 
-  for (int k0 = 0; k0 < K; k0 += TK) {
+  for (int k0 = kbeg; k0 < K; k0 += TK) {
     const bool more = k0 + TK < K;
     if (more) {
       load_chunk<TA>(Ab, g.lda, mvalid, k0 + TK, K, t, g.vec_a, ra);
@@ -167,6 +170,7 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
   KArgs k;
   k.M = a.M; k.N = a.N; k.K = a.K; k.k_last = a.k_last;
+  k.k_from_n = a.k_from_n; k.k_to_m = a.k_to_m;
   k.alpha = a.alpha; k.beta = a.beta;
   k.A = a.A; k.lda = a.lda; k.strideA = a.strideA;
   k.B = a.B; k.ldb = a.ldb; k.strideB = a.strideB;

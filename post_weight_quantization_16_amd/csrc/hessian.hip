@@ -2,20 +2,24 @@
 // ...", Second-Order Taylor Expansion and the Hessian: H = 2XXᵀ with the
 // page's X = d x N).
 //
-// Only the upper-triangle 128x128 tiles are computed (SYRK: d(d+1)N flops).
-// The token axis is split S ways; each (tile, split) workgroup writes its
-// fp32 partial tile, and a reduction kernel adds 2·Σ_s partial_s into both
-// triangles of H in a fixed order (deterministic, exactly symmetric).
+// Only upper-triangle tiles are computed (SYRK: d(d+1)N flops).  The token
+// axis is split S >= 1 ways; each (tile, split) workgroup writes an fp32
+// partial tile and a reduction adds 2·Σ_s partial_s into H's upper triangle
+// in a fixed order.  A final
+// LDS-tiled transpose copies the upper triangle into the lower one, so H is
+// exactly symmetric and the result is deterministic.
 //
-// bf16/fp16 path: v_mfma_f32_32x32x16_{bf16,f16}; the products are exact in
-// fp32 and accumulate in fp32.  The MFMA operand layout wants 8 consecutive
-// tokens of one column per lane, while X is contiguous along columns, so each
-// thread loads an 8-token x 8-column block (eight 16-byte loads), transposes it
-// in registers and stores eight 16-byte column runs into LDS ([col][token]
-// layout, rows padded to 72 halves so both the stores and the MFMA operand
-// reads are bank-conflict free).
-//
-// fp32 path: the generic fp32 MFMA GEMM on op(A) = Xᵀ, op(B) = X.
+// bf16/fp16 inputs: v_mfma_f32_32x32x16_{bf16,f16}; the products are exact in
+// fp32 and accumulate in fp32.  The MFMA operand wants 8 consecutive tokens of
+// one column per lane while X is contiguous along columns:
+//   fast path (d, ld multiples of 8, X 16-byte aligned): 256x256 tiles, X kept
+//     in natural layout in LDS and read with LDS transpose loads;
+//   generic path: 128x128 tiles; each thread loads an 8-token x 8-column block,
+//     transposes it in registers and stores [col][token] runs into LDS.
+// fp32 inputs: the generic fp32 MFMA GEMM on op(A) = Xᵀ, op(B) = X.
+#include <algorithm>
+#include <cmath>
+
 #include "common.hpp"
 
 namespace gq {
@@ -49,7 +53,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void syrk16_kernel(const uint16_t* __restrict__ X, int64_t ld,
+__global__ __launch_bounds__(256) void syrk16_generic_kernel(const uint16_t* __restrict__ X, int64_t ld,
                                                      int d, int64_t n_tok, int64_t chunk, int nt,
                                                      float* __restrict__ P, int64_t dp, int vec) {
   int ti, tj;
@@ -160,7 +164,169 @@ __global__ __launch_bounds__(256) void syrk16_kernel(const uint16_t* __restrict_
       }
 }
 
-// H[i][j] += 2·Σ_s P_s[i][j] for i <= j, mirrored to H[j][i].
+// ---------------------------------------------------------------- fast path
+// 256x256 output tiles, 4 waves each owning a 128x128 block (4x4 tiles of
+// v_mfma_f32_32x32x16).  X stays in its natural [token][column] layout in LDS:
+// 64 tokens per stage, rows of 512 bytes whose 16-byte chunks are XOR-swizzled
+// by (row & 3) << 2.  MFMA operands (8 consecutive tokens of one column per
+// lane) come from two ds_read_b64_tr_b16 each: in every group of 16 lanes,
+// lane i receives element i%4 of the 8-byte piece addressed by lane 4r + i/4
+// (r = 0..3), so lanes addressing 4 rows x 16 columns get one column each.
+// With the swizzle, the 4 rows x 64 bytes a half-wave reads hit 64 distinct
+// banks.  The next stage is fetched into registers during the MFMAs.
+// Requires d % 8 == 0, ld % 8 == 0 and a 16-byte aligned X.
+constexpr int FT = 256;                 // output tile
+constexpr int FK = 64;                  // tokens per stage
+constexpr int FROW = FT * 2;            // bytes per LDS row (one token)
+constexpr int FOP = FK * FROW;          // bytes per operand per stage (32 KB)
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ int fswz(int row) { return (row & 3) << 2; }
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict__ X, int64_t ld,
+                                                      int d, int64_t n_tok, int64_t chunk, int nt,
+                                                      float* __restrict__ P, int64_t dp) {
+  int ti, tj;
+  tile_of(blockIdx.x, nt, ti, tj);
+  const int split = blockIdx.y;
+  const int64_t t_begin = (int64_t)split * chunk;
+  const int64_t t_end = min(n_tok, t_begin + chunk);
+
+  __shared__ __attribute__((aligned(16))) char S[2 * FOP];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // loader: chunk idx = t + 256*i, i < 8: operand, row, 16-byte chunk
+  constexpr int NLD = 2 * FK * (FROW / 16) / 256;
+  u32x4 stg[NLD];
+  const int col_a = ti * FT, col_b = tj * FT;
+  // Every load reads an in-bounds address (token and column clamped into the
+  // matrix) and out-of-range chunks are zeroed with a select: predicated
+  // loads here would push the staging registers into scratch.
+  auto gload = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = t + 256 * i;
+      const int op = idx / (FK * 32), row = (idx >> 5) % FK, ch = idx & 31;
+      const int col = (op ? col_b : col_a) + ch * 8;
+      const int64_t tok = t0 + row;
+      const bool ok = tok < t_end && col < d;
+      const int64_t tk = ok ? tok : t_begin;
+      const int cc = ok ? col : 0;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(X + tk * ld + cc);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      stg[i] = ok ? v : zero;
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = t + 256 * i;
+      const int op = idx / (FK * 32), row = (idx >> 5) % FK, ch = idx & 31;
+      *reinterpret_cast<u32x4*>(S + op * FOP + row * FROW + ((ch ^ fswz(row)) << 4)) = stg[i];
+    }
+  };
+
+  // per-lane tr-read coordinates
+  const int g = lane >> 4, j16 = lane & 15;
+  const int rsub = 8 * (g >> 1) + (j16 >> 2);     // + ks*16 + 4h
+  const int csub = 16 * (g & 1) + 4 * (j16 & 3);  // + fragment column base
+  const char* SA = S;
+  const char* SB = S + FOP;
+
+  auto frag = [&](const char* base, int colbase, int ks) {
+    s16x4 lo, hi;
+    {
+      const int row = ks * 16 + rsub, col = colbase + csub;
+      const int off = row * FROW + (((col >> 3) ^ fswz(row)) << 4) + ((col & 7) << 1);
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+    }
+    {
+      const int row = ks * 16 + 4 + rsub, col = colbase + csub;
+      const int off = row * FROW + (((col >> 3) ^ fswz(row)) << 4) + ((col & 7) << 1);
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+    }
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return v;
+  };
+
+  gload(t_begin);
+  lstore();
+  __syncthreads();
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += FK) {
+    gload(t0 + FK);  // past the end this loads zeros; no branch around it
+#pragma unroll
+    for (int ks = 0; ks < FK / 16; ++ks) {
+      typedef __attribute__((ext_vector_type(8))) short s16x8;
+      asm volatile("" ::: "memory");  // one sub-step's operand reads at a time
+      s16x8 a[4], b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        a[f] = frag(SA, wm * 128 + f * 32, ks);
+        b[f] = frag(SB, wn * 128 + f * 32, ks);
+      }
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 4; ++fj) {
+          if constexpr (BF16)
+            acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[fi]), __builtin_bit_cast(bf16x8, b[fj]), acc[fi][fj], 0, 0, 0);
+          else
+            acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, a[fi]), __builtin_bit_cast(f16x8, b[fj]), acc[fi][fj], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    lstore();
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32 of each 32x32 tile
+#pragma unroll
+  for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = ti * FT + wm * 128 + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int cl = tj * FT + wn * 128 + fj * 32 + (lane & 31);
+        P[(int64_t)split * dp * dp + (int64_t)row * dp + cl] = acc[fi][fj][r];
+      }
+}
+
+// H[j][i] = H[i][j] for i < j: 64x64 tiles of the upper triangle through LDS.
+__global__ __launch_bounds__(256) void mirror_kernel(float* __restrict__ H, int d, int nb) {
+  int bi, bj;
+  tile_of(blockIdx.x, nb, bi, bj);
+  __shared__ float Tl[64][65];
+  const int t = threadIdx.x;
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int a = e >> 6, b = e & 63;
+    const int i = bi * 64 + a, j = bj * 64 + b;
+    Tl[a][b] = (i < d && j < d) ? H[(int64_t)i * d + j] : 0.f;
+  }
+  __syncthreads();
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int b = e >> 6, a = e & 63;   // write row j = bj*64+b, column i = bi*64+a
+    const int i = bi * 64 + a, j = bj * 64 + b;
+    if (i < d && j < d && i < j) H[(int64_t)j * d + i] = Tl[a][b];
+  }
+}
+
+// H[i][j] += 2·Σ_s P_s[i][j] for i <= j (the mirror kernel fills i > j).
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ H, int d,
                                                           const float* __restrict__ P, int64_t dp,
                                                           int splits, int nt) {
@@ -173,15 +339,18 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ H,
     if (i >= d || j >= d) continue;
     float v = 0.f;
     for (int s = 0; s < splits; ++s) v += P[(int64_t)s * dp * dp + (int64_t)i * dp + j];
-    v *= 2.f;
-    H[(int64_t)i * d + j] += v;
-    if (i != j) H[(int64_t)j * d + i] += v;
+    H[(int64_t)i * d + j] += 2.f * v;
   }
 }
 
 }  // namespace
 
-int hessian_splits(int64_t d, int64_t n_tok) {
+namespace {
+
+constexpr int kCUs = 256;  // MI355X compute units (one fast-path workgroup each)
+
+// Splits for the generic 128-tile kernel and the fp32 path.
+int generic_splits(int64_t d, int64_t n_tok) {
   const int64_t nt = ceil_div(d, HT);
   const int64_t tiles = nt * (nt + 1) / 2;
   int64_t s = ceil_div(2048, tiles);
@@ -192,43 +361,92 @@ int hessian_splits(int64_t d, int64_t n_tok) {
   return (int)ceil_div(std::max<int64_t>(n_tok, 1), chunk);
 }
 
+// Splits for the 256-tile kernel: minimise the modelled time of
+// ceil(tiles·S / CUs) rounds of 1/S of a tile's work, plus writing and
+// reading S partial Hessians.
+int fast_splits(int64_t d, int64_t n_tok) {
+  const int64_t nt = ceil_div(d, FT);
+  const double tiles = (double)(nt * (nt + 1) / 2);
+  const double dp = (double)(nt * FT);
+  const double t_tile = 2.0 * FT * FT * (double)n_tok / (1.5e15 / kCUs);
+  const double t_byte = 1.0 / 8e12;
+  int best = 1;
+  double best_t = 1e300;
+  for (int S = 1; S <= 32; ++S) {
+    if (S > 1 && ceil_div(n_tok, S) < 4 * FK) break;
+    const double rounds = std::ceil(tiles * S / kCUs);
+    const double t = rounds * t_tile / S + 2.0 * S * dp * dp * 4 * t_byte;
+    if (t < best_t * 0.98) { best_t = t; best = S; }
+  }
+  const int64_t chunk = ceil_div(ceil_div(n_tok, best), FK) * FK;
+  return (int)ceil_div(n_tok, chunk);
+}
+
+}  // namespace
+
+int hessian_splits(int64_t d, int64_t n_tok) { return fast_splits(d, n_tok); }
+
 size_t hessian_ws_bytes(int64_t d, int64_t n_tok) {
-  const int64_t dp = ceil_div(d, HT) * HT;
-  return align_up((size_t)hessian_splits(d, n_tok) * dp * dp * sizeof(float));
+  const int64_t dpg = ceil_div(d, FT) * FT;
+  const size_t fast = (size_t)fast_splits(d, n_tok) * dpg * dpg * sizeof(float);
+  const size_t gen = (size_t)generic_splits(d, n_tok) * dpg * dpg * sizeof(float);
+  return align_up(std::max<size_t>(std::max(fast, gen), 256));
 }
 
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
                           int64_t ld_x, void* ws, hipStream_t s) {
   if (n_tok <= 0) return hipSuccess;
-  const int nt = (int)ceil_div(d, HT);
-  const int64_t dp = (int64_t)nt * HT;
-  const int tiles = nt * (nt + 1) / 2;
-  const int splits = hessian_splits(d, n_tok);
-  const int64_t chunk = ceil_div(ceil_div(n_tok, splits), HK) * HK;
+  const int64_t dp = ceil_div(d, FT) * FT;   // partial Hessians are dp x dp
   float* P = static_cast<float*>(ws);
-  if (x_dtype == GPTQ_F32) {
-    GemmArgs g{};
-    g.M = (int)d; g.N = (int)d;
-    g.K = (int)chunk; g.k_last = (int)(n_tok - (int64_t)(splits - 1) * chunk);
-    g.batch = splits; g.alpha = 1.f; g.beta = 0.f;
-    g.A = static_cast<const float*>(X); g.lda = ld_x; g.strideA = chunk * ld_x; g.trans_a = true;
-    g.B = static_cast<const float*>(X); g.ldb = ld_x; g.strideB = chunk * ld_x; g.trans_b = false;
-    g.C = P; g.ldc = dp; g.strideC = dp * dp; g.tri = 2;
-    hipError_t e = gemm_f32(g, s);
-    if (e != hipSuccess) return e;
-  } else {
-    const int vec = ((uintptr_t)X % 16 == 0) && (ld_x % 8 == 0);
+  hipError_t e;
+  const bool fast = x_dtype != GPTQ_F32 && d % 8 == 0 && ld_x % 8 == 0 && (uintptr_t)X % 16 == 0;
+  int splits;
+  if (fast) {
+    const int nt = (int)ceil_div(d, FT);
+    const int tiles = nt * (nt + 1) / 2;
+    splits = fast_splits(d, n_tok);
+    const int64_t chunk = ceil_div(ceil_div(n_tok, splits), FK) * FK;
     dim3 grid(tiles, splits);
     if (x_dtype == GPTQ_BF16)
-      syrk16_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
-                                               chunk, nt, P, dp, vec);
+      syrk256_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
+                                                chunk, nt, P, dp);
     else
-      syrk16_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
-                                                chunk, nt, P, dp, vec);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+      syrk256_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
+                                                 n_tok, chunk, nt, P, dp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    const int nt = (int)ceil_div(d, HT);
+    const int tiles = nt * (nt + 1) / 2;
+    splits = generic_splits(d, n_tok);
+    const int64_t chunk = ceil_div(ceil_div(n_tok, splits), HK) * HK;
+    if (x_dtype == GPTQ_F32) {
+      GemmArgs g{};
+      g.M = (int)d; g.N = (int)d;
+      g.K = (int)chunk; g.k_last = (int)(n_tok - (int64_t)(splits - 1) * chunk);
+      g.batch = splits; g.alpha = 1.f; g.beta = 0.f;
+      g.A = static_cast<const float*>(X); g.lda = ld_x; g.strideA = chunk * ld_x; g.trans_a = true;
+      g.B = static_cast<const float*>(X); g.ldb = ld_x; g.strideB = chunk * ld_x; g.trans_b = false;
+      g.C = P; g.ldc = dp; g.strideC = dp * dp; g.tri = 2;
+      if ((e = gemm_f32(g, s)) != hipSuccess) return e;
+    } else {
+      const int vec = ((uintptr_t)X % 16 == 0) && (ld_x % 8 == 0);
+      dim3 grid(tiles, splits);
+      if (x_dtype == GPTQ_BF16)
+        syrk16_generic_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
+                                                         n_tok, chunk, nt, P, dp, vec);
+      else
+        syrk16_generic_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
+                                                          n_tok, chunk, nt, P, dp, vec);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  syrk_reduce_kernel<<<tiles, 256, 0, s>>>(H, (int)d, P, dp, splits, nt);
+  {
+    const int nt128 = (int)(dp / HT);
+    syrk_reduce_kernel<<<nt128 * (nt128 + 1) / 2, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int nb = (int)ceil_div(d, 64);
+  mirror_kernel<<<nb * (nb + 1) / 2, 256, 0, s>>>(H, (int)d, nb);
   return hipGetLastError();
 }
 
