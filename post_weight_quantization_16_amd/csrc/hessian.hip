@@ -167,35 +167,63 @@ __global__ __launch_bounds__(256) void syrk16_generic_kernel(const uint16_t* __r
 // ---------------------------------------------------------------- fast path
 // 256x256 output tiles, 4 waves each owning a 128x128 block (4x4 tiles of
 // v_mfma_f32_32x32x16).  X stays in its natural [token][column] layout in LDS:
-// 64 tokens per stage, rows of 512 bytes whose 16-byte chunks are XOR-swizzled
-// by (row & 3) << 2.  MFMA operands (8 consecutive tokens of one column per
-// lane) come from two ds_read_b64_tr_b16 each: in every group of 16 lanes,
-// lane i receives element i%4 of the 8-byte piece addressed by lane 4r + i/4
-// (r = 0..3), so lanes addressing 4 rows x 16 columns get one column each.
-// With the swizzle, the 4 rows x 64 bytes a half-wave reads hit 64 distinct
-// banks.  The next stage is fetched into registers during the MFMAs.
+// stages of 32 tokens, rows of 512 bytes whose 16-byte chunks are
+// XOR-swizzled by (row & 3) << 2, double-buffered.  Each stage is fetched two
+// stages ahead into one of two register sets (8 x 16 bytes per thread), and
+// written to LDS one stage ahead, so about two stage-times of MFMA work cover
+// each load's latency.  Loads read clamped in-bounds addresses and zero
+// out-of-range chunks with a select (no branches around loads).  MFMA
+// operands (8 consecutive tokens of one column per lane) come from two
+// ds_read_b64_tr_b16 each: in every group of 16 lanes, lane i receives element
+// i%4 of the 8-byte piece addressed by lane 4r + i/4 (r = 0..3), so lanes
+// addressing 4 rows x 16 columns get one column each; with the swizzle a
+// half-wave's 4 rows x 64 bytes hit 64 distinct banks.
+// Work placement: workgroup L runs on XCD L % 8.  When the tile count allows
+// (nt % 16 == 0), each XCD gets whole pairs of tile rows {q, nt-1-q} (nt+1
+// tiles per pair), all tiles of one split before the next split, so tiles
+// that share an X panel share an L2 and run at the same tokens.
 // Requires d % 8 == 0, ld % 8 == 0 and a 16-byte aligned X.
 constexpr int FT = 256;                 // output tile
-constexpr int FK = 64;                  // tokens per stage
+constexpr int FK = 32;                  // tokens per stage
 constexpr int FROW = FT * 2;            // bytes per LDS row (one token)
-constexpr int FOP = FK * FROW;          // bytes per operand per stage (32 KB)
+constexpr int FOP = FK * FROW;          // bytes per operand per stage (16 KB)
+constexpr int FSTAGE = 2 * FOP;         // bytes per stage (32 KB)
+constexpr int NLD = FSTAGE / (256 * 16);   // 16-byte loads per thread per stage (8)
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int fswz(int row) { return (row & 3) << 2; }
+
+__device__ __forceinline__ void fast_tile(int L, int nt, int tiles, int& ti, int& tj, int& split) {
+  if (nt % 16 == 0) {
+    const int xcd = L & 7, k = L >> 3;
+    const int per = tiles / 8;                  // tiles per XCD per split
+    split = k / per;
+    const int u = k % per;
+    const int q = (u / (nt + 1)) * 8 + xcd;     // row pair {q, nt-1-q}
+    const int v = u % (nt + 1);
+    if (v < nt - q) { ti = q; tj = q + v; }
+    else { ti = nt - 1 - q; tj = ti + (v - (nt - q)); }
+  } else {
+    split = L / tiles;
+    tile_of(L % tiles, nt, ti, tj);
+  }
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict__ X, int64_t ld,
                                                       int d, int64_t n_tok, int64_t chunk, int nt,
                                                       float* __restrict__ P, int64_t dp) {
-  int ti, tj;
-  tile_of(blockIdx.x, nt, ti, tj);
-  const int split = blockIdx.y;
+  const int tiles = nt * (nt + 1) / 2;
+  int ti, tj, split;
+  fast_tile(blockIdx.x, nt, tiles, ti, tj, split);
   const int64_t t_begin = (int64_t)split * chunk;
   const int64_t t_end = min(n_tok, t_begin + chunk);
+  const int nstage = (int)((t_end - t_begin + FK - 1) / FK);
 
-  __shared__ __attribute__((aligned(16))) char S[2 * FOP];
+  __shared__ __attribute__((aligned(1024))) char S[2 * FSTAGE];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
 
@@ -207,34 +235,29 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // loader: chunk idx = t + 256*i, i < 8: operand, row, 16-byte chunk
-  constexpr int NLD = 2 * FK * (FROW / 16) / 256;
-  u32x4 stg[NLD];
-  const int col_a = ti * FT, col_b = tj * FT;
-  // Every load reads an in-bounds address (token and column clamped into the
-  // matrix) and out-of-range chunks are zeroed with a select: predicated
-  // loads here would push the staging registers into scratch.
-  auto gload = [&](int64_t t0) {
+  // loader: chunk idx = t + 256*i: operand idx / (FK*32), row (idx/32) % FK, chunk idx % 32
+  u32x4 ra[NLD], rb[NLD];
+  auto gload = [&](int st, u32x4 (&r)[NLD]) {
+    const int64_t t0 = t_begin + (int64_t)st * FK;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = t + 256 * i;
       const int op = idx / (FK * 32), row = (idx >> 5) % FK, ch = idx & 31;
-      const int col = (op ? col_b : col_a) + ch * 8;
+      const int col = (op ? tj : ti) * FT + ch * 8;
       const int64_t tok = t0 + row;
       const bool ok = tok < t_end && col < d;
-      const int64_t tk = ok ? tok : t_begin;
-      const int cc = ok ? col : 0;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(X + tk * ld + cc);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(X + (ok ? tok : t_begin) * ld + (ok ? col : 0));
       const u32x4 zero = {0u, 0u, 0u, 0u};
-      stg[i] = ok ? v : zero;
+      r[i] = ok ? v : zero;
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int st, const u32x4 (&r)[NLD]) {
+    char* base = S + (st & 1) * FSTAGE;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = t + 256 * i;
       const int op = idx / (FK * 32), row = (idx >> 5) % FK, ch = idx & 31;
-      *reinterpret_cast<u32x4*>(S + op * FOP + row * FROW + ((ch ^ fswz(row)) << 4)) = stg[i];
+      *reinterpret_cast<u32x4*>(base + op * FOP + row * FROW + ((ch ^ fswz(row)) << 4)) = r[i];
     }
   };
 
@@ -242,9 +265,6 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
   const int g = lane >> 4, j16 = lane & 15;
   const int rsub = 8 * (g >> 1) + (j16 >> 2);     // + ks*16 + 4h
   const int csub = 16 * (g & 1) + 4 * (j16 & 3);  // + fragment column base
-  const char* SA = S;
-  const char* SB = S + FOP;
-
   auto frag = [&](const char* base, int colbase, int ks) {
     s16x4 lo, hi;
     {
@@ -257,20 +277,13 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
       const int off = row * FROW + (((col >> 3) ^ fswz(row)) << 4) + ((col & 7) << 1);
       hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
     }
-    typedef __attribute__((ext_vector_type(8))) short s16x8;
-    s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return v;
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-
-  gload(t_begin);
-  lstore();
-  __syncthreads();
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += FK) {
-    gload(t0 + FK);  // past the end this loads zeros; no branch around it
+  auto compute = [&](int st) {
+    const char* SA = S + (st & 1) * FSTAGE;
+    const char* SB = SA + FOP;
 #pragma unroll
     for (int ks = 0; ks < FK / 16; ++ks) {
-      typedef __attribute__((ext_vector_type(8))) short s16x8;
-      asm volatile("" ::: "memory");  // one sub-step's operand reads at a time
       s16x8 a[4], b[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -289,12 +302,30 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
                 __builtin_bit_cast(f16x8, a[fi]), __builtin_bit_cast(f16x8, b[fj]), acc[fi][fj], 0, 0, 0);
         }
     }
+  };
+
+  // stage s: fetched into register set s%2 at iteration s-2, stored to LDS
+  // buffer s%2 at the end of iteration s-1, multiplied at iteration s.  The
+  // loop runs in pairs so the register sets are named statically.
+  gload(0, ra);
+  gload(1, rb);
+  lstore(0, ra);
+  __syncthreads();
+  for (int st = 0; st < nstage; st += 2) {
+    gload(st + 2, ra);       // past the end: zeros, harmless
+    compute(st);
     __syncthreads();
-    lstore();
+    lstore(st + 1, rb);      // stage st+1 (fetched last iteration)
+    __syncthreads();
+    gload(st + 3, rb);
+    compute(st + 1);         // past the end: an all-zero stage
+    __syncthreads();
+    lstore(st + 2, ra);
     __syncthreads();
   }
 
   // epilogue: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32 of each 32x32 tile
+  float* Pt = P + (int64_t)split * dp * dp;
 #pragma unroll
   for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
@@ -303,7 +334,7 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
       for (int r = 0; r < 16; ++r) {
         const int row = ti * FT + wm * 128 + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int cl = tj * FT + wn * 128 + fj * 32 + (lane & 31);
-        P[(int64_t)split * dp * dp + (int64_t)row * dp + cl] = acc[fi][fj][r];
+        Pt[(int64_t)row * dp + cl] = acc[fi][fj][r];
       }
 }
 
@@ -406,7 +437,7 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
     const int tiles = nt * (nt + 1) / 2;
     splits = fast_splits(d, n_tok);
     const int64_t chunk = ceil_div(ceil_div(n_tok, splits), FK) * FK;
-    dim3 grid(tiles, splits);
+    const unsigned grid = (unsigned)(tiles * splits);
     if (x_dtype == GPTQ_BF16)
       syrk256_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
                                                 chunk, nt, P, dp);

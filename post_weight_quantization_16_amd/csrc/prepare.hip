@@ -11,11 +11,12 @@
 // reversal, G = J·H_d·J = L·Lᵀ (ordinary lower Cholesky); then
 // H_d = (JLJ)(JLJ)ᵀ with JLJ upper, so H_d⁻¹ = (JL⁻¹J)ᵀ(JL⁻¹J) and
 // U = J·L⁻¹·J, the unique upper factor with positive diagonal.  Two O(d³)
-// steps: a blocked right-looking Cholesky (64-wide panels factored in
-// registers, trailing SYRK on the fp32 MFMA GEMM) and a triangular inverse:
-// all 64x64 diagonal blocks inverted at once, then recursive doubling
-// ([[A,0],[B,C]]⁻¹ has off-diagonal block −C⁻¹·B·A⁻¹, products skipping the
-// zero triangles), both fp32.
+// steps, both fp32: a blocked right-looking Cholesky with 64-wide panels
+// (each diagonal block factored and inverted together in one wave, the
+// panel below solved with that inverse and the trailing SYRK, both on the
+// fp32 MFMA GEMM), then the rest of the triangular inverse by recursive
+// doubling ([[A,0],[B,C]]⁻¹ has off-diagonal block −C⁻¹·B·A⁻¹, products
+// skipping the zero triangles).
 #include <algorithm>
 #include <climits>
 
@@ -114,118 +115,61 @@ __global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, in
   }
 }
 
-// One Cholesky panel: factor the kb x kb diagonal block at k0 (kb <= 64) and
-// solve the rows below it, L21 = G21·L11⁻ᵀ.  One wave per workgroup; every
-// workgroup factors the small diagonal block itself (row i in lane i's
-// registers, left-looking: step j finishes column j from row j of L, which
-// is broadcast from LDS; pivots via readlane), so no
-// workgroup waits for another.  G's diagonal block is only read here (other
-// workgroups of the same launch read it), so workgroup 0 writes L11 to the
-// diagonal block of Linv instead, where trtri_diag_kernel inverts it in place;
-// workgroup b solves rows k0+kb+64b .. +63 by forward substitution in registers.
-// The block is padded to 64 with the identity.  A non-positive (or NaN/inf)
-// pivot is recorded in *status (smallest index wins) and replaced by 1 so the
-// arithmetic stays finite.  Results leave the unrolled register arrays through
-// LDS (unconditional stores) and reach memory in a bounds-checked loop: stores
-// predicated inside the unrolled code would push the arrays into scratch.
-__global__ __launch_bounds__(64) void potrf_trsm_kernel(float* __restrict__ G, int64_t d, int k0,
-                                                        int kb, float* __restrict__ Ldiag,
-                                                        int* __restrict__ status) {
-  __shared__ float LM[NB][NB + 4];  // LM[i][j] = L[i][j]
-  __shared__ float LT[NB][NB + 4];  // LT[j][k] = L[k][j]
-  __shared__ float XO[NB][NB + 1];  // solved rows, one per lane
+// One Cholesky panel's diagonal block: L11 = chol(G11) and X = L11⁻¹ in a
+// single right-looking sweep (one wave; the block is padded to 64 with the
+// identity).  Lane i holds row i of the block being factored (a) and column i
+// of the inverse being built (r).  Step j: the pivot is lane j's a[j];
+// every lane scales its a[j] into l_ij and publishes it through LDS; then
+// a[k] −= l_ij·l_kj (the trailing rank-1 update) and, for the inverse,
+// x_j = r[j]/l_jj followed by r[k] −= l_kj·x_j (forward substitution
+// carried along the same column of L).  Only X is stored, into the diagonal
+// block of Linv: the rows below are then L21 = G21·Xᵀ, one GEMM, and the
+// doubling inverse needs X, not L11.  A non-positive (or NaN/inf) pivot is
+// recorded in *status (smallest index wins) and replaced by 1 so the
+// arithmetic stays finite.
+__global__ __launch_bounds__(64) void potrf_inv_kernel(const float* __restrict__ G, int64_t d,
+                                                       int k0, int kb, float* __restrict__ Linv,
+                                                       int* __restrict__ status) {
+  __shared__ float col[2][NB];      // column j of L, double-buffered by step parity
+  __shared__ float XS[NB][NB + 1];  // X staged row-major for a coalesced write
   const int i = threadIdx.x;
-  float a[NB];
+  float a[NB], r[NB];
   const float* grow = G + (int64_t)(k0 + i) * d + k0;
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     float v = (i == k) ? 1.f : 0.f;
     if (i < kb && k < kb && k <= i) v = grow[k];
     a[k] = v;
+    r[k] = (i == k) ? 1.f : 0.f;
   }
-  // left-looking: step j finishes column j; row j of L (final since step j-1)
-  // is read from LM with wave-uniform loads
   int bad_j = -1;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    __syncthreads();
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int t = 0; t < j; ++t) {
-      if (t & 1) s1 = fmaf(a[t], LM[j][t], s1);
-      else s0 = fmaf(a[t], LM[j][t], s0);
-    }
-    const float v = a[j] - (s0 + s1);
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
     const bool bad = !(piv > 0.f) || !(piv < INFINITY);
-    if (bad && bad_j < 0) bad_j = j;
+    bad_j = (bad && bad_j < 0) ? j : bad_j;
     const float ljj = bad ? 1.f : sqrtf(piv);
-    a[j] = (i > j) ? v / ljj : (i == j ? ljj : 0.f);
-    LM[i][j] = a[j];
-    LT[j][i] = a[j];
-  }
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    if (i == 0 && bad_j >= 0) atomicMin(status, k0 + bad_j);
-    for (int e = i; e < kb * kb; e += NB) {
-      const int r = e / kb, c = e % kb;
-      if (c <= r) Ldiag[(int64_t)(k0 + r) * d + k0 + c] = LT[c][r];
+    const float inv = 1.f / ljj;
+    const float l = (i > j) ? a[j] * inv : (i == j ? ljj : 0.f);
+    a[j] = l;
+    const float x = r[j] * inv;
+    r[j] = x;
+    col[j & 1][i] = l;
+    __syncthreads();
+#pragma unroll
+    for (int k = j + 1; k < NB; ++k) {
+      const float ck = col[j & 1][k];
+      a[k] = fmaf(-l, ck, a[k]);
+      r[k] = fmaf(-ck, x, r[k]);
     }
   }
-  const int64_t rbase = (int64_t)k0 + kb + (int64_t)blockIdx.x * NB;
-  const int64_t r = rbase + i;
-  const float* row = G + r * d + k0;
-  float g[NB];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) g[k] = (r < d && k < kb) ? row[k] : 0.f;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const float x = g[j] / LT[j][j];
-    g[j] = x;
-#pragma unroll
-    for (int k = j + 1; k < NB; ++k) g[k] = fmaf(-x, LT[j][k], g[k]);
-  }
-#pragma unroll
-  for (int k = 0; k < NB; ++k) XO[i][k] = g[k];
+  for (int k = 0; k < NB; ++k) XS[k][i] = r[k];
   __syncthreads();
-  const int nrows = (int)min<int64_t>(NB, d - rbase);
-  for (int e = i; e < nrows * kb; e += NB) {
+  if (i == 0 && bad_j >= 0) atomicMin(status, k0 + bad_j);
+  for (int e = i; e < kb * kb; e += NB) {
     const int rr = e / kb, c = e % kb;
-    G[(rbase + rr) * d + k0 + c] = XO[rr][c];
-  }
-}
-
-// Inverses of all 64x64 diagonal blocks of the factor L, in place in Linv
-// (where the panel kernel left the factored blocks).  One wave per block;
-// lane c computes column c of L_bb⁻¹ by forward substitution
-// (x_i = ([i == c] − Σ_{t<i} L_it x_t) / L_ii), reading the block's rows from
-// LDS with wave-uniform loads; the result goes back through LDS.
-__global__ __launch_bounds__(64) void trtri_diag_kernel(int64_t d, float* __restrict__ Linv) {
-  __shared__ float L[NB][NB + 4];
-  const int64_t b0 = (int64_t)blockIdx.x * NB;
-  const int kb = (int)min<int64_t>(NB, d - b0);
-  const int c = threadIdx.x;
-  for (int t = 0; t < NB; ++t) {
-    float v = (c == t) ? 1.f : 0.f;
-    if (c < kb && t < kb && t <= c) v = Linv[(b0 + c) * d + b0 + t];
-    L[c][t] = v;
-  }
-  __syncthreads();
-  float x[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    float sacc = 0.f;
-#pragma unroll
-    for (int t = 0; t < i; ++t) sacc = fmaf(L[i][t], x[t], sacc);
-    x[i] = ((i == c ? 1.f : 0.f) - sacc) / L[i][i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NB; ++i) L[i][c] = (i >= c) ? x[i] : 0.f;
-  __syncthreads();
-  for (int e = c; e < kb * kb; e += NB) {
-    const int i = e / kb, cc = e % kb;
-    Linv[(b0 + i) * d + b0 + cc] = L[i][cc];
+    Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr][c];
   }
 }
 
@@ -290,15 +234,22 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();
 
-  // blocked right-looking Cholesky of G (lower): per panel, one fused
-  // factor+solve launch and one trailing SYRK on the fp32 MFMA GEMM
+  // blocked right-looking Cholesky of G (lower), 64-wide panels: the
+  // diagonal block's factor and inverse X in one workgroup, the rows below
+  // as L21 = G21·Xᵀ and the trailing SYRK, both on the fp32 MFMA GEMM
   for (int64_t k0 = 0; k0 < d; k0 += NB) {
     const int kb = (int)std::min<int64_t>(NB, d - k0);
     const int64_t r0 = k0 + kb, nr = d - r0;
-    const unsigned nblk = (unsigned)std::max<int64_t>(1, ceil_div(nr, NB));
-    potrf_trsm_kernel<<<nblk, NB, 0, s>>>(w.G, d, (int)k0, kb, w.Linv, w.status);
+    potrf_inv_kernel<<<1, NB, 0, s>>>(w.G, d, (int)k0, kb, w.Linv, w.status);
     GQ_CHECK();
     if (nr <= 0) break;
+    GemmArgs p{};  // L21 = G21 · Xᵀ, in place: one column of output tiles
+    p.M = (int)nr; p.N = kb; p.K = kb; p.k_last = kb; p.batch = 1;  // (N <= 128), so each
+    p.alpha = 1.f; p.beta = 0.f;                                      // workgroup reads all
+    p.A = w.G + r0 * d + k0; p.lda = d; p.trans_a = false;           // of its rows before
+    p.B = w.Linv + k0 * d + k0; p.ldb = d; p.trans_b = true;          // writing them
+    p.C = w.G + r0 * d + k0; p.ldc = d; p.tri = 0;
+    if ((e = gemm_f32(p, s)) != hipSuccess) return e;
     GemmArgs h{};  // G22 −= L21 · L21ᵀ  (lower triangle)
     h.M = (int)nr; h.N = (int)nr; h.K = kb; h.k_last = kb; h.batch = 1;
     h.alpha = -1.f; h.beta = 1.f;
@@ -307,8 +258,6 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     h.C = w.G + r0 * d + r0; h.ldc = d; h.tri = 1;
     if ((e = gemm_f32(h, s)) != hipSuccess) return e;
   }
-  trtri_diag_kernel<<<(unsigned)ceil_div(d, NB), NB, 0, s>>>(d, w.Linv);
-  GQ_CHECK();
 
   // triangular inverse by recursive doubling on 64-aligned blocks
   for (int64_t sz = NB; sz < d; sz *= 2) {
