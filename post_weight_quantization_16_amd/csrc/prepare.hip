@@ -12,8 +12,8 @@
 // H_d = (JLJ)(JLJ)ᵀ with JLJ upper, so H_d⁻¹ = (JL⁻¹J)ᵀ(JL⁻¹J) and
 // U = J·L⁻¹·J, the unique upper factor with positive diagonal.  Two O(d³)
 // steps, both fp32: a blocked right-looking Cholesky with 64-wide panels
-// (each diagonal block factored and inverted together in one wave, the
-// panel below solved with that inverse and the trailing SYRK, both on the
+// (each diagonal block factored and inverted together, the panel below
+// solved with that inverse in the same launch, the trailing SYRK on the
 // fp32 MFMA GEMM), then the rest of the triangular inverse by recursive
 // doubling ([[A,0],[B,C]]⁻¹ has off-diagonal block −C⁻¹·B·A⁻¹, products
 // skipping the zero triangles).
@@ -115,61 +115,120 @@ __global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, in
   }
 }
 
-// One Cholesky panel's diagonal block: L11 = chol(G11) and X = L11⁻¹ in a
-// single right-looking sweep (one wave; the block is padded to 64 with the
-// identity).  Lane i holds row i of the block being factored (a) and column i
-// of the inverse being built (r).  Step j: the pivot is lane j's a[j];
-// every lane scales its a[j] into l_ij and publishes it through LDS; then
-// a[k] −= l_ij·l_kj (the trailing rank-1 update) and, for the inverse,
-// x_j = r[j]/l_jj followed by r[k] −= l_kj·x_j (forward substitution
-// carried along the same column of L).  Only X is stored, into the diagonal
-// block of Linv: the rows below are then L21 = G21·Xᵀ, one GEMM, and the
-// doubling inverse needs X, not L11.  A non-positive (or NaN/inf) pivot is
-// recorded in *status (smallest index wins) and replaced by 1 so the
-// arithmetic stays finite.
-__global__ __launch_bounds__(64) void potrf_inv_kernel(const float* __restrict__ G, int64_t d,
-                                                       int k0, int kb, float* __restrict__ Linv,
-                                                       int* __restrict__ status) {
-  __shared__ float col[2][NB];      // column j of L, double-buffered by step parity
-  __shared__ float XS[NB][NB + 1];  // X staged row-major for a coalesced write
-  const int i = threadIdx.x;
-  float a[NB], r[NB];
-  const float* grow = G + (int64_t)(k0 + i) * d + k0;
+// One 64-wide Cholesky panel at column k0 (kb <= 64 columns):
+//   L11 = chol(G11),  X = L11⁻¹,  L21 = G21·Xᵀ.
+// Every workgroup (4 waves) factors and inverts the small diagonal block
+// itself, so no workgroup waits for another; workgroup b then solves the
+// 64 rows k0+kb+64b .. +63 of the panel with one 64x64x64 fp32 MFMA product,
+// in place in G, and workgroup 0 stores X into the diagonal block of Linv
+// (L11 itself is not needed later).  The block is padded to 64 with the
+// identity.
+// The factor and the inverse are one right-looking sweep.  Lane i of wave w
+// holds A[i][16w..16w+15] (a) and X[16w..16w+15][i] (r).  Step j: the wave
+// owning column j takes the pivot from lane j, scales the column into
+// l_ij = a_ij / l_jj and finishes x_j = r_j / l_jj, and publishes both
+// through LDS with l_ij zeroed for i <= j; after one barrier every lane
+// applies a_ik −= l_ij·l_kj and r_k −= l_kj·x_j to its 16 columns -- the
+// zeroed entries make the update a no-op where k <= j, so it needs no
+// masks.  A non-positive (or NaN/inf) pivot is recorded in *status
+// (smallest index wins) and replaced by 1 so the arithmetic stays finite.
+__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ G, int64_t d, int k0,
+                                                    int kb, float* __restrict__ Linv,
+                                                    int* __restrict__ status) {
+  constexpr int LS = NB + 2;  // row stride: the two half-waves' MFMA reads hit disjoint banks
+  __shared__ float AS[NB * LS];    // G11, then this workgroup's block of G21
+  __shared__ float XS[NB * LS];    // X
+  __shared__ float pub[2][2][NB];  // [step parity][l, x][lane]
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int64_t R0 = (int64_t)k0 + kb + (int64_t)blockIdx.x * NB;
+
+  // the block of G21 this workgroup solves, fetched now and used after the sweep
+  float pre[16];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    float v = (i == k) ? 1.f : 0.f;
-    if (i < kb && k < kb && k <= i) v = grow[k];
-    a[k] = v;
-    r[k] = (i == k) ? 1.f : 0.f;
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + 256 * u, rr = idx >> 6, cc = idx & 63;
+    const bool ok = R0 + rr < d && cc < kb;
+    const float v = G[(ok ? R0 + rr : 0) * d + (ok ? k0 + cc : 0)];
+    pre[u] = ok ? v : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
+    const bool ok = i < kb && k <= i;
+    const float v = G[(int64_t)(k0 + (ok ? i : 0)) * d + k0 + (ok ? k : 0)];
+    AS[i * LS + k] = ok ? v : (i == k ? 1.f : 0.f);
+  }
+  __syncthreads();
+  float a[16], r[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    a[q] = AS[lane * LS + 16 * w + q];
+    r[q] = (16 * w + q == lane) ? 1.f : 0.f;
   }
   int bad_j = -1;
+  for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
-    const bool bad = !(piv > 0.f) || !(piv < INFINITY);
-    bad_j = (bad && bad_j < 0) ? j : bad_j;
-    const float ljj = bad ? 1.f : sqrtf(piv);
-    const float inv = 1.f / ljj;
-    const float l = (i > j) ? a[j] * inv : (i == j ? ljj : 0.f);
-    a[j] = l;
-    const float x = r[j] * inv;
-    r[j] = x;
-    col[j & 1][i] = l;
-    __syncthreads();
+    for (int q0 = 0; q0 < 16; ++q0) {
+      const int j = jb * 16 + q0, par = q0 & 1;
+      if (w == jb) {
+        const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
+        const bool bad = !(piv > 0.f) || !(piv < INFINITY);
+        bad_j = (bad && bad_j < 0) ? j : bad_j;
+        // one hardware reciprocal square root on the serial chain (about
+        // 1 ulp; 1/l_jj and l_jj = piv·(1/l_jj) both come from it)
+        const float inv = bad ? 1.f : __builtin_amdgcn_rsqf(piv);
+        const float ljj = bad ? 1.f : piv * inv;
+        const float l = a[q0] * inv;
+        a[q0] = lane > j ? l : (lane == j ? ljj : 0.f);
+        const float x = r[q0] * inv;
+        r[q0] = x;
+        pub[par][0][lane] = lane > j ? l : 0.f;
+        pub[par][1][lane] = x;
+      }
+      __syncthreads();
+      const float li = pub[par][0][lane], xv = pub[par][1][lane];
 #pragma unroll
-    for (int k = j + 1; k < NB; ++k) {
-      const float ck = col[j & 1][k];
-      a[k] = fmaf(-l, ck, a[k]);
-      r[k] = fmaf(-ck, x, r[k]);
+      for (int q = 0; q < 16; ++q) {
+        const float c = pub[par][0][16 * w + q];
+        a[q] = fmaf(-li, c, a[q]);
+        r[q] = fmaf(-c, xv, r[q]);
+      }
     }
   }
 #pragma unroll
-  for (int k = 0; k < NB; ++k) XS[k][i] = r[k];
+  for (int q = 0; q < 16; ++q) XS[(16 * w + q) * LS + lane] = r[q];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + 256 * u;
+    AS[(idx >> 6) * LS + (idx & 63)] = pre[u];
+  }
   __syncthreads();
-  if (i == 0 && bad_j >= 0) atomicMin(status, k0 + bad_j);
-  for (int e = i; e < kb * kb; e += NB) {
-    const int rr = e / kb, c = e % kb;
-    Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr][c];
+  if (blockIdx.x == 0) {
+    if (lane == 0 && bad_j >= 0) atomicMin(status, k0 + bad_j);
+    for (int e = t; e < kb * kb; e += 256) {
+      const int rr = e / kb, c = e % kb;
+      Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr * LS + c];
+    }
+  }
+  if (R0 >= d) return;
+  // L21 block = G21 block · Xᵀ: wave w computes the 32x32 tile (w/2, w%2);
+  // v_mfma_f32_32x32x2f32 takes A(m = lane%32, k = lane/32), B(k, n = lane%32)
+  const int mi = w >> 1, ni = w & 1;
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NB / 2; ++kk) {
+    const int k = 2 * kk + (lane >> 5);
+    const float av = AS[(32 * mi + (lane & 31)) * LS + k];
+    const float bv = XS[(32 * ni + (lane & 31)) * LS + k];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = 32 * mi + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+    const int col = 32 * ni + (lane & 31);
+    if (R0 + row < d && col < kb) G[(R0 + row) * d + k0 + col] = acc[e];
   }
 }
 
@@ -234,22 +293,16 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();
 
-  // blocked right-looking Cholesky of G (lower), 64-wide panels: the
-  // diagonal block's factor and inverse X in one workgroup, the rows below
-  // as L21 = G21·Xᵀ and the trailing SYRK, both on the fp32 MFMA GEMM
+  // blocked right-looking Cholesky of G (lower), 64-wide panels: one fused
+  // factor / inverse / panel-solve launch and the trailing SYRK on the fp32
+  // MFMA GEMM
   for (int64_t k0 = 0; k0 < d; k0 += NB) {
     const int kb = (int)std::min<int64_t>(NB, d - k0);
     const int64_t r0 = k0 + kb, nr = d - r0;
-    potrf_inv_kernel<<<1, NB, 0, s>>>(w.G, d, (int)k0, kb, w.Linv, w.status);
+    const unsigned nblk = (unsigned)std::max<int64_t>(1, ceil_div(nr, NB));
+    panel_kernel<<<nblk, 256, 0, s>>>(w.G, d, (int)k0, kb, w.Linv, w.status);
     GQ_CHECK();
     if (nr <= 0) break;
-    GemmArgs p{};  // L21 = G21 · Xᵀ, in place: one column of output tiles
-    p.M = (int)nr; p.N = kb; p.K = kb; p.k_last = kb; p.batch = 1;  // (N <= 128), so each
-    p.alpha = 1.f; p.beta = 0.f;                                      // workgroup reads all
-    p.A = w.G + r0 * d + k0; p.lda = d; p.trans_a = false;           // of its rows before
-    p.B = w.Linv + k0 * d + k0; p.ldb = d; p.trans_b = true;          // writing them
-    p.C = w.G + r0 * d + k0; p.ldc = d; p.tri = 0;
-    if ((e = gemm_f32(p, s)) != hipSuccess) return e;
     GemmArgs h{};  // G22 −= L21 · L21ᵀ  (lower triangle)
     h.M = (int)nr; h.N = (int)nr; h.K = kb; h.k_last = kb; h.batch = 1;
     h.alpha = -1.f; h.beta = 1.f;

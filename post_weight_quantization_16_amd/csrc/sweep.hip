@@ -6,19 +6,21 @@
 // This file is compiled once per group-size variant (-DGQ_SWEEP_G=0/32/64/128)
 // so the heavily unrolled variants build in parallel.
 //
-// Layout: four lanes (a DPP quad) per weight row, lane c of the quad holding
-// the row's columns 32c..32c+31 of the block in registers; a wave covers 16
-// rows, a workgroup 16·W rows.  The block's 128x128 part of U and 1/U_jj are
+// Layout: one 16-lane DPP row per weight row; lane c holds the row's block
+// columns 4c..4c+3 and 64+4c..64+4c+3 in registers (so the lanes of a row
+// read one contiguous 256-byte span of a U row per half), a wave covers 4
+// rows, a workgroup 4·W rows.  The block's 128x128 part of U and 1/U_jj are
 // staged in LDS once per workgroup.  For each column j of the block:
-//   w_j is broadcast inside the quad from its owner lane (DPP quad_perm),
-//   at a group start the quad reduces the group's current min/max,
+//   w_j is broadcast inside the row from its owner lane (DPP row_newbcast),
+//   at a group start the row reduces the group's current min/max (DPP),
 //   v = w_j·(1/s) + z;  q = clamp(rint(v), 0, 2ᵇ−1);  ŵ = s(q − z)
-//   err = (w_j − ŵ)·(1/U_jj);  every lane: w_k −= err·U_jk for its 32 columns
-// (U is upper triangular, so columns at or left of j receive zeros and the
-// update needs no per-lane bounds).  ŵ, err and q go to LDS and are written
-// back coalesced after the block.  The working copy is padded to whole blocks:
-// padded columns hold 0 and their U rows/columns are 0 with a unit diagonal,
-// so they quantize to 0 with err 0.
+//   err = (w_j − ŵ)·(1/U_jj);  every lane: w_k −= err·U_jk for its 8 columns
+// (U is upper triangular, so columns left of j receive zeros and the update
+// needs no per-lane bounds); the owner lane then keeps ŵ, err and q in the
+// column's register slot, and the block is written back coalesced from the
+// registers.  Every lane of a row computes the same v, q, ŵ and err.  The
+// working copy is padded to whole blocks: padded columns hold 0 and their U
+// rows/columns are 0 with a unit diagonal, so they quantize to 0 with err 0.
 #include "common.hpp"
 
 #ifndef GQ_SWEEP_G
@@ -28,27 +30,41 @@
 namespace gq {
 namespace {
 
-constexpr int QC = kBlock / 4;        // columns per lane
-constexpr int SROW = kBlock + 1;      // LDS staging row stride (odd: no bank conflicts)
-constexpr int QROW = kBlock + 4;      // code staging row stride (bytes)
-constexpr size_t kWaveStage = (size_t)2 * 16 * SROW * sizeof(float) + 16 * QROW;
+constexpr int QC = kBlock / 16;   // columns per lane
+constexpr int SROW = kBlock + 1;  // err staging row stride (odd: the rows' writes hit distinct banks)
+constexpr int QROW = kBlock + 4;  // code staging row stride (bytes)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-// quad_perm selector with every lane reading quad lane o
-template <int O>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return dpp<O | (O << 2) | (O << 4) | (O << 6)>(x);
+// lane o of each 16-lane row to the whole row; o is a constant once the
+// column loop is unrolled, so the switch folds away
+__device__ __forceinline__ float row_bcast(float x, int o) {
+  switch (o) {
+    case 0: return dpp<0x150>(x);  case 1: return dpp<0x151>(x);
+    case 2: return dpp<0x152>(x);  case 3: return dpp<0x153>(x);
+    case 4: return dpp<0x154>(x);  case 5: return dpp<0x155>(x);
+    case 6: return dpp<0x156>(x);  case 7: return dpp<0x157>(x);
+    case 8: return dpp<0x158>(x);  case 9: return dpp<0x159>(x);
+    case 10: return dpp<0x15A>(x); case 11: return dpp<0x15B>(x);
+    case 12: return dpp<0x15C>(x); case 13: return dpp<0x15D>(x);
+    case 14: return dpp<0x15E>(x); default: return dpp<0x15F>(x);
+  }
 }
-__device__ __forceinline__ float quad_min(float x) {
-  x = fminf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  return fminf(x, dpp<0x4E>(x)); // quad_perm [2,3,0,1]
+// reductions over a 16-lane row: quad_perm [1,0,3,2], [2,3,0,1], then
+// row_half_mirror and row_mirror; every lane ends with the row's result
+__device__ __forceinline__ float row_min(float x) {
+  x = fminf(x, dpp<0xB1>(x));
+  x = fminf(x, dpp<0x4E>(x));
+  x = fminf(x, dpp<0x141>(x));
+  return fminf(x, dpp<0x140>(x));
 }
-__device__ __forceinline__ float quad_max(float x) {
+__device__ __forceinline__ float row_max(float x) {
   x = fmaxf(x, dpp<0xB1>(x));
-  return fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  return fmaxf(x, dpp<0x140>(x));
 }
 
 // G > 0: groups of G columns inside the block (parameters from registers);
@@ -59,7 +75,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   constexpr int GG = G > 0 ? G : 1;
   __shared__ __attribute__((aligned(16))) float Us[kBlock * kBlock];
   __shared__ float rud[kBlock];
-  extern __shared__ __attribute__((aligned(16))) char dyn[];  // per wave: ŵ, err [16][SROW] fp32, codes [16][QROW] u8
+  // per wave: err [4][SROW] fp32 and codes [4][QROW] u8 of the block's columns
+  __shared__ __attribute__((aligned(16))) char stage[4][4 * SROW * 4 + 4 * QROW];
   const int nthr = blockDim.x, t = threadIdx.x;
   {
     const bool vec = (((uintptr_t)a.Ublk) % 16 == 0) && (a.ldu % 4 == 0);
@@ -80,21 +97,20 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   __syncthreads();
 
   const int wave = t >> 6, lane = t & 63;
-  const int rloc = lane >> 2, c = lane & 3;          // row within the wave, quad lane
-  const int64_t rbase = ((int64_t)blockIdx.x * (nthr >> 6) + wave) * 16;
-  const int64_t r = rbase + rloc;
+  const int c = lane & 15, rloc = lane >> 4;          // lane within the row, row in the wave
+  const int64_t r = ((int64_t)blockIdx.x * (nthr >> 6) + wave) * 4 + (lane >> 4);
   const bool live = r < a.m;
-  float* SW = reinterpret_cast<float*>(dyn + wave * kWaveStage);   // ŵ
-  float* SE = SW + 16 * SROW;                                        // err
-  uint8_t* SQ = reinterpret_cast<uint8_t*>(SE + 16 * SROW);          // codes
-
+  // slot sl < 4: column 4c+sl; slot sl >= 4: column 64+4c+sl-4
   float w[QC];
+  float* SE = reinterpret_cast<float*>(stage[wave]);
+  uint8_t* SQ = reinterpret_cast<uint8_t*>(SE + 4 * SROW);
   {
-    const float* src = a.Wk + (live ? r : 0) * a.ldw + a.b0 + c * QC;
+    const float* src = a.Wk + (live ? r : 0) * a.ldw + a.b0 + 4 * c;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 64);
 #pragma unroll
-    for (int k = 0; k < QC; k += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + k);
-      w[k] = v[0]; w[k + 1] = v[1]; w[k + 2] = v[2]; w[k + 3] = v[3];
+    for (int q = 0; q < 4; ++q) {
+      w[q] = lo[q]; w[4 + q] = hi[q];
     }
   }
 
@@ -107,26 +123,44 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
     }
     rs = 1.f / s;
   }
-  float loss = 0.f;
   const float fmaxq = (float)a.maxq;
   constexpr int NG = G > 0 ? kBlock / GG : 1;   // groups starting in this block
   float gs[NG], gz[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) { gs[k] = 1.f; gz[k] = 0.f; }
+  // U row j and 1/U_jj are read from LDS two columns ahead; the scheduling
+  // barrier at the end of each column keeps the compiler from hoisting all
+  // 128 columns' reads (which would not fit in registers)
+  constexpr int PF = 2;
+  f32x4 ub0[PF], ub1[PF];
+  float ubr[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    ub0[p] = *reinterpret_cast<const f32x4*>(Us + p * kBlock + 4 * c);
+    ub1[p] = *reinterpret_cast<const f32x4*>(Us + p * kBlock + 64 + 4 * c);
+    ubr[p] = rud[p];
+  }
 #pragma unroll
   for (int j = 0; j < kBlock; ++j) {
-    const int o = j / QC, jj = j % QC;
+    const int o = (j & 63) >> 2, slot = (j >> 6) * 4 + (j & 3);
+    const f32x4 u0 = ub0[j % PF], u1 = ub1[j % PF];
+    const float ru = ubr[j % PF];
+    if (j + PF < kBlock) {
+      ub0[j % PF] = *reinterpret_cast<const f32x4*>(Us + (j + PF) * kBlock + 4 * c);
+      ub1[j % PF] = *reinterpret_cast<const f32x4*>(Us + (j + PF) * kBlock + 64 + 4 * c);
+      ubr[j % PF] = rud[j + PF];
+    }
     if (G > 0 && j % GG == 0) {
-      // the group's columns [j, j+G) ∩ real columns, spread over the quad
+      // the group's columns [j, j+G) ∩ real columns, spread over the row
       float mn = INFINITY, mx = -INFINITY, am = 0.f;
 #pragma unroll
-      for (int k = 0; k < QC; ++k) {
-        const int col = c * QC + k;
+      for (int sl = 0; sl < QC; ++sl) {
+        const int col = (sl < 4) ? 4 * c + sl : 64 + 4 * c + (sl - 4);
         const bool in = col >= j && col < j + GG && col < a.bw;
-        mn = fminf(mn, in ? w[k] : INFINITY); mx = fmaxf(mx, in ? w[k] : -INFINITY);
-        am = fmaxf(am, in ? fabsf(w[k]) : 0.f);
+        mn = fminf(mn, in ? w[sl] : INFINITY); mx = fmaxf(mx, in ? w[sl] : -INFINITY);
+        am = fmaxf(am, in ? fabsf(w[sl]) : 0.f);
       }
-      mn = quad_min(mn); mx = quad_max(mx); am = quad_max(am);
+      mn = row_min(mn); mx = row_max(mx); am = row_max(am);
       float s2, z2;
       group_qparams(mn, mx, am, a.maxq, a.sym, s2, z2);
       // groups starting beyond the real columns keep the previous parameters
@@ -137,30 +171,27 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       gs[j / GG] = s;
       gz[j / GG] = z;
     }
-    float wj;
-    switch (o) {
-      case 0: wj = quad_bcast<0>(w[jj]); break;
-      case 1: wj = quad_bcast<1>(w[jj]); break;
-      case 2: wj = quad_bcast<2>(w[jj]); break;
-      default: wj = quad_bcast<3>(w[jj]); break;
-    }
+    const float wj = row_bcast(w[slot], o);
     const float v = wj * rs + z;
     const float q = fminf(fmaxf(rintf(v), 0.f), fmaxq);
     const float wq = s * (q - z);
-    const float err = (wj - wq) * rud[j];
-    // every lane of the quad holds the same ŵ, err, q: same-address writes
-    SW[rloc * SROW + j] = wq;
+    const float err = (wj - wq) * ru;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      w[q4] = fmaf(-err, u0[q4], w[q4]);
+      w[4 + q4] = fmaf(-err, u1[q4], w[4 + q4]);
+    }
+    w[slot] = (c == o) ? wq : w[slot];
+    // every lane of the row holds the same err and q: same-address writes
     SE[rloc * SROW + j] = err;
     SQ[rloc * QROW + j] = (uint8_t)q;
-    loss = (c == o) ? fmaf(err, err, loss) : loss;
-    const float* Urow = Us + j * kBlock + c * QC;
+    // keep the compiler from deferring column updates to the end of the
+    // block (which holds every column's err in registers): the updated
+    // weights must exist here
 #pragma unroll
-    for (int k = 0; k < QC; ++k) w[k] = fmaf(-err, Urow[k], w[k]);
+    for (int k = 0; k < QC; ++k) asm volatile("" : "+v"(w[k]));
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // row loss: sum the quad's partial sums
-  loss += dpp<0xB1>(loss);
-  loss += dpp<0x4E>(loss);
-  if (live && c == 0 && a.row_loss) a.row_loss[r] += 0.5f * loss;
   if (G > 0 && live && c == 0) {
     for (int k = 0; k < NG && k * GG < a.bw; ++k) {
       const int64_t gi = (a.b0 + k * GG) / GG;
@@ -171,24 +202,38 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       a.zeros[r * a.ng + gi] = (uint8_t)zv;
     }
   }
-  __syncthreads();
-  // write back: lane (row, c) stores its row's columns c*32 .. +31
-  if (live) {
-    float* dw = a.Wk + r * a.ldw + a.b0 + c * QC;
-    float* de = a.Err + r * kBlock + c * QC;
-    uint8_t* dq = a.codes + r * a.ldw + a.b0 + c * QC;
+  __builtin_amdgcn_wave_barrier();   // the row's staged err / codes are complete
+  // row loss ½·Σ err² from the staged errors: 8 columns per lane, then the row
+  float loss = 0.f;
 #pragma unroll
-    for (int k = 0; k < QC; k += 4) {
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float e = SE[rloc * SROW + 64 * h + 4 * c + q];
+      loss = fmaf(e, e, loss);
+    }
+  loss += dpp<0xB1>(loss);
+  loss += dpp<0x4E>(loss);
+  loss += dpp<0x141>(loss);
+  loss += dpp<0x140>(loss);
+  if (live && c == 0 && a.row_loss) a.row_loss[r] += 0.5f * loss;
+  // write back: lane c stores its row's columns 4c..4c+3 and 64+4c..64+4c+3
+  if (live) {
+    float* dw = a.Wk + r * a.ldw + a.b0 + 4 * c;
+    float* de = a.Err + r * kBlock + 4 * c;
+    uint8_t* dq = a.codes + r * a.ldw + a.b0 + 4 * c;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
       f32x4 vw, ve;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        vw[q] = SW[rloc * SROW + c * QC + k + q];
-        ve[q] = SE[rloc * SROW + c * QC + k + q];
+        vw[q] = w[4 * h + q];
+        ve[q] = SE[rloc * SROW + 64 * h + 4 * c + q];
       }
-      *reinterpret_cast<f32x4*>(dw + k) = vw;
-      *reinterpret_cast<f32x4*>(de + k) = ve;
-      *reinterpret_cast<uint32_t*>(dq + k) =
-          *reinterpret_cast<const uint32_t*>(SQ + rloc * QROW + c * QC + k);
+      const uint32_t pk = *reinterpret_cast<const uint32_t*>(SQ + rloc * QROW + 64 * h + 4 * c);
+      *reinterpret_cast<f32x4*>(dw + 64 * h) = vw;
+      *reinterpret_cast<f32x4*>(de + 64 * h) = ve;
+      *reinterpret_cast<uint32_t*>(dq + 64 * h) = pk;
     }
   }
 }
@@ -198,10 +243,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
 template <>
 hipError_t launch_sweep<GQ_SWEEP_G>(const SweepArgs& a, hipStream_t s) {
   // waves per workgroup: enough workgroups to cover the CUs, at most 4 waves
-  const int64_t waves = ceil_div(a.m, 16);
+  const int64_t waves = ceil_div(a.m, 4);
   const int W = (int)std::max<int64_t>(1, std::min<int64_t>(4, waves / 256));
-  const size_t dyn = (size_t)W * kWaveStage;
-  sweep_kernel<GQ_SWEEP_G><<<(unsigned)ceil_div(waves, W), 64 * W, dyn, s>>>(a);
+  sweep_kernel<GQ_SWEEP_G><<<(unsigned)ceil_div(waves, W), 64 * W, 0, s>>>(a);
   return hipGetLastError();
 }
 
