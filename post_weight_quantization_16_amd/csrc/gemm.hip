@@ -1,239 +1,21 @@
 // fp32 MFMA GEMM for gfx950: the lazy block update of the GPTQ sweep and the
-// trailing updates of the blocked Cholesky / triangular inverse.
-//
-// Tile 128x128 per workgroup of 256 threads (4 waves in a 2x2 grid, each wave
-// 64x64 = 2x2 tiles of v_mfma_f32_32x32x2f32, whose operands are one float per
-// lane: A(m = lane%32, k = lane/32) and B(k = lane/32, n = lane%32)).
-// K advances in chunks of 32 through a double-buffered LDS stage: the next
-// chunk is fetched into registers while the current one is multiplied, then
-// stored into the other buffer; one barrier per chunk.  Each operand is kept
-// in LDS in its memory orientation:
-//   contiguous along m (or n): [k][128 + 32] -- a half-wave reads 32
-//     consecutive words, the other half-wave's row is 32 banks away;
-//   contiguous along k: [m][32 + 2] -- the odd-pair stride 34 sends the 32
-//     rows a half-wave reads to 32 distinct banks.
-// 80 KB of LDS, so two workgroups share a CU.
-#include "common.hpp"
+// trailing updates of the triangular inverse (the tile itself is in
+// gemm_tile.hpp).
+#include "gemm_tile.hpp"
 
 namespace gq {
+namespace gemm_detail {
 namespace {
-
-constexpr int TM = 128, TN = 128, TK = 32;
-constexpr int SA = TM + 32;   // stride of a [k][128] operand (floats)
-constexpr int SK = TK + 2;    // stride of a [128][k] operand (floats)
-constexpr int OPF = TK * SA > TM * SK ? TK * SA : TM * SK;   // floats per operand buffer
-static_assert(TM * (TN + 8) <= 4 * OPF, "the epilogue tile must fit in the operand buffers");
-
-struct KArgs {
-  int M, N, K, k_last;
-  int k_from_n, k_to_m;
-  float alpha, beta;
-  const float* A; int64_t lda, strideA;
-  const float* B; int64_t ldb, strideB;
-  float* C; int64_t ldc, strideC;
-  int tri;
-  int vec_a, vec_b, vec_c;
-};
-
-// One 32 x 128 operand chunk in registers: 4 float4 per thread.
-// ALONG: the 128-wide dimension is contiguous in memory; otherwise k is.
-template <bool ALONG>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t ld, int rows_valid,
-                                           int k0, int kvalid, int t, bool vec, f32x4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = t + 256 * i;
-    int a, b;  // a: index along the 128-wide dim, b: k
-    if (ALONG) { b = idx >> 5; a = (idx & 31) * 4; }
-    else       { a = idx >> 3; b = (idx & 7) * 4; }
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (ALONG) {
-      const int kk = k0 + b;
-      if (kk < kvalid) {
-        const float* q = p + (int64_t)kk * ld + a;
-        if (vec && a + 3 < rows_valid) {
-          v = *reinterpret_cast<const f32x4*>(q);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (a + j < rows_valid) ? q[j] : 0.f;
-        }
-      }
-    } else {
-      if (a < rows_valid) {
-        const float* q = p + (int64_t)a * ld + k0 + b;
-        if (vec && k0 + b + 3 < kvalid) {
-          v = *reinterpret_cast<const f32x4*>(q);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (k0 + b + j < kvalid) ? q[j] : 0.f;
-        }
-      }
-    }
-    r[i] = v;
-  }
-}
-
-template <bool ALONG>
-__device__ __forceinline__ void store_chunk(float* __restrict__ s, int t, const f32x4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = t + 256 * i;
-    if (ALONG) {
-      const int b = idx >> 5, a = (idx & 31) * 4;
-      *reinterpret_cast<f32x4*>(s + b * SA + a) = r[i];
-    } else {
-      const int a = idx >> 3, b = (idx & 7) * 4;
-      typedef __attribute__((ext_vector_type(2))) float f32x2;
-      f32x2 lo = {r[i][0], r[i][1]}, hi = {r[i][2], r[i][3]};
-      *reinterpret_cast<f32x2*>(s + a * SK + b) = lo;
-      *reinterpret_cast<f32x2*>(s + a * SK + b + 2) = hi;
-    }
-  }
-}
-
-template <bool ALONG>
-__device__ __forceinline__ float opread(const float* s, int a, int k) {
-  return ALONG ? s[k * SA + a] : s[a * SK + k];
-}
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g) {
-  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
-  if (g.tri == 1 && n0 > m0 + TM - 1) return;
-  if (g.tri == 2 && n0 + TN - 1 < m0) return;
-  const int z = blockIdx.z;
-  const int Kz = (z == (int)gridDim.z - 1) ? g.k_last : g.K;
-  const int kbeg = g.k_from_n ? (n0 / TK) * TK : 0;
-  const int K = g.k_to_m ? min(Kz, m0 + TM) : Kz;
-  const float* A = g.A + (int64_t)z * g.strideA;
-  const float* B = g.B + (int64_t)z * g.strideB;
-  float* C = g.C + (int64_t)z * g.strideC;
-
-  // A: op(A)(m,k); TA: stored [K x M] (m contiguous) -> ALONG.  B: TB stored [N x K].
-  constexpr bool AL_A = TA, AL_B = !TB;
-  __shared__ __attribute__((aligned(16))) float Sm[2][2][OPF];
-
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const float* Ab = TA ? A + m0 : A + (int64_t)m0 * g.lda;
-  const float* Bb = TB ? B + (int64_t)n0 * g.ldb : B + n0;
-  const int mvalid = g.M - m0, nvalid = g.N - n0;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  f32x4 ra[4], rb[4];
-  if (kbeg < K) {
-    load_chunk<AL_A>(Ab, g.lda, mvalid, kbeg, K, t, g.vec_a, ra);
-    load_chunk<AL_B>(Bb, g.ldb, nvalid, kbeg, K, t, g.vec_b, rb);
-    store_chunk<AL_A>(Sm[0][0], t, ra);
-    store_chunk<AL_B>(Sm[0][1], t, rb);
-  }
-  __syncthreads();
-
-  int buf = 0;
-  for (int k0 = kbeg; k0 < K; k0 += TK) {
-    const bool more = k0 + TK < K;
-    if (more) {
-      load_chunk<AL_A>(Ab, g.lda, mvalid, k0 + TK, K, t, g.vec_a, ra);
-      load_chunk<AL_B>(Bb, g.ldb, nvalid, k0 + TK, K, t, g.vec_b, rb);
-    }
-    const float* As = Sm[buf][0];
-    const float* Bs = Sm[buf][1];
-#pragma unroll
-    for (int kk = 0; kk < TK / 2; ++kk) {
-      const int ka = kk * 2 + (lane >> 5);
-      const float a0 = opread<AL_A>(As, wm * 64 + (lane & 31), ka);
-      const float a1 = opread<AL_A>(As, wm * 64 + 32 + (lane & 31), ka);
-      const float b0 = opread<AL_B>(Bs, wn * 64 + (lane & 31), ka);
-      const float b1 = opread<AL_B>(Bs, wn * 64 + 32 + (lane & 31), ka);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-    }
-    if (more) {
-      store_chunk<AL_A>(Sm[buf ^ 1][0], t, ra);
-      store_chunk<AL_B>(Sm[buf ^ 1][1], t, rb);
-    }
-    __syncthreads();
-    buf ^= 1;
-  }
-
-  // Epilogue through LDS (the operand buffers are free after the loop's last
-  // barrier): the tile goes to LDS as alpha·acc, then every thread owns 16
-  // float4 of it.  All of a thread's C reads are issued before any of its
-  // writes -- C is read and written through one pointer, so reads placed
-  // after writes would each wait for a full memory round trip.
-  // MFMA layout: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32.
-  constexpr int ES = TN + 8;   // 4·ES ≡ 32 (mod 64): the half-waves' rows hit disjoint banks
-  float* E = &Sm[0][0][0];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = wn * 64 + j * 32 + (lane & 31);
-        E[row * ES + col] = g.alpha * acc[i][j][r];
-      }
-  __syncthreads();
-  const bool has_beta = g.beta != 0.f;
-  const bool tri_all = g.tri == 0 || (g.tri == 1 && n0 + TN - 1 <= m0) ||
-                       (g.tri == 2 && n0 >= m0 + TM - 1);
-  if (tri_all && mvalid >= TM && nvalid >= TN && g.vec_c) {
-    f32x4 cv[16];
-    if (has_beta) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int idx = t + 256 * u, row = idx >> 5, c4 = (idx & 31) * 4;
-        cv[u] = *reinterpret_cast<const f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = t + 256 * u, row = idx >> 5, c4 = (idx & 31) * 4;
-      f32x4 v = *reinterpret_cast<const f32x4*>(E + row * ES + c4);
-      if (has_beta) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = fmaf(g.beta, cv[u][q], v[q]);
-      }
-      *reinterpret_cast<f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4) = v;
-    }
-  } else {
-    // edge or diagonal tile: element-wise, reads (at clamped, valid
-    // addresses) batched ahead of the masked writes 16 at a time
-    for (int e0 = 0; e0 < TM * TN; e0 += 256 * 16) {
-      float cs[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = e0 + t + 256 * u, row = e / TN, col = e % TN;
-        const int rr = min(row, mvalid - 1), cc = min(col, nvalid - 1);
-        cs[u] = has_beta ? C[(int64_t)(m0 + rr) * g.ldc + n0 + cc] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = e0 + t + 256 * u, row = e / TN, col = e % TN;
-        const int gr = m0 + row, gc = n0 + col;
-        bool ok = row < mvalid && col < nvalid;
-        if (g.tri == 1) ok = ok && gc <= gr;
-        if (g.tri == 2) ok = ok && gc >= gr;
-        if (ok) C[(int64_t)gr * g.ldc + gc] = fmaf(g.beta, cs[u], E[row * ES + col]);
-      }
-    }
-  }
+  __shared__ __attribute__((aligned(16))) float Sm[GEMM_SMEM_FLOATS];
+  gemm_tile<TA, TB>(g, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, Sm);
 }
 
 }  // namespace
 
-hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
+KArgs make_kargs(const GemmArgs& a) {
   KArgs k;
   k.M = a.M; k.N = a.N; k.K = a.K; k.k_last = a.k_last;
   k.k_from_n = a.k_from_n; k.k_to_m = a.k_to_m;
@@ -248,6 +30,15 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   k.vec_a = aligned(a.A, a.lda, a.strideA);
   k.vec_b = aligned(a.B, a.ldb, a.strideB);
   k.vec_c = aligned(a.C, a.ldc, a.strideC);
+  return k;
+}
+
+}  // namespace gemm_detail
+
+hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
+  using namespace gemm_detail;
+  if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
+  const KArgs k = make_kargs(a);
   dim3 grid((unsigned)ceil_div(a.N, TN), (unsigned)ceil_div(a.M, TM), (unsigned)a.batch);
   if (!a.trans_a && !a.trans_b) gemm_f32_kernel<false, false><<<grid, 256, 0, s>>>(k);
   else if (!a.trans_a && a.trans_b) gemm_f32_kernel<false, true><<<grid, 256, 0, s>>>(k);

@@ -13,14 +13,16 @@
 // U = J·L⁻¹·J, the unique upper factor with positive diagonal.  Two O(d³)
 // steps, both fp32: a blocked right-looking Cholesky with 64-wide panels
 // (each diagonal block factored and inverted together, the panel below
-// solved with that inverse in the same launch, the trailing SYRK on the
-// fp32 MFMA GEMM), then the rest of the triangular inverse by recursive
+// solved with that inverse; one launch per panel that also runs the previous
+// panel's trailing update on fp32 MFMA GEMM tiles), then the rest of the
+// triangular inverse by recursive
 // doubling ([[A,0],[B,C]]⁻¹ has off-diagonal block −C⁻¹·B·A⁻¹, products
 // skipping the zero triangles).
 #include <algorithm>
 #include <climits>
 
 #include "common.hpp"
+#include "gemm_tile.hpp"
 
 namespace gq {
 namespace {
@@ -115,7 +117,37 @@ __global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, in
   }
 }
 
-// One 64-wide Cholesky panel at column k0 (kb <= 64 columns):
+struct PanelArgs {
+  float* G; int64_t d; int k0, kb;
+  float* Linv; int* status;
+};
+
+constexpr int LS = NB + 2;       // LDS row stride: the half-waves' MFMA reads hit disjoint banks
+constexpr int BLK = NB * LS;     // one 64x64 block in LDS (floats)
+static_assert(4 * BLK + 4 * NB <= gemm_detail::GEMM_SMEM_FLOATS, "panel LDS exceeds the shared buffer");
+
+// acc += S1 · S2ᵀ for one 32x32 tile (rows 32mi.., columns 32ni..) of two
+// 64x64 LDS blocks; v_mfma_f32_32x32x2f32 takes A(m = lane%32, k = lane/32),
+// B(k, n = lane%32), so both operands are read along their rows
+__device__ __forceinline__ void mfma_abt(const float* S1, const float* S2, int mi, int ni,
+                                         int lane, f32x16& acc) {
+#pragma unroll
+  for (int kk = 0; kk < NB / 2; ++kk) {
+    const int k = 2 * kk + (lane >> 5);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(S1[(32 * mi + (lane & 31)) * LS + k],
+                                               S2[(32 * ni + (lane & 31)) * LS + k], acc, 0, 0, 0);
+  }
+}
+// row / column of accumulator element e in the 32x32 tile (mi, ni)
+__device__ __forceinline__ int acc_row(int mi, int lane, int e) {
+  return 32 * mi + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+}
+
+// One 64-wide Cholesky panel at column k0 (kb <= 64 columns), for workgroup
+// b of the panel's grid:
+//   first, the previous panel's contribution to this panel's columns,
+//     G[:, panel] −= L21ₚ·L21ₚ[panel rows]ᵀ (the trailing update of the
+//     previous step skips these columns so this launch can run it),
 //   L11 = chol(G11),  X = L11⁻¹,  L21 = G21·Xᵀ.
 // Every workgroup (4 waves) factors and inverts the small diagonal block
 // itself, so no workgroup waits for another; workgroup b then solves the
@@ -132,33 +164,54 @@ __global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, in
 // zeroed entries make the update a no-op where k <= j, so it needs no
 // masks.  A non-positive (or NaN/inf) pivot is recorded in *status
 // (smallest index wins) and replaced by 1 so the arithmetic stays finite.
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ G, int64_t d, int k0,
-                                                    int kb, float* __restrict__ Linv,
-                                                    int* __restrict__ status) {
-  constexpr int LS = NB + 2;  // row stride: the two half-waves' MFMA reads hit disjoint banks
-  __shared__ float AS[NB * LS];    // G11, then this workgroup's block of G21
-  __shared__ float XS[NB * LS];    // X
-  __shared__ float pub[2][2][NB];  // [step parity][l, x][lane]
+__device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __restrict__ smem) {
+  float* AS = smem;              // G11 (lower, identity-padded)
+  float* BS = smem + BLK;        // this workgroup's 64 rows of G21
+  float* XS = smem + 2 * BLK;    // X; before the sweep: the previous panel's rows k0..k0+63
+  float* QS = smem + 3 * BLK;    // the previous panel's values in this workgroup's rows
+  float* pub = smem + 4 * BLK;   // [step parity][l, x][lane]
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  const int64_t R0 = (int64_t)k0 + kb + (int64_t)blockIdx.x * NB;
+  const int64_t d = p.d;
+  const int k0 = p.k0, kb = p.kb;
+  const int64_t R0 = (int64_t)k0 + kb + (int64_t)b * NB;
+  const bool upd = k0 > 0;       // previous panels are full width
+  const int kp = k0 - NB;
+  float* G = p.G;
 
-  // the block of G21 this workgroup solves, fetched now and used after the sweep
-  float pre[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + 256 * u, rr = idx >> 6, cc = idx & 63;
-    const bool ok = R0 + rr < d && cc < kb;
-    const float v = G[(ok ? R0 + rr : 0) * d + (ok ? k0 + cc : 0)];
-    pre[u] = ok ? v : 0.f;
-  }
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-    const bool ok = i < kb && k <= i;
-    const float v = G[(int64_t)(k0 + (ok ? i : 0)) * d + k0 + (ok ? k : 0)];
-    AS[i * LS + k] = ok ? v : (i == k ? 1.f : 0.f);
+    const bool okd = i < kb && k <= i;
+    const float vd = G[(int64_t)(k0 + (okd ? i : 0)) * d + k0 + (okd ? k : 0)];
+    AS[i * LS + k] = okd ? vd : (i == k ? 1.f : 0.f);
+    const bool okb = R0 + i < d && k < kb;
+    const float vb = G[(okb ? R0 + i : 0) * d + (okb ? k0 + k : 0)];
+    BS[i * LS + k] = okb ? vb : 0.f;
+    if (upd) {
+      const bool okp = i < kb;
+      const float vp = G[(int64_t)(k0 + (okp ? i : 0)) * d + kp + k];
+      XS[i * LS + k] = okp ? vp : 0.f;
+      const bool okq = R0 + i < d;
+      const float vq = G[(okq ? R0 + i : 0) * d + kp + k];
+      QS[i * LS + k] = okq ? vq : 0.f;
+    }
   }
   __syncthreads();
+  const int mi = w >> 1, ni = w & 1;
+  if (upd) {
+    f32x16 dacc, eacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dacc[e] = 0.f; eacc[e] = 0.f; }
+    mfma_abt(XS, XS, mi, ni, lane, dacc);
+    mfma_abt(QS, XS, mi, ni, lane, eacc);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int o = acc_row(mi, lane, e) * LS + 32 * ni + (lane & 31);
+      AS[o] -= dacc[e];
+      BS[o] -= eacc[e];
+    }
+    __syncthreads();
+  }
   float a[16], r[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -170,6 +223,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ G, int64
 #pragma unroll
     for (int q0 = 0; q0 < 16; ++q0) {
       const int j = jb * 16 + q0, par = q0 & 1;
+      float* pl = pub + par * 2 * NB;
       if (w == jb) {
         const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
         const bool bad = !(piv > 0.f) || !(piv < INFINITY);
@@ -182,14 +236,14 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ G, int64
         a[q0] = lane > j ? l : (lane == j ? ljj : 0.f);
         const float x = r[q0] * inv;
         r[q0] = x;
-        pub[par][0][lane] = lane > j ? l : 0.f;
-        pub[par][1][lane] = x;
+        pl[lane] = lane > j ? l : 0.f;
+        pl[NB + lane] = x;
       }
       __syncthreads();
-      const float li = pub[par][0][lane], xv = pub[par][1][lane];
+      const float li = pl[lane], xv = pl[NB + lane];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float c = pub[par][0][16 * w + q];
+        const float c = pl[16 * w + q];
         a[q] = fmaf(-li, c, a[q]);
         r[q] = fmaf(-c, xv, r[q]);
       }
@@ -197,38 +251,52 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ G, int64
   }
 #pragma unroll
   for (int q = 0; q < 16; ++q) XS[(16 * w + q) * LS + lane] = r[q];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + 256 * u;
-    AS[(idx >> 6) * LS + (idx & 63)] = pre[u];
-  }
   __syncthreads();
-  if (blockIdx.x == 0) {
-    if (lane == 0 && bad_j >= 0) atomicMin(status, k0 + bad_j);
+  if (b == 0) {
+    if (lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
     for (int e = t; e < kb * kb; e += 256) {
       const int rr = e / kb, c = e % kb;
-      Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr * LS + c];
+      p.Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr * LS + c];
     }
   }
   if (R0 >= d) return;
-  // L21 block = G21 block · Xᵀ: wave w computes the 32x32 tile (w/2, w%2);
-  // v_mfma_f32_32x32x2f32 takes A(m = lane%32, k = lane/32), B(k, n = lane%32)
-  const int mi = w >> 1, ni = w & 1;
+  // L21 block = G21 block · Xᵀ, wave w the 32x32 tile (w/2, w%2)
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < NB / 2; ++kk) {
-    const int k = 2 * kk + (lane >> 5);
-    const float av = AS[(32 * mi + (lane & 31)) * LS + k];
-    const float bv = XS[(32 * ni + (lane & 31)) * LS + k];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-  }
+  mfma_abt(BS, XS, mi, ni, lane, acc);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int row = 32 * mi + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-    const int col = 32 * ni + (lane & 31);
+    const int row = acc_row(mi, lane, e), col = 32 * ni + (lane & 31);
     if (R0 + row < d && col < kb) G[(R0 + row) * d + k0 + col] = acc[e];
+  }
+}
+
+// Lower-triangular tile enumeration: L -> (row by, column bx <= by).
+__device__ __forceinline__ void lower_tile(int L, int& by, int& bx) {
+  int y = (int)((sqrtf(8.f * (float)L + 1.f) - 1.f) * 0.5f);
+  while ((y + 1) * (y + 2) / 2 <= L) ++y;
+  while (y * (y + 1) / 2 > L) --y;
+  by = y;
+  bx = L - y * (y + 1) / 2;
+}
+
+// One step of the blocked Cholesky: workgroups [0, nP) run panel k (its
+// columns first receive the previous panel's update), the rest run the
+// previous panel's trailing update of the columns beyond panel k,
+// G22 −= L21ₚ·L21ₚᵀ (lower tiles only, fp32 MFMA GEMM tiles).  The two sets
+// touch disjoint parts of G: the panel reads the previous panel's columns
+// and writes its own, the update writes only columns right of the panel.
+__global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP,
+                                                        gemm_detail::KArgs tr) {
+  __shared__ __attribute__((aligned(16))) float smem[gemm_detail::GEMM_SMEM_FLOATS];
+  const int L = blockIdx.x;
+  if (L < nP) {
+    panel_body(p, L, smem);
+  } else {
+    int by, bx;
+    lower_tile(L - nP, by, bx);
+    gemm_detail::gemm_tile<false, true>(tr, bx, by, 0, 1, smem);
   }
 }
 
@@ -293,23 +361,29 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();
 
-  // blocked right-looking Cholesky of G (lower), 64-wide panels: one fused
-  // factor / inverse / panel-solve launch and the trailing SYRK on the fp32
-  // MFMA GEMM
+  // blocked right-looking Cholesky of G (lower), 64-wide panels, one launch
+  // per panel: the panel itself and, beside it, the previous panel's
+  // trailing update of the columns beyond it
   for (int64_t k0 = 0; k0 < d; k0 += NB) {
     const int kb = (int)std::min<int64_t>(NB, d - k0);
     const int64_t r0 = k0 + kb, nr = d - r0;
-    const unsigned nblk = (unsigned)std::max<int64_t>(1, ceil_div(nr, NB));
-    panel_kernel<<<nblk, 256, 0, s>>>(w.G, d, (int)k0, kb, w.Linv, w.status);
+    const int nP = (int)std::max<int64_t>(1, ceil_div(nr, NB));
+    PanelArgs pa{w.G, d, (int)k0, kb, w.Linv, w.status};
+    gemm_detail::KArgs tr{};
+    int64_t nT = 0;
+    if (k0 > 0 && nr > 0) {
+      GemmArgs h{};  // G[r0:, r0:] −= L21ₚ · L21ₚᵀ  (lower triangle)
+      h.M = (int)nr; h.N = (int)nr; h.K = NB; h.k_last = NB; h.batch = 1;
+      h.alpha = -1.f; h.beta = 1.f;
+      h.A = w.G + r0 * d + (k0 - NB); h.lda = d; h.trans_a = false;
+      h.B = w.G + r0 * d + (k0 - NB); h.ldb = d; h.trans_b = true;
+      h.C = w.G + r0 * d + r0; h.ldc = d; h.tri = 1;
+      tr = gemm_detail::make_kargs(h);
+      const int64_t nb = ceil_div(nr, 128);
+      nT = nb * (nb + 1) / 2;
+    }
+    chol_step_kernel<<<(unsigned)(nP + nT), 256, 0, s>>>(pa, nP, tr);
     GQ_CHECK();
-    if (nr <= 0) break;
-    GemmArgs h{};  // G22 −= L21 · L21ᵀ  (lower triangle)
-    h.M = (int)nr; h.N = (int)nr; h.K = kb; h.k_last = kb; h.batch = 1;
-    h.alpha = -1.f; h.beta = 1.f;
-    h.A = w.G + r0 * d + k0; h.lda = d; h.trans_a = false;
-    h.B = w.G + r0 * d + k0; h.ldb = d; h.trans_b = true;
-    h.C = w.G + r0 * d + r0; h.ldc = d; h.tri = 1;
-    if ((e = gemm_f32(h, s)) != hipSuccess) return e;
   }
 
   // triangular inverse by recursive doubling on 64-aligned blocks
