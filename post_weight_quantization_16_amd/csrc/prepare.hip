@@ -155,22 +155,34 @@ __device__ __forceinline__ int acc_row(int mi, int lane, int e) {
 // in place in G, and workgroup 0 stores X into the diagonal block of Linv
 // (L11 itself is not needed later).  The block is padded to 64 with the
 // identity.
+//
 // The factor and the inverse are one right-looking sweep.  Lane i of wave w
-// holds A[i][16w..16w+15] (a) and X[16w..16w+15][i] (r).  Step j: the wave
-// owning column j takes the pivot from lane j, scales the column into
-// l_ij = a_ij / l_jj and finishes x_j = r_j / l_jj, and publishes both
-// through LDS with l_ij zeroed for i <= j; after one barrier every lane
-// applies a_ik −= l_ij·l_kj and r_k −= l_kj·x_j to its 16 columns -- the
-// zeroed entries make the update a no-op where k <= j, so it needs no
-// masks.  A non-positive (or NaN/inf) pivot is recorded in *status
-// (smallest index wins) and replaced by 1 so the arithmetic stays finite.
+// holds A[i][16w..16w+15] (a) and X[16w..16w+15][i] (r).  Wave w owns steps
+// 16w..16w+15: step j takes the pivot from lane j, scales column j into
+// l_ij = a_ij / l_jj (zeroed for i <= j), finishes x_j = r_j / l_jj, applies
+// a_ik −= l_ij·l_kj and r_k −= l_kj·x_j to its own later columns (l_kj read
+// from lane k with readlane) and publishes l and x for step j in LDS with a
+// flag.  Before its own steps, wave w consumes steps 0 .. 16w−1 as their
+// flags appear, applying the same update to its 16 columns.  The owner of a
+// step never waits for another wave, so the serial chain carries no
+// workgroup barrier; every wait is on a step some wave has already begun or
+// will begin without waiting (wave 0 waits for nothing), and is bounded.
+// A non-positive (or NaN/inf) pivot is recorded in *status (smallest index
+// wins) and replaced by 1 so the arithmetic stays finite.
+constexpr int kSpinLimit = 1 << 20;   // safety bound on a flag wait (never reached)
+
 __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __restrict__ smem) {
   float* AS = smem;              // G11 (lower, identity-padded)
   float* BS = smem + BLK;        // this workgroup's 64 rows of G21
   float* XS = smem + 2 * BLK;    // X; before the sweep: the previous panel's rows k0..k0+63
   float* QS = smem + 3 * BLK;    // the previous panel's values in this workgroup's rows
-  float* pub = smem + 4 * BLK;   // [step parity][l, x][lane]
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  // during the sweep XS and QS hold the published steps: l [64][64], x [64][64], flags [64]
+  float* PL = smem + 2 * BLK;
+  float* PX = PL + NB * NB;
+  int* flag = reinterpret_cast<int*>(PX + NB * NB);
+  static_assert(2 * NB * NB + NB <= 2 * BLK, "published steps exceed their LDS region");
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t d = p.d;
   const int k0 = p.k0, kb = p.kb;
   const int64_t R0 = (int64_t)k0 + kb + (int64_t)b * NB;
@@ -178,22 +190,44 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   const int kp = k0 - NB;
   float* G = p.G;
 
+  {
+    // all loads first, then the LDS stores (a load-store pair per element
+    // would wait a memory round trip each)
+    float va[16], vb[16];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-    const bool okd = i < kb && k <= i;
-    const float vd = G[(int64_t)(k0 + (okd ? i : 0)) * d + k0 + (okd ? k : 0)];
-    AS[i * LS + k] = okd ? vd : (i == k ? 1.f : 0.f);
-    const bool okb = R0 + i < d && k < kb;
-    const float vb = G[(okb ? R0 + i : 0) * d + (okb ? k0 + k : 0)];
-    BS[i * LS + k] = okb ? vb : 0.f;
+    for (int u = 0; u < 16; ++u) {
+      const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
+      const bool okd = i < kb && k <= i;
+      va[u] = G[(int64_t)(k0 + (okd ? i : 0)) * d + k0 + (okd ? k : 0)];
+      va[u] = okd ? va[u] : (i == k ? 1.f : 0.f);
+      const bool okb = R0 + i < d && k < kb;
+      vb[u] = G[(okb ? R0 + i : 0) * d + (okb ? k0 + k : 0)];
+      vb[u] = okb ? vb[u] : 0.f;
+    }
     if (upd) {
-      const bool okp = i < kb;
-      const float vp = G[(int64_t)(k0 + (okp ? i : 0)) * d + kp + k];
-      XS[i * LS + k] = okp ? vp : 0.f;
-      const bool okq = R0 + i < d;
-      const float vq = G[(okq ? R0 + i : 0) * d + kp + k];
-      QS[i * LS + k] = okq ? vq : 0.f;
+      float vp[16], vq[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
+        const bool okp = i < kb;
+        vp[u] = G[(int64_t)(k0 + (okp ? i : 0)) * d + kp + k];
+        vp[u] = okp ? vp[u] : 0.f;
+        const bool okq = R0 + i < d;
+        vq[u] = G[(okq ? R0 + i : 0) * d + kp + k];
+        vq[u] = okq ? vq[u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
+        XS[i * LS + k] = vp[u];
+        QS[i * LS + k] = vq[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
+      AS[i * LS + k] = va[u];
+      BS[i * LS + k] = vb[u];
     }
   }
   __syncthreads();
@@ -210,50 +244,85 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
       AS[o] -= dacc[e];
       BS[o] -= eacc[e];
     }
-    __syncthreads();
   }
+  __syncthreads();
   float a[16], r[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     a[q] = AS[lane * LS + 16 * w + q];
     r[q] = (16 * w + q == lane) ? 1.f : 0.f;
   }
+  if (t < NB) flag[t] = 0;
+  __syncthreads();
+
+  // consume the steps of the waves before this one, four at a time: one
+  // wait on the fourth step's flag covers all four (one wave publishes them
+  // in order, each flag a release of the writes before it)
   int bad_j = -1;
-  for (int jb = 0; jb < 4; ++jb) {
-#pragma unroll
-    for (int q0 = 0; q0 < 16; ++q0) {
-      const int j = jb * 16 + q0, par = q0 & 1;
-      float* pl = pub + par * 2 * NB;
-      if (w == jb) {
-        const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
-        const bool bad = !(piv > 0.f) || !(piv < INFINITY);
-        bad_j = (bad && bad_j < 0) ? j : bad_j;
-        // one hardware reciprocal square root on the serial chain (about
-        // 1 ulp; 1/l_jj and l_jj = piv·(1/l_jj) both come from it)
-        const float inv = bad ? 1.f : __builtin_amdgcn_rsqf(piv);
-        const float ljj = bad ? 1.f : piv * inv;
-        const float l = a[q0] * inv;
-        a[q0] = lane > j ? l : (lane == j ? ljj : 0.f);
-        const float x = r[q0] * inv;
-        r[q0] = x;
-        pl[lane] = lane > j ? l : 0.f;
-        pl[NB + lane] = x;
+  bool stalled = false;   // after one expired wait, stop waiting (the result is flagged bad)
+  for (int j0 = 0; j0 < 16 * w; j0 += 4) {
+    int spin = 0;
+    while (!stalled &&
+           __hip_atomic_load(&flag[j0 + 3], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+      if (++spin > kSpinLimit) {
+        stalled = true;
+        bad_j = (bad_j < 0) ? j0 : bad_j;
       }
-      __syncthreads();
-      const float li = pl[lane], xv = pl[NB + lane];
+      __builtin_amdgcn_s_sleep(1);
+    }
+    float li[4], xv[4];
+    f32x4 cv[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      li[u] = PL[(j0 + u) * NB + lane];
+      xv[u] = PX[(j0 + u) * NB + lane];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        cv[u][h] = *reinterpret_cast<const f32x4*>(PL + (j0 + u) * NB + 16 * w + 4 * h);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float c = pl[16 * w + q];
-        a[q] = fmaf(-li, c, a[q]);
-        r[q] = fmaf(-c, xv, r[q]);
+        const float c = cv[u][q >> 2][q & 3];
+        a[q] = fmaf(-li[u], c, a[q]);
+        r[q] = fmaf(-c, xv[u], r[q]);
       }
-    }
   }
+  // own steps: the next column's update first (it feeds the next pivot),
+  // then the publication, the remaining columns, and the step's flag
+#pragma unroll
+  for (int q0 = 0; q0 < 16; ++q0) {
+    const int j = 16 * w + q0;
+    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
+    const bool bad = !(piv > 0.f) || !(piv < INFINITY);
+    bad_j = (bad && bad_j < 0) ? j : bad_j;
+    // one hardware reciprocal square root on the serial chain (about 1 ulp)
+    const float inv = bad ? 1.f : __builtin_amdgcn_rsqf(piv);
+    const float l = lane > j ? a[q0] * inv : 0.f;
+    const float x = r[q0] * inv;
+    r[q0] = x;
+    if (q0 + 1 < 16) {
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), j + 1));
+      a[q0 + 1] = fmaf(-l, c, a[q0 + 1]);
+      r[q0 + 1] = fmaf(-c, x, r[q0 + 1]);
+    }
+    PL[j * NB + lane] = l;
+    PX[j * NB + lane] = x;
+#pragma unroll
+    for (int q = q0 + 2; q < 16; ++q) {
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 16 * w + q));
+      a[q] = fmaf(-l, c, a[q]);
+      r[q] = fmaf(-c, x, r[q]);
+    }
+    __hip_atomic_store(&flag[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
 #pragma unroll
   for (int q = 0; q < 16; ++q) XS[(16 * w + q) * LS + lane] = r[q];
   __syncthreads();
+  if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
   if (b == 0) {
-    if (lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
     for (int e = t; e < kb * kb; e += 256) {
       const int rr = e / kb, c = e % kb;
       p.Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr * LS + c];
