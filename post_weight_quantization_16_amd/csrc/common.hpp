@@ -18,6 +18,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kBlock = 128;   // lazy-update block width B used by this library
 constexpr int kPanel = 64;    // Cholesky panel width
+constexpr int kSuper = 4;     // blocks per super-block of the two-level lazy update
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -84,7 +85,7 @@ struct SweepArgs {
   const float* Ublk; int64_t ldu; // U's diagonal block for this block (row j at Ublk + j*ldu)
   int maxq, sym;
   float* scales; uint8_t* zeros; int ng; int64_t g;
-  float* Err;                     // [m x 128]
+  float* Err; int64_t lde;        // the block's errors: [m x 128] at Err, row stride lde
   uint8_t* codes;                 // [m x ldw]
   float* row_loss;                // may be null
 };

@@ -338,39 +338,58 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
       }
 }
 
-// H[j][i] = H[i][j] for i < j: 64x64 tiles of the upper triangle through LDS.
-__global__ __launch_bounds__(256) void mirror_kernel(float* __restrict__ H, int d, int nb) {
-  int bi, bj;
-  tile_of(blockIdx.x, nb, bi, bj);
-  __shared__ float Tl[64][65];
-  const int t = threadIdx.x;
-  for (int e = t; e < 64 * 64; e += 256) {
-    const int a = e >> 6, b = e & 63;
-    const int i = bi * 64 + a, j = bj * 64 + b;
-    Tl[a][b] = (i < d && j < d) ? H[(int64_t)i * d + j] : 0.f;
-  }
-  __syncthreads();
-  for (int e = t; e < 64 * 64; e += 256) {
-    const int b = e >> 6, a = e & 63;   // write row j = bj*64+b, column i = bi*64+a
-    const int i = bi * 64 + a, j = bj * 64 + b;
-    if (i < d && j < d && i < j) H[(int64_t)j * d + i] = Tl[a][b];
-  }
-}
-
-// H[i][j] += 2·Σ_s P_s[i][j] for i <= j (the mirror kernel fills i > j).
-__global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ H, int d,
-                                                          const float* __restrict__ P, int64_t dp,
-                                                          int splits, int nt) {
+// H[i][j] += 2·Σ_s P_s[i][j] over the upper triangle, and the mirrored
+// H[j][i] = H[i][j], one 128x128 upper tile (ti <= tj) per workgroup.  The
+// split partials are summed in a fixed order (deterministic); each thread
+// owns float4 runs of the tile, and the finished tile goes through LDS to
+// be written transposed, so both writes are coalesced.
+__global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
+                                                            const float* __restrict__ P,
+                                                            int64_t dp, int splits, int nt,
+                                                            int vec_h) {
   int ti, tj;
   tile_of(blockIdx.x, nt, ti, tj);
-  for (int e = threadIdx.x; e < HT * HT; e += 256) {
-    const int a = e / HT, b = e % HT;
-    if (ti == tj && a > b) continue;
-    const int i = ti * HT + a, j = tj * HT + b;
-    if (i >= d || j >= d) continue;
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += P[(int64_t)s * dp * dp + (int64_t)i * dp + j];
-    H[(int64_t)i * d + j] += 2.f * v;
+  __shared__ float T[HT][HT + 1];
+  const int t = threadIdx.x;
+  const int64_t pstride = dp * dp;
+#pragma unroll 4
+  for (int it = 0; it < HT * HT / (256 * 4); ++it) {
+    const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+    const int i = ti * HT + a, j = tj * HT + b4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float* src = P + (int64_t)i * dp + j;   // i, j < dp: always inside the partials
+    for (int sp = 0; sp < splits; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + sp * pstride);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+    }
+    if (vec_h && ti < tj && i < d && j + 3 < d) {
+      f32x4* hp = reinterpret_cast<f32x4*>(H + (int64_t)i * d + j);
+      f32x4 h = *hp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = fmaf(2.f, acc[q], h[q]);
+      *hp = h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[a][b4 + q] = h[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int jq = j + q;
+        float v = 0.f;
+        if (i < d && jq < d && jq >= i) {
+          v = fmaf(2.f, acc[q], H[(int64_t)i * d + jq]);
+          H[(int64_t)i * d + jq] = v;
+        }
+        T[a][b4 + q] = v;
+      }
+    }
+  }
+  __syncthreads();
+  // lower triangle: row tj*HT + bb, columns ti*HT + aa (contiguous in aa)
+  for (int e = t; e < HT * HT; e += 256) {
+    const int bb = e / HT, aa = e % HT;
+    const int r = tj * HT + bb, c = ti * HT + aa;
+    if (r < d && c < d && c < r) H[(int64_t)r * d + c] = T[aa][bb];
   }
 }
 
@@ -471,13 +490,10 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  {
-    const int nt128 = (int)(dp / HT);
-    syrk_reduce_kernel<<<nt128 * (nt128 + 1) / 2, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  const int nb = (int)ceil_div(d, 64);
-  mirror_kernel<<<nb * (nb + 1) / 2, 256, 0, s>>>(H, (int)d, nb);
+  const int nt128 = (int)(dp / HT);
+  const int vec_h = ((uintptr_t)H % 16 == 0) && (d % 4 == 0);
+  reduce_mirror_kernel<<<nt128 * (nt128 + 1) / 2, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128,
+                                                               vec_h);
   return hipGetLastError();
 }
 

@@ -4,13 +4,20 @@
 //
 // Working state: Wk [m x d] fp32, columns already in quantization order and
 // dead columns zeroed.  For each block of 128 columns:
-//   sweep   one thread per row keeps the block's 128 weights in registers and
-//           runs the sequential column loop: group (s, z) at group starts,
+//   sweep   16 lanes per row keep the block's 128 weights in registers and
+//           run the sequential column loop: group (s, z) at group starts,
 //           q = clamp(rint(w/s + z)), ŵ = s(q − z), err = (w − ŵ)/U_cc and
-//           w_k −= err·U_ck for the block's later columns.  U's row is the
-//           same for every row, so its values are wave-uniform loads.
-//   update  Wk[:, e:] −= Err[:, block] · U[block, e:] on the fp32 MFMA GEMM
-//           (the "lazy batch" product; U for both updates, see below).
+//           w_k −= err·U_ck for the block's later columns (sweep.hip).
+//   update  the "lazy batch" product W[:, later] −= Err[:, block]·U[block, later]
+//           on the fp32 MFMA GEMM, in two levels: blocks are grouped into
+//           super-blocks of 4; after a block only the rest of its
+//           super-block is updated, and after the super-block everything to
+//           its right receives the whole super-block's update at once
+//           (K = 512).  The sum of the four rank-128 products is the same
+//           update; the columns right of the super-block are not read until
+//           it is done.  Group parameters taken at a group start need the
+//           group's columns current, so super-blocks are used only when every
+//           group start is a super-block start or the group lies inside one.
 // Finally codes are packed and Ŵ is written in the original column order.
 //
 // Reading where the pages disagree: U (the upper Cholesky factor of H_d⁻¹)
@@ -31,7 +38,7 @@ QWs carve(void* ws, int64_t m, int64_t d) {
   char* p = static_cast<char*>(ws);
   QWs w;
   w.Wk = reinterpret_cast<float*>(p); p += align_up((size_t)m * dp * 4);
-  w.Err = reinterpret_cast<float*>(p); p += align_up((size_t)m * kBlock * 4);
+  w.Err = reinterpret_cast<float*>(p); p += align_up((size_t)m * kSuper * kBlock * 4);
   w.codes = reinterpret_cast<uint8_t*>(p); p += align_up((size_t)m * dp);
   w.inv = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
   w.Upad = reinterpret_cast<float*>(p);
@@ -141,35 +148,54 @@ hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_p
                       hipStream_t s) {
   const int64_t dp = ceil_div(d, kBlock) * kBlock;
   const int maxq = (1 << p.bits) - 1;
+  // super-blocks only where no group straddles a super-block boundary
+  // with its start inside it (groups of G > 0 columns stay inside a block)
+  const int64_t sbw = kSuper * kBlock;
+  const bool two_level = G > 0 || g >= d || g % sbw == 0 || sbw % g == 0;
+  const int64_t sb = two_level ? sbw : kBlock;
+  const int64_t lde = kSuper * kBlock;
   hipError_t e;
-  for (int64_t b0 = 0; b0 < d; b0 += kBlock) {
-    const int bw = (int)std::min<int64_t>(kBlock, d - b0);
-    if (G == 0 && b0 % g == 0) {
-      group_params_kernel<<<(unsigned)ceil_div(m, 4), 256, 0, s>>>(
-          w.Wk, m, dp, b0, std::min<int64_t>(b0 + g, d), maxq, p.sym, scales, zeros, ng,
-          (int)(b0 / g));
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int64_t sb0 = 0; sb0 < d; sb0 += sb) {
+    const int64_t se = std::min<int64_t>(sb0 + sb, d);
+    for (int64_t b0 = sb0; b0 < se; b0 += kBlock) {
+      const int bw = (int)std::min<int64_t>(kBlock, d - b0);
+      if (G == 0 && b0 % g == 0) {
+        group_params_kernel<<<(unsigned)ceil_div(m, 4), 256, 0, s>>>(
+            w.Wk, m, dp, b0, std::min<int64_t>(b0 + g, d), maxq, p.sym, scales, zeros, ng,
+            (int)(b0 / g));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      SweepArgs a{};
+      a.Wk = w.Wk; a.ldw = dp; a.m = m; a.b0 = b0; a.bw = bw;
+      if (bw == kBlock) {
+        a.Ublk = U + b0 * d + b0; a.ldu = d;
+      } else {
+        pad_u_kernel<<<1, 256, 0, s>>>(U, d, b0, bw, w.Upad);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        a.Ublk = w.Upad; a.ldu = kBlock;
+      }
+      a.maxq = maxq; a.sym = p.sym; a.scales = scales; a.zeros = zeros; a.ng = ng; a.g = g;
+      a.Err = w.Err + (b0 - sb0); a.lde = lde;
+      a.codes = w.codes; a.row_loss = row_loss;
+      if ((e = launch_sweep<G>(a, s)) != hipSuccess) return e;
+      const int64_t b1 = b0 + bw;
+      if (b1 < se) {  // the rest of the super-block: W[:, b1:se] −= Err_b · U[b, b1:se]
+        GemmArgs u{};
+        u.M = (int)m; u.N = (int)(se - b1); u.K = bw; u.k_last = bw; u.batch = 1;
+        u.alpha = -1.f; u.beta = 1.f;
+        u.A = w.Err + (b0 - sb0); u.lda = lde; u.trans_a = false;
+        u.B = U + b0 * d + b1; u.ldb = d; u.trans_b = false;
+        u.C = w.Wk + b1; u.ldc = dp; u.tri = 0;
+        if ((e = gemm_f32(u, s)) != hipSuccess) return e;
+      }
     }
-    SweepArgs a{};
-    a.Wk = w.Wk; a.ldw = dp; a.m = m; a.b0 = b0; a.bw = bw;
-    if (bw == kBlock) {
-      a.Ublk = U + b0 * d + b0; a.ldu = d;
-    } else {
-      pad_u_kernel<<<1, 256, 0, s>>>(U, d, b0, bw, w.Upad);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      a.Ublk = w.Upad; a.ldu = kBlock;
-    }
-    a.maxq = maxq; a.sym = p.sym; a.scales = scales; a.zeros = zeros; a.ng = ng; a.g = g;
-    a.Err = w.Err; a.codes = w.codes; a.row_loss = row_loss;
-    if ((e = launch_sweep<G>(a, s)) != hipSuccess) return e;
-    const int64_t b1 = b0 + bw;
-    if (b1 < d) {
+    if (se < d) {  // everything right of it: W[:, se:] −= Err_sb · U[sb, se:]
       GemmArgs u{};
-      u.M = (int)m; u.N = (int)(d - b1); u.K = bw; u.k_last = bw; u.batch = 1;
+      u.M = (int)m; u.N = (int)(d - se); u.K = (int)(se - sb0); u.k_last = u.K; u.batch = 1;
       u.alpha = -1.f; u.beta = 1.f;
-      u.A = w.Err; u.lda = kBlock; u.trans_a = false;
-      u.B = U + b0 * d + b1; u.ldb = d; u.trans_b = false;
-      u.C = w.Wk + b1; u.ldc = dp; u.tri = 0;
+      u.A = w.Err; u.lda = lde; u.trans_a = false;
+      u.B = U + sb0 * d + se; u.ldb = d; u.trans_b = false;
+      u.C = w.Wk + se; u.ldc = dp; u.tri = 0;
       if ((e = gemm_f32(u, s)) != hipSuccess) return e;
     }
   }
@@ -180,7 +206,8 @@ hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_p
 
 size_t quantize_ws_bytes(int64_t m, int64_t d) {
   const int64_t dp = ceil_div(d, kBlock) * kBlock;
-  return align_up((size_t)m * dp * 4) + align_up((size_t)m * kBlock * 4) + align_up((size_t)m * dp) +
+  return align_up((size_t)m * dp * 4) + align_up((size_t)m * kSuper * kBlock * 4) +
+         align_up((size_t)m * dp) +
          align_up((size_t)d * 4) + align_up((size_t)kBlock * kBlock * 4);
 }
 

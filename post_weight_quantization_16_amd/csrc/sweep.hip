@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   // write back: lane c stores its row's columns 4c..4c+3 and 64+4c..64+4c+3
   if (live) {
     float* dw = a.Wk + r * a.ldw + a.b0 + 4 * c;
-    float* de = a.Err + r * kBlock + 4 * c;
+    float* de = a.Err + r * a.lde + 4 * c;
     uint8_t* dq = a.codes + r * a.ldw + a.b0 + 4 * c;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
