@@ -100,23 +100,6 @@ __global__ __launch_bounds__(256) void build_g_kernel(const float* __restrict__ 
   }
 }
 
-// H_out[x][y] = H_d[x][y] rebuilt from G's untouched strict upper triangle.
-__global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, int64_t d,
-                                                       const float* __restrict__ G,
-                                                       const float* __restrict__ diag,
-                                                       const int* __restrict__ perm,
-                                                       const float* __restrict__ lam) {
-  for (int64_t x = blockIdx.y; x < d; x += gridDim.y) {
-    for (int64_t y = blockIdx.x * 256 + threadIdx.x; y < d; y += (int64_t)gridDim.x * 256) {
-      float v;
-      if (x == y) v = diag[perm[x]] + lam[0];
-      else if (x > y) v = G[(d - 1 - x) * d + (d - 1 - y)];
-      else v = G[(d - 1 - y) * d + (d - 1 - x)];
-      H[x * d + y] = v;
-    }
-  }
-}
-
 struct PanelArgs {
   float* G; int64_t d; int k0, kb;
   float* Linv; int* status;
@@ -350,6 +333,40 @@ __device__ __forceinline__ void lower_tile(int L, int& by, int& bx) {
   bx = L - y * (y + 1) / 2;
 }
 
+// H_out[x][y] = H_d[x][y] rebuilt from G's untouched strict upper triangle
+// (G = J·H_d·J, so H_d[x][y] = G[d-1-x][d-1-y]), one lower 64x64 tile of
+// H_out per workgroup: the tile is read along G's rows, written directly,
+// and written transposed through LDS as its mirror above the diagonal.
+__global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, int64_t d,
+                                                       const float* __restrict__ G,
+                                                       const float* __restrict__ diag,
+                                                       const int* __restrict__ perm,
+                                                       const float* __restrict__ lam) {
+  int by, bx;
+  lower_tile(blockIdx.x, by, bx);
+  __shared__ float T[64][65];
+  const int t = threadIdx.x;
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    const int64_t x = 64 * by + i, y = 64 * bx + j;
+    float v = 0.f;
+    if (x < d && y < d) {
+      if (x == y) v = diag[perm[x]] + lam[0];
+      else if (x > y) v = G[(d - 1 - x) * d + (d - 1 - y)];
+      else v = G[(d - 1 - y) * d + (d - 1 - x)];   // inside a diagonal tile only
+      H[x * d + y] = v;
+    }
+    T[i][j] = v;
+  }
+  if (by == bx) return;
+  __syncthreads();
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int jj = e >> 6, ii = e & 63;   // output row 64bx+jj, column 64by+ii
+    const int64_t y = 64 * bx + jj, x = 64 * by + ii;
+    if (x < d && y < d) H[y * d + x] = T[ii][jj];
+  }
+}
+
 // One step of the blocked Cholesky: workgroups [0, nP) run panel k (its
 // columns first receive the previous panel's update), the rest run the
 // previous panel's trailing update of the columns beyond panel k,
@@ -487,7 +504,11 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
 
   write_u_kernel<<<dim3(gx, gy), 256, 0, s>>>(w.Linv, d, U);
   GQ_CHECK();
-  write_hd_kernel<<<dim3(gx, gy), 256, 0, s>>>(H, d, w.G, w.diag, w.perm, w.lam);
+  {
+    const int64_t nb64 = ceil_div(d, 64);
+    write_hd_kernel<<<(unsigned)(nb64 * (nb64 + 1) / 2), 256, 0, s>>>(H, d, w.G, w.diag, w.perm,
+                                                                      w.lam);
+  }
   GQ_CHECK();
   if (perm_out) {
     e = hipMemcpyAsync(perm_out, w.perm, (size_t)d * 4, hipMemcpyDeviceToDevice, s);

@@ -53,25 +53,32 @@ __device__ __forceinline__ float load_w(const void* W, int dt, int64_t i) {
 }
 
 // Wk[r][a] = W[r][π(a)] (0 for dead channels and padding a >= d);
-// inv[π(a)] = a; row_loss = 0.
+// inv[π(a)] = a; row_loss = 0.  Each thread writes 4 consecutive columns
+// (one float4: dp is a multiple of 128).
 __global__ __launch_bounds__(256) void init_kernel(const void* __restrict__ W, int dt, int64_t ld_w,
                                                    int64_t m, int64_t d, int64_t dp,
                                                    const int* __restrict__ perm,
                                                    const uint8_t* __restrict__ dead,
                                                    float* __restrict__ Wk, int* __restrict__ inv,
                                                    float* __restrict__ row_loss) {
+  const int64_t a0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
-    for (int64_t a = blockIdx.x * 256 + threadIdx.x; a < dp; a += (int64_t)gridDim.x * 256) {
-      float v = 0.f;
+    if (row_loss && blockIdx.x == 0 && threadIdx.x == 0) row_loss[r] = 0.f;
+    if (a0 >= dp) continue;
+    f32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t a = a0 + q;
+      float x = 0.f;
       if (a < d) {
         const int c = perm ? perm[a] : (int)a;
-        v = load_w(W, dt, r * ld_w + c);
-        if (dead && dead[c]) v = 0.f;
+        x = load_w(W, dt, r * ld_w + c);
+        if (dead && dead[c]) x = 0.f;
         if (r == 0) inv[c] = (int)a;
       }
-      Wk[r * dp + a] = v;
+      v[q] = x;
     }
-    if (row_loss && blockIdx.x == 0 && threadIdx.x == 0) row_loss[r] = 0.f;
+    *reinterpret_cast<f32x4*>(Wk + r * dp + a0) = v;
   }
 }
 
@@ -116,26 +123,51 @@ __global__ __launch_bounds__(256) void pad_u_kernel(const float* __restrict__ U,
   }
 }
 
-// Pack codes and write Ŵ / g_idx in the original column order.
+// Write Ŵ / g_idx and pack the codes, in the original column order.  The
+// first loop gives each thread 4 consecutive output columns of Ŵ (gathered
+// through inv, which is contiguous without act-order); the second gives
+// each thread one packed word.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ Wk,
                                                        const uint8_t* __restrict__ codes,
                                                        const int* __restrict__ inv, int64_t m,
                                                        int64_t d, int64_t dp, int bits, int64_t g,
                                                        uint32_t* __restrict__ qweight,
                                                        float* __restrict__ W_hat,
-                                                       int32_t* __restrict__ g_idx) {
+                                                       int32_t* __restrict__ g_idx, int vec_w) {
   const int cpw = bits <= 4 ? 8 : 4, cwid = 32 / cpw;
   const int64_t nw = (d + cpw - 1) / cpw;
+  const int64_t lin = (int64_t)blockIdx.x * 256 + threadIdx.x;
   for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
-    for (int64_t k = blockIdx.x * 256 + threadIdx.x; k < nw; k += (int64_t)gridDim.x * 256) {
+    const int64_t c0 = lin * 4;
+    if ((W_hat || (g_idx && r == 0)) && c0 < d) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c = c0 + q;
+        v[q] = 0.f;
+        if (c < d) {
+          const int a = inv[c];
+          v[q] = Wk[r * dp + a];
+          if (g_idx && r == 0) g_idx[c] = (int32_t)(a / g);
+        }
+      }
+      if (W_hat) {
+        if (vec_w && c0 + 3 < d) {
+          const f32x4 o = {v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(W_hat + r * d + c0) = o;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (c0 + q < d) W_hat[r * d + c0 + q] = v[q];
+        }
+      }
+    }
+    for (int64_t k = lin; k < nw; k += (int64_t)gridDim.x * 256) {
       uint32_t word = 0;
       for (int i = 0; i < cpw; ++i) {
         const int64_t c = k * cpw + i;
         if (c >= d) break;
-        const int a = inv[c];
-        word |= (uint32_t)codes[r * dp + a] << (cwid * i);
-        if (W_hat) W_hat[r * d + c] = Wk[r * dp + a];
-        if (g_idx && r == 0) g_idx[c] = (int32_t)(a / g);
+        word |= (uint32_t)codes[r * dp + inv[c]] << (cwid * i);
       }
       qweight[r * nw + k] = word;
     }
@@ -219,11 +251,11 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
   QWs w = carve(ws, m, d);
   const int64_t g = (p.group_size <= 0 || p.group_size >= d) ? d : p.group_size;
   const int ng = (int)ceil_div(d, g);
-  const unsigned gx = (unsigned)std::min<int64_t>(ceil_div(d, 256), 16);
   const unsigned gy = (unsigned)std::min<int64_t>(m, 65535);
   const int64_t dp = ceil_div(d, kBlock) * kBlock;
-  init_kernel<<<dim3(gx, gy), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp, perm, dead, w.Wk, w.inv,
-                                           row_loss);
+  init_kernel<<<dim3((unsigned)ceil_div(dp, 1024), gy), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp,
+                                                                    perm, dead, w.Wk, w.inv,
+                                                                    row_loss);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g) {
@@ -233,10 +265,9 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
     default: e = run_blocks<0>(w, m, d, U, p, g, ng, scales, zeros, row_loss, s); break;
   }
   if (e != hipSuccess) return e;
-  const int cpw = p.bits <= 4 ? 8 : 4;
-  const unsigned fx = (unsigned)std::min<int64_t>(ceil_div(ceil_div(d, cpw), 256), 16);
-  finalize_kernel<<<dim3(fx, gy), 256, 0, s>>>(w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight,
-                                               W_hat, g_idx);
+  const int vec_w = W_hat && ((uintptr_t)W_hat % 16 == 0) && (d % 4 == 0);
+  finalize_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(
+      w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight, W_hat, g_idx, vec_w);
   return hipGetLastError();
 }
 
