@@ -1,16 +1,34 @@
-// fp32 MFMA GEMM for gfx950: the lazy block update of the GPTQ sweep and the
-// trailing updates of the triangular inverse (the tile itself is in
-// gemm_tile.hpp).
+// fp32 MFMA GEMM for gfx950: the lazy block updates of the GPTQ sweep and the
+// products of the triangular inverse (the tile itself is in gemm_tile.hpp).
 #include "gemm_tile.hpp"
 
 namespace gq {
 namespace gemm_detail {
 namespace {
 
-template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g) {
-  __shared__ __attribute__((aligned(16))) float Sm[GEMM_SMEM_FLOATS];
-  gemm_tile<TA, TB>(g, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, Sm);
+// blockIdx.x enumerates the nx x ny tiles.  Workgroups start in index
+// order, so the order is longest-first where tiles differ in K: column-major
+// from the left when column n starts its K loop at n (k_from_n), row-major
+// from the bottom when row m stops at m (k_to_m), row-major otherwise.
+template <int T, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g, int nx, int ny) {
+  __shared__ __attribute__((aligned(16))) float Sm[4 * Tile<T>::OPF];
+  const int L = blockIdx.x;
+  int bx, by;
+  if (g.k_from_n) { bx = L / ny; by = L % ny; }
+  else if (g.k_to_m) { by = ny - 1 - L / nx; bx = L % nx; }
+  else { by = L / nx; bx = L % nx; }
+  gemm_tile<T, TA, TB>(g, bx, by, blockIdx.z, gridDim.z, Sm);
+}
+
+template <int T>
+void launch(const KArgs& k, const GemmArgs& a, hipStream_t s) {
+  const int nx = (int)ceil_div(a.N, T), ny = (int)ceil_div(a.M, T);
+  dim3 grid((unsigned)(nx * ny), 1, (unsigned)a.batch);
+  if (!a.trans_a && !a.trans_b) gemm_f32_kernel<T, false, false><<<grid, 256, 0, s>>>(k, nx, ny);
+  else if (!a.trans_a && a.trans_b) gemm_f32_kernel<T, false, true><<<grid, 256, 0, s>>>(k, nx, ny);
+  else if (a.trans_a && !a.trans_b) gemm_f32_kernel<T, true, false><<<grid, 256, 0, s>>>(k, nx, ny);
+  else gemm_f32_kernel<T, true, true><<<grid, 256, 0, s>>>(k, nx, ny);
 }
 
 }  // namespace
@@ -39,11 +57,13 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   using namespace gemm_detail;
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
   const KArgs k = make_kargs(a);
-  dim3 grid((unsigned)ceil_div(a.N, TN), (unsigned)ceil_div(a.M, TM), (unsigned)a.batch);
-  if (!a.trans_a && !a.trans_b) gemm_f32_kernel<false, false><<<grid, 256, 0, s>>>(k);
-  else if (!a.trans_a && a.trans_b) gemm_f32_kernel<false, true><<<grid, 256, 0, s>>>(k);
-  else if (a.trans_a && !a.trans_b) gemm_f32_kernel<true, false><<<grid, 256, 0, s>>>(k);
-  else gemm_f32_kernel<true, true><<<grid, 256, 0, s>>>(k);
+  // 128-tiles unless they would leave most CUs without a second workgroup
+  // or the K loop is long (the triangular products' tiles then differ a lot
+  // in length, and small tiles spread the long ones over more CUs)
+  const int64_t tiles128 = ceil_div(a.M, 128) * ceil_div(a.N, 128) * a.batch;
+  const bool small = tiles128 < 512 || ((a.k_from_n || a.k_to_m) && a.K >= 1024);
+  if (small) launch<64>(k, a, s);
+  else launch<128>(k, a, s);
   return hipGetLastError();
 }
 

@@ -1,18 +1,21 @@
 // fp32 MFMA GEMM tile for gfx950, shared by the stand-alone GEMM kernel and
 // the fused Cholesky step of the preparation.
 //
-// Tile 128x128 per workgroup of 256 threads (4 waves in a 2x2 grid, each wave
-// 64x64 = 2x2 tiles of v_mfma_f32_32x32x2f32, whose operands are one float per
-// lane: A(m = lane%32, k = lane/32) and B(k = lane/32, n = lane%32)).
+// Square T x T output tile (T = 128 or 64) per workgroup of 256 threads:
+// 4 waves in a 2x2 grid, each wave (T/2)x(T/2) = (T/64)^2 tiles of
+// v_mfma_f32_32x32x2f32, whose operands are one float per lane:
+// A(m = lane%32, k = lane/32) and B(k = lane/32, n = lane%32).
 // K advances in chunks of 32 through a double-buffered LDS stage: the next
 // chunk is fetched into registers while the current one is multiplied, then
 // stored into the other buffer; one barrier per chunk.  Each operand is kept
 // in LDS in its memory orientation:
-//   contiguous along m (or n): [k][128 + 32] -- a half-wave reads 32
+//   contiguous along m (or n): [k][T + 32] -- a half-wave reads 32
 //     consecutive words, the other half-wave's row is 32 banks away;
 //   contiguous along k: [m][32 + 2] -- the odd-pair stride 34 sends the 32
 //     rows a half-wave reads to 32 distinct banks.
-// 80 KB of LDS, so two workgroups share a CU.
+// T = 128 takes 80 KB of LDS (two workgroups per CU); T = 64 serves
+// products whose 128-tiles would not fill the chip or whose K is long and
+// uneven across tiles.
 #pragma once
 
 #include "common.hpp"
@@ -20,11 +23,20 @@
 namespace gq {
 namespace gemm_detail {
 
-constexpr int TM = 128, TN = 128, TK = 32;
-constexpr int SA = TM + 32;   // stride of a [k][128] operand (floats)
-constexpr int SK = TK + 2;    // stride of a [128][k] operand (floats)
-constexpr int OPF = TK * SA > TM * SK ? TK * SA : TM * SK;   // floats per operand buffer
-static_assert(TM * (TN + 8) <= 4 * OPF, "the epilogue tile must fit in the operand buffers");
+constexpr int TK = 32;
+template <int T> struct Tile {
+  static constexpr int SA = T + 32;   // stride of a [k][T] operand (floats)
+  static constexpr int SK = TK + 2;   // stride of a [T][k] operand (floats)
+  static constexpr int OPF = TK * SA > T * SK ? TK * SA : T * SK;   // floats per operand buffer
+  static constexpr int NV = TK * T / (256 * 4);                       // float4 per thread per chunk
+  static constexpr int ES = T + 8;    // epilogue stride: 4·ES ≡ 32 (mod 64), half-waves' rows disjoint
+  static constexpr int FI = T / 64;   // MFMA tiles per wave along each edge
+  static_assert(T * ES <= 4 * OPF, "the epilogue tile must fit in the operand buffers");
+};
+constexpr int GEMM_SMEM_FLOATS = 4 * Tile<128>::OPF;   // enough for either tile size
+static_assert(4 * Tile<64>::OPF <= GEMM_SMEM_FLOATS, "");
+// the 128 tile is used by callers that name these
+constexpr int TM = 128, TN = 128;
 
 struct KArgs {
   int M, N, K, k_last;
@@ -37,16 +49,17 @@ struct KArgs {
   int vec_a, vec_b, vec_c;
 };
 
-// One 32 x 128 operand chunk in registers: 4 float4 per thread.
-// ALONG: the 128-wide dimension is contiguous in memory; otherwise k is.
-template <bool ALONG>
+// One 32 x T operand chunk in registers: NV float4 per thread.
+// ALONG: the T-wide dimension is contiguous in memory; otherwise k is.
+template <int T, bool ALONG>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t ld, int rows_valid,
-                                           int k0, int kvalid, int t, bool vec, f32x4 (&r)[4]) {
+                                           int k0, int kvalid, int t, bool vec,
+                                           f32x4 (&r)[Tile<T>::NV]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < Tile<T>::NV; ++i) {
     const int idx = t + 256 * i;
-    int a, b;  // a: index along the 128-wide dim, b: k
-    if (ALONG) { b = idx >> 5; a = (idx & 31) * 4; }
+    int a, b;  // a: index along the T-wide dim, b: k
+    if (ALONG) { b = idx / (T / 4); a = (idx % (T / 4)) * 4; }
     else       { a = idx >> 3; b = (idx & 7) * 4; }
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (ALONG) {
@@ -75,41 +88,44 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
   }
 }
 
-template <bool ALONG>
-__device__ __forceinline__ void store_chunk(float* __restrict__ s, int t, const f32x4 (&r)[4]) {
+template <int T, bool ALONG>
+__device__ __forceinline__ void store_chunk(float* __restrict__ s, int t,
+                                            const f32x4 (&r)[Tile<T>::NV]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < Tile<T>::NV; ++i) {
     const int idx = t + 256 * i;
     if (ALONG) {
-      const int b = idx >> 5, a = (idx & 31) * 4;
-      *reinterpret_cast<f32x4*>(s + b * SA + a) = r[i];
+      const int b = idx / (T / 4), a = (idx % (T / 4)) * 4;
+      *reinterpret_cast<f32x4*>(s + b * Tile<T>::SA + a) = r[i];
     } else {
       const int a = idx >> 3, b = (idx & 7) * 4;
       typedef __attribute__((ext_vector_type(2))) float f32x2;
       f32x2 lo = {r[i][0], r[i][1]}, hi = {r[i][2], r[i][3]};
-      *reinterpret_cast<f32x2*>(s + a * SK + b) = lo;
-      *reinterpret_cast<f32x2*>(s + a * SK + b + 2) = hi;
+      *reinterpret_cast<f32x2*>(s + a * Tile<T>::SK + b) = lo;
+      *reinterpret_cast<f32x2*>(s + a * Tile<T>::SK + b + 2) = hi;
     }
   }
 }
 
-template <bool ALONG>
+template <int T, bool ALONG>
 __device__ __forceinline__ float opread(const float* s, int a, int k) {
-  return ALONG ? s[k * SA + a] : s[a * SK + k];
+  return ALONG ? s[k * Tile<T>::SA + a] : s[a * Tile<T>::SK + k];
 }
 
-// One 128x128 output tile (bx, by) of batch z; nz = number of batches.
+// One T x T output tile (bx, by) of batch z; nz = number of batches.
 // Sm: GEMM_SMEM_FLOATS floats of LDS.  All 256 threads of the workgroup
 // must call it (it synchronizes).
-template <bool TA, bool TB>
+template <int T, bool TA, bool TB>
 __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z, int nz,
                                           float* __restrict__ Sm) {
-  const int m0 = by * TM, n0 = bx * TN;
-  if (g.tri == 1 && n0 > m0 + TM - 1) return;
-  if (g.tri == 2 && n0 + TN - 1 < m0) return;
+  using TL = Tile<T>;
+  constexpr int OPF = TL::OPF, FI = TL::FI, WT = T / 2;
+  const int m0 = by * T, n0 = bx * T;
+  if (g.tri == 1 && n0 > m0 + T - 1) return;
+  if (g.tri == 2 && n0 + T - 1 < m0) return;
   const int Kz = (z == nz - 1) ? g.k_last : g.K;
   const int kbeg = g.k_from_n ? (n0 / TK) * TK : 0;
-  const int K = g.k_to_m ? min(Kz, m0 + TM) : Kz;
+  const int K = g.k_to_m ? min(Kz, m0 + T) : Kz;
   const float* A = g.A + (int64_t)z * g.strideA;
   const float* B = g.B + (int64_t)z * g.strideB;
   float* C = g.C + (int64_t)z * g.strideC;
@@ -123,20 +139,20 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
   const float* Bb = TB ? B + (int64_t)n0 * g.ldb : B + n0;
   const int mvalid = g.M - m0, nvalid = g.N - n0;
 
-  f32x16 acc[2][2];
+  f32x16 acc[FI][FI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  f32x4 ra[4], rb[4];
+  f32x4 ra[TL::NV], rb[TL::NV];
   if (kbeg < K) {
-    load_chunk<AL_A>(Ab, g.lda, mvalid, kbeg, K, t, g.vec_a, ra);
-    load_chunk<AL_B>(Bb, g.ldb, nvalid, kbeg, K, t, g.vec_b, rb);
-    store_chunk<AL_A>((Sm + 0 * OPF), t, ra);
-    store_chunk<AL_B>((Sm + 1 * OPF), t, rb);
+    load_chunk<T, AL_A>(Ab, g.lda, mvalid, kbeg, K, t, g.vec_a, ra);
+    load_chunk<T, AL_B>(Bb, g.ldb, nvalid, kbeg, K, t, g.vec_b, rb);
+    store_chunk<T, AL_A>(Sm + 0 * OPF, t, ra);
+    store_chunk<T, AL_B>(Sm + 1 * OPF, t, rb);
   }
   __syncthreads();
 
@@ -144,65 +160,68 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
   for (int k0 = kbeg; k0 < K; k0 += TK) {
     const bool more = k0 + TK < K;
     if (more) {
-      load_chunk<AL_A>(Ab, g.lda, mvalid, k0 + TK, K, t, g.vec_a, ra);
-      load_chunk<AL_B>(Bb, g.ldb, nvalid, k0 + TK, K, t, g.vec_b, rb);
+      load_chunk<T, AL_A>(Ab, g.lda, mvalid, k0 + TK, K, t, g.vec_a, ra);
+      load_chunk<T, AL_B>(Bb, g.ldb, nvalid, k0 + TK, K, t, g.vec_b, rb);
     }
-    const float* As = (Sm + (2 * buf + 0) * OPF);
-    const float* Bs = (Sm + (2 * buf + 1) * OPF);
+    const float* As = Sm + (2 * buf + 0) * OPF;
+    const float* Bs = Sm + (2 * buf + 1) * OPF;
 #pragma unroll
     for (int kk = 0; kk < TK / 2; ++kk) {
       const int ka = kk * 2 + (lane >> 5);
-      const float a0 = opread<AL_A>(As, wm * 64 + (lane & 31), ka);
-      const float a1 = opread<AL_A>(As, wm * 64 + 32 + (lane & 31), ka);
-      const float b0 = opread<AL_B>(Bs, wn * 64 + (lane & 31), ka);
-      const float b1 = opread<AL_B>(Bs, wn * 64 + 32 + (lane & 31), ka);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      float av[FI], bv[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        av[i] = opread<T, AL_A>(As, wm * WT + i * 32 + (lane & 31), ka);
+        bv[i] = opread<T, AL_B>(Bs, wn * WT + i * 32 + (lane & 31), ka);
+      }
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
     if (more) {
-      store_chunk<AL_A>((Sm + (2 * (buf ^ 1) + 0) * OPF), t, ra);
-      store_chunk<AL_B>((Sm + (2 * (buf ^ 1) + 1) * OPF), t, rb);
+      store_chunk<T, AL_A>(Sm + (2 * (buf ^ 1) + 0) * OPF, t, ra);
+      store_chunk<T, AL_B>(Sm + (2 * (buf ^ 1) + 1) * OPF, t, rb);
     }
     __syncthreads();
     buf ^= 1;
   }
 
   // Epilogue through LDS (the operand buffers are free after the loop's last
-  // barrier): the tile goes to LDS as alpha·acc, then every thread owns 16
-  // float4 of it.  All of a thread's C reads are issued before any of its
-  // writes -- C is read and written through one pointer, so reads placed
-  // after writes would each wait for a full memory round trip.
+  // barrier): the tile goes to LDS as alpha·acc, then every thread owns
+  // T·T/1024 float4 of it.  All of a thread's C reads are issued before any
+  // of its writes -- C is read and written through one pointer, so reads
+  // placed after writes would each wait for a full memory round trip.
   // MFMA layout: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32.
-  constexpr int ES = TN + 8;   // 4·ES ≡ 32 (mod 64): the half-waves' rows hit disjoint banks
-  float* E = &(Sm + 0 * OPF)[0];
+  constexpr int ES = TL::ES, NE = T * T / 1024;
+  float* E = Sm;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = wn * 64 + j * 32 + (lane & 31);
+        const int row = wm * WT + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = wn * WT + j * 32 + (lane & 31);
         E[row * ES + col] = g.alpha * acc[i][j][r];
       }
   __syncthreads();
   const bool has_beta = g.beta != 0.f;
-  const bool tri_all = g.tri == 0 || (g.tri == 1 && n0 + TN - 1 <= m0) ||
-                       (g.tri == 2 && n0 >= m0 + TM - 1);
-  if (tri_all && mvalid >= TM && nvalid >= TN && g.vec_c) {
-    f32x4 cv[16];
+  const bool tri_all = g.tri == 0 || (g.tri == 1 && n0 + T - 1 <= m0) ||
+                       (g.tri == 2 && n0 >= m0 + T - 1);
+  if (tri_all && mvalid >= T && nvalid >= T && g.vec_c) {
+    f32x4 cv[NE];
     if (has_beta) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int idx = t + 256 * u, row = idx >> 5, c4 = (idx & 31) * 4;
+      for (int u = 0; u < NE; ++u) {
+        const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
         cv[u] = *reinterpret_cast<const f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4);
       }
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = t + 256 * u, row = idx >> 5, c4 = (idx & 31) * 4;
+    for (int u = 0; u < NE; ++u) {
+      const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
       f32x4 v = *reinterpret_cast<const f32x4*>(E + row * ES + c4);
       if (has_beta) {
 #pragma unroll
@@ -213,17 +232,17 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
   } else {
     // edge or diagonal tile: element-wise, reads (at clamped, valid
     // addresses) batched ahead of the masked writes 16 at a time
-    for (int e0 = 0; e0 < TM * TN; e0 += 256 * 16) {
+    for (int e0 = 0; e0 < T * T; e0 += 256 * 16) {
       float cs[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int e = e0 + t + 256 * u, row = e / TN, col = e % TN;
+        const int e = e0 + t + 256 * u, row = e / T, col = e % T;
         const int rr = min(row, mvalid - 1), cc = min(col, nvalid - 1);
         cs[u] = has_beta ? C[(int64_t)(m0 + rr) * g.ldc + n0 + cc] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int e = e0 + t + 256 * u, row = e / TN, col = e % TN;
+        const int e = e0 + t + 256 * u, row = e / T, col = e % T;
         const int gr = m0 + row, gc = n0 + col;
         bool ok = row < mvalid && col < nvalid;
         if (g.tri == 1) ok = ok && gc <= gr;
@@ -233,9 +252,6 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
     }
   }
 }
-
-
-constexpr int GEMM_SMEM_FLOATS = 4 * OPF;
 
 // Kernel arguments for a host-side GemmArgs (vector-load eligibility included).
 KArgs make_kargs(const GemmArgs& a);

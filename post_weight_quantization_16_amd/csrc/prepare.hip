@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP,
   } else {
     int by, bx;
     lower_tile(L - nP, by, bx);
-    gemm_detail::gemm_tile<false, true>(tr, bx, by, 0, 1, smem);
+    gemm_detail::gemm_tile<128, false, true>(tr, bx, by, 0, 1, smem);
   }
 }
 
