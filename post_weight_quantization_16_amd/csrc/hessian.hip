@@ -166,29 +166,36 @@ __global__ __launch_bounds__(256) void syrk16_generic_kernel(const uint16_t* __r
 
 // ---------------------------------------------------------------- fast path
 // 256x256 output tiles, 4 waves each owning a 128x128 block (4x4 tiles of
-// v_mfma_f32_32x32x16).  X stays in its natural [token][column] layout in LDS:
-// stages of 32 tokens, rows of 512 bytes whose 16-byte chunks are
-// XOR-swizzled by (row & 3) << 2, double-buffered.  Each stage is fetched two
-// stages ahead into one of two register sets (8 x 16 bytes per thread), and
-// written to LDS one stage ahead, so about two stage-times of MFMA work cover
-// each load's latency.  Loads read clamped in-bounds addresses and zero
-// out-of-range chunks with a select (no branches around loads).  MFMA
-// operands (8 consecutive tokens of one column per lane) come from two
-// ds_read_b64_tr_b16 each: in every group of 16 lanes, lane i receives element
-// i%4 of the 8-byte piece addressed by lane 4r + i/4 (r = 0..3), so lanes
-// addressing 4 rows x 16 columns get one column each; with the swizzle a
-// half-wave's 4 rows x 64 bytes hit 64 distinct banks.
-// Work placement: workgroup L runs on XCD L % 8.  When the tile count allows
-// (nt % 16 == 0), each XCD gets whole pairs of tile rows {q, nt-1-q} (nt+1
-// tiles per pair), all tiles of one split before the next split, so tiles
-// that share an X panel share an L2 and run at the same tokens.
+// v_mfma_f32_32x32x16).  X stays in its natural [token][column] layout in
+// LDS: stages of 32 tokens, rows of 512 bytes whose 16-byte chunks are
+// XOR-swizzled by (row & 3) << 2, in a ring of four stage buffers.  Stages
+// go from memory straight into LDS (global_load_lds_dwordx4: no registers,
+// no LDS store instructions), three stages ahead, each wave copying 8 KB of
+// every stage; a wave waits for its own copies of the stage it is about to
+// read (s_waitcnt vmcnt), then one barrier makes everyone's copies visible
+// and frees the buffer read in the previous stage for the next copy.  The
+// swizzle is applied on the global side (a lane fetches the chunk its LDS
+// slot will hold); lanes whose token or column is out of range fetch a
+// zeroed 16-byte chunk instead.  The copies are written as inline asm
+// because the compiler, not seeing which buffer a copy writes, would wait
+// for all of them before every LDS read.  MFMA operands (8 consecutive
+// tokens of one column per lane) come from two ds_read_b64_tr_b16 each: in
+// every group of 16 lanes, lane i receives element i%4 of the 8-byte piece
+// addressed by lane 4r + i/4 (r = 0..3), so lanes addressing 4 rows x 16
+// columns get one column each; with the swizzle a half-wave's 4 rows x 64
+// bytes hit 64 distinct banks.
+// Work placement: workgroup L runs on XCD L % 8; see block_tile.
 // Requires d % 8 == 0, ld % 8 == 0 and a 16-byte aligned X.
 constexpr int FT = 256;                 // output tile
 constexpr int FK = 32;                  // tokens per stage
 constexpr int FROW = FT * 2;            // bytes per LDS row (one token)
 constexpr int FOP = FK * FROW;          // bytes per operand per stage (16 KB)
 constexpr int FSTAGE = 2 * FOP;         // bytes per stage (32 KB)
-constexpr int NLD = FSTAGE / (256 * 16);   // 16-byte loads per thread per stage (8)
+constexpr int NBUF = 4;                 // stage buffers in the LDS ring (128 KB)
+// s_waitcnt immediate for vmcnt(8·(NBUF-2)), expcnt/lgkmcnt not waited:
+// vmcnt is split over bits [3:0] and [15:14]
+constexpr int kWaitCount = 8 * (NBUF - 2);
+constexpr int kWaitStage = ((kWaitCount >> 4) << 14) | (kWaitCount & 15) | 0x70 | 0xF00;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
@@ -196,16 +203,38 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int fswz(int row) { return (row & 3) << 2; }
 
+// Tile order for L2 reuse.  The upper-triangle tiles of one split are listed
+// block by block: panels are grouped in fours, blocks (I, J) with I <= J in
+// row-major order, tiles inside a block row-major (upper triangle only on
+// the diagonal).  The list is repeated for every split (split-major), cut
+// into 8 contiguous runs, and workgroup L (which runs on XCD L % 8) takes
+// element L / 8 of run L % 8.  The 32 tiles an XCD runs at once then come
+// from two or three neighbouring blocks of one split, so they read about a
+// dozen panels at the same tokens from one L2.
+__device__ __forceinline__ void block_tile(int r, int nt, int& ti, int& tj) {
+  const int ng = nt / 4;
+  for (int I = 0; I < ng; ++I)
+    for (int J = I; J < ng; ++J) {
+      const int n = (I == J) ? 10 : 16;
+      if (r < n) {
+        int a, b;
+        if (I == J) tile_of(r, 4, a, b);
+        else { a = r / 4; b = r % 4; }
+        ti = 4 * I + a;
+        tj = 4 * J + b;
+        return;
+      }
+      r -= n;
+    }
+  ti = tj = 0;   // not reached for r < nt(nt+1)/2
+}
+
 __device__ __forceinline__ void fast_tile(int L, int nt, int tiles, int& ti, int& tj, int& split) {
-  if (nt % 16 == 0) {
-    const int xcd = L & 7, k = L >> 3;
-    const int per = tiles / 8;                  // tiles per XCD per split
-    split = k / per;
-    const int u = k % per;
-    const int q = (u / (nt + 1)) * 8 + xcd;     // row pair {q, nt-1-q}
-    const int v = u % (nt + 1);
-    if (v < nt - q) { ti = q; tj = q + v; }
-    else { ti = nt - 1 - q; tj = ti + (v - (nt - q)); }
+  const int grid = (int)gridDim.x;
+  if (nt % 4 == 0 && grid % 8 == 0) {
+    const int u = (L & 7) * (grid / 8) + (L >> 3);
+    split = u / tiles;
+    block_tile(u % tiles, nt, ti, tj);
   } else {
     split = L / tiles;
     tile_of(L % tiles, nt, ti, tj);
@@ -214,19 +243,19 @@ __device__ __forceinline__ void fast_tile(int L, int nt, int tiles, int& ti, int
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict__ X, int64_t ld,
-                                                      int d, int64_t n_tok, int64_t chunk, int nt,
-                                                      float* __restrict__ P, int64_t dp) {
+                                                       int d, int64_t n_tok, int64_t chunk, int nt,
+                                                       float* __restrict__ P, int64_t dp,
+                                                       const uint16_t* __restrict__ zero16) {
   const int tiles = nt * (nt + 1) / 2;
   int ti, tj, split;
   fast_tile(blockIdx.x, nt, tiles, ti, tj, split);
   const int64_t t_begin = (int64_t)split * chunk;
   const int64_t t_end = min(n_tok, t_begin + chunk);
   const int nstage = (int)((t_end - t_begin + FK - 1) / FK);
-
-  __shared__ __attribute__((aligned(1024))) char S[2 * FSTAGE];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ __attribute__((aligned(1024))) char S[NBUF * FSTAGE];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -234,37 +263,42 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // loader: chunk idx = t + 256*i: operand idx / (FK*32), row (idx/32) % FK, chunk idx % 32
-  u32x4 ra[NLD], rb[NLD];
-  auto gload = [&](int st, u32x4 (&r)[NLD]) {
+  // DMA plan: wave w's instruction i fills LDS bytes [(8w+i) KB, +1 KB) of a
+  // stage: operand (8w+i)/16, token rows 2((8w+i)%16) + lane/32, 16-byte slot
+  // lane%32 which holds chunk slot ^ swizzle(row).
+  constexpr int NI = FSTAGE / (4 * 1024);   // DMA instructions per wave per stage (8)
+  int64_t coff[NI];
+  int rrow[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int seg = w * NI + i;
+    const int op = seg / (FOP / 1024);
+    const int r = ((seg % (FOP / 1024)) << 1) + (lane >> 5);
+    const int ch = (lane & 31) ^ fswz(r);
+    const int col = (op ? tj : ti) * FT + ch * 8;
+    coff[i] = col < d ? (int64_t)col * 2 : -1;
+    rrow[i] = r;
+  }
+  const unsigned sbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)S;
+  auto dma = [&](int st) {
     const int64_t t0 = t_begin + (int64_t)st * FK;
+    const unsigned lb = sbase + (unsigned)((st % NBUF) * FSTAGE) + (unsigned)(w * NI) * 1024u;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = t + 256 * i;
-      const int op = idx / (FK * 32), row = (idx >> 5) % FK, ch = idx & 31;
-      const int col = (op ? tj : ti) * FT + ch * 8;
-      const int64_t tok = t0 + row;
-      const bool ok = tok < t_end && col < d;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(X + (ok ? tok : t_begin) * ld + (ok ? col : 0));
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      r[i] = ok ? v : zero;
+    for (int i = 0; i < NI; ++i) {
+      const int64_t tok = t0 + rrow[i];
+      const bool ok = tok < t_end && coff[i] >= 0;
+      const char* a = ok ? reinterpret_cast<const char*>(X) + tok * ld * 2 + coff[i]
+                         : reinterpret_cast<const char*>(zero16);
+      // global_load_lds_dwordx4: 16 bytes per lane from address a to LDS
+      // M0 + 16·lane.  It has no register result; the stage's wait below
+      // (s_waitcnt vmcnt) is what orders it before the reads.
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(lb + (unsigned)i * 1024u), "v"(a) : "memory");
     }
   };
-  auto lstore = [&](int st, const u32x4 (&r)[NLD]) {
-    char* base = S + (st & 1) * FSTAGE;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = t + 256 * i;
-      const int op = idx / (FK * 32), row = (idx >> 5) % FK, ch = idx & 31;
-      *reinterpret_cast<u32x4*>(base + op * FOP + row * FROW + ((ch ^ fswz(row)) << 4)) = r[i];
-    }
-  };
-
-  // per-lane tr-read coordinates
   const int g = lane >> 4, j16 = lane & 15;
-  const int rsub = 8 * (g >> 1) + (j16 >> 2);     // + ks*16 + 4h
-  const int csub = 16 * (g & 1) + 4 * (j16 & 3);  // + fragment column base
+  const int rsub = 8 * (g >> 1) + (j16 >> 2);
+  const int csub = 16 * (g & 1) + 4 * (j16 & 3);
   auto frag = [&](const char* base, int colbase, int ks) {
     s16x4 lo, hi;
     {
@@ -280,7 +314,7 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto compute = [&](int st) {
-    const char* SA = S + (st & 1) * FSTAGE;
+    const char* SA = S + (st % NBUF) * FSTAGE;
     const char* SB = SA + FOP;
 #pragma unroll
     for (int ks = 0; ks < FK / 16; ++ks) {
@@ -293,38 +327,25 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-        for (int fj = 0; fj < 4; ++fj) {
+        for (int fj = 0; fj < 4; ++fj)
           if constexpr (BF16)
             acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, a[fi]), __builtin_bit_cast(bf16x8, b[fj]), acc[fi][fj], 0, 0, 0);
           else
             acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 __builtin_bit_cast(f16x8, a[fi]), __builtin_bit_cast(f16x8, b[fj]), acc[fi][fj], 0, 0, 0);
-        }
     }
   };
-
-  // stage s: fetched into register set s%2 at iteration s-2, stored to LDS
-  // buffer s%2 at the end of iteration s-1, multiplied at iteration s.  The
-  // loop runs in pairs so the register sets are named statically.
-  gload(0, ra);
-  gload(1, rb);
-  lstore(0, ra);
-  __syncthreads();
-  for (int st = 0; st < nstage; st += 2) {
-    gload(st + 2, ra);       // past the end: zeros, harmless
+  for (int s = 0; s < NBUF - 1; ++s) dma(s);
+  for (int st = 0; st < nstage; ++st) {
+    // this wave's copies for stage st are done when at most the next
+    // NBUF-2 stages' (8 instructions each) are pending
+    __builtin_amdgcn_s_waitcnt(kWaitStage);
+    __builtin_amdgcn_s_barrier();
+    dma(st + NBUF - 1);
     compute(st);
-    __syncthreads();
-    lstore(st + 1, rb);      // stage st+1 (fetched last iteration)
-    __syncthreads();
-    gload(st + 3, rb);
-    compute(st + 1);         // past the end: an all-zero stage
-    __syncthreads();
-    lstore(st + 2, ra);
-    __syncthreads();
   }
-
-  // epilogue: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32 of each 32x32 tile
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA may outlive the workgroup
   float* Pt = P + (int64_t)split * dp * dp;
 #pragma unroll
   for (int fi = 0; fi < 4; ++fi)
@@ -336,6 +357,12 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
         const int cl = tj * FT + wn * 128 + fj * 32 + (lane & 31);
         Pt[(int64_t)row * dp + cl] = acc[fi][fj][r];
       }
+}
+
+// The 256-byte zero chunk of the workspace (a fill kernel, not a memset, so
+// a captured graph replays it correctly).
+__global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z) {
+  z[threadIdx.x] = 0u;
 }
 
 // H[i][j] += 2·Σ_s P_s[i][j] over the upper triangle, and the mirrored
@@ -440,7 +467,8 @@ size_t hessian_ws_bytes(int64_t d, int64_t n_tok) {
   const int64_t dpg = ceil_div(d, FT) * FT;
   const size_t fast = (size_t)fast_splits(d, n_tok) * dpg * dpg * sizeof(float);
   const size_t gen = (size_t)generic_splits(d, n_tok) * dpg * dpg * sizeof(float);
-  return align_up(std::max<size_t>(std::max(fast, gen), 256));
+  // + a 256-byte zero chunk after the partials (source of out-of-range copies)
+  return align_up(std::max<size_t>(std::max(fast, gen), 256)) + 256;
 }
 
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
@@ -457,12 +485,16 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
     splits = fast_splits(d, n_tok);
     const int64_t chunk = ceil_div(ceil_div(n_tok, splits), FK) * FK;
     const unsigned grid = (unsigned)(tiles * splits);
+    uint16_t* zero16 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+                                                   hessian_ws_bytes(d, n_tok) - 256);
+    zero_chunk_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(zero16));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (x_dtype == GPTQ_BF16)
       syrk256_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
-                                                chunk, nt, P, dp);
+                                                chunk, nt, P, dp, zero16);
     else
       syrk256_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
-                                                 n_tok, chunk, nt, P, dp);
+                                                 n_tok, chunk, nt, P, dp, zero16);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
     const int nt = (int)ceil_div(d, HT);
