@@ -266,9 +266,10 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
   // DMA plan: wave w's instruction i fills LDS bytes [(8w+i) KB, +1 KB) of a
   // stage: operand (8w+i)/16, token rows 2((8w+i)%16) + lane/32, 16-byte slot
   // lane%32 which holds chunk slot ^ swizzle(row).
-  constexpr int NI = FSTAGE / (4 * 1024);   // DMA instructions per wave per stage (8)
-  int64_t coff[NI];
+  constexpr int NI = FSTAGE / (4 * 1024);   // copy instructions per wave per stage (8)
+  const char* pbase[NI];   // this lane's source for stage 0 (zero chunk if the column is out)
   int rrow[NI];
+  bool colok[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int seg = w * NI + i;
@@ -276,19 +277,21 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
     const int r = ((seg % (FOP / 1024)) << 1) + (lane >> 5);
     const int ch = (lane & 31) ^ fswz(r);
     const int col = (op ? tj : ti) * FT + ch * 8;
-    coff[i] = col < d ? (int64_t)col * 2 : -1;
+    colok[i] = col < d;
     rrow[i] = r;
+    pbase[i] = colok[i] ? reinterpret_cast<const char*>(X) + (t_begin + r) * ld * 2 + (int64_t)col * 2
+                        : reinterpret_cast<const char*>(zero16);
   }
   const unsigned sbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)S;
+  const int nrows = (int)(t_end - t_begin);
   auto dma = [&](int st) {
-    const int64_t t0 = t_begin + (int64_t)st * FK;
+    const int rem = min(max(nrows - st * FK, 0), FK);   // valid token rows of the stage
+    const int64_t soff = (int64_t)st * FK * ld * 2;
     const unsigned lb = sbase + (unsigned)((st % NBUF) * FSTAGE) + (unsigned)(w * NI) * 1024u;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int64_t tok = t0 + rrow[i];
-      const bool ok = tok < t_end && coff[i] >= 0;
-      const char* a = ok ? reinterpret_cast<const char*>(X) + tok * ld * 2 + coff[i]
-                         : reinterpret_cast<const char*>(zero16);
+      const bool ok = colok[i] && rrow[i] < rem;
+      const char* a = ok ? pbase[i] + soff : reinterpret_cast<const char*>(zero16);
       // global_load_lds_dwordx4: 16 bytes per lane from address a to LDS
       // M0 + 16·lane.  It has no register result; the stage's wait below
       // (s_waitcnt vmcnt) is what orders it before the reads.
@@ -313,37 +316,41 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
     }
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  auto compute = [&](int st) {
+  auto frags = [&](int st, int ks, s16x8 (&a)[4], s16x8 (&b)[4]) {
     const char* SA = S + (st % NBUF) * FSTAGE;
     const char* SB = SA + FOP;
 #pragma unroll
-    for (int ks = 0; ks < FK / 16; ++ks) {
-      s16x8 a[4], b[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        a[f] = frag(SA, wm * 128 + f * 32, ks);
-        b[f] = frag(SB, wn * 128 + f * 32, ks);
-      }
-#pragma unroll
-      for (int fi = 0; fi < 4; ++fi)
-#pragma unroll
-        for (int fj = 0; fj < 4; ++fj)
-          if constexpr (BF16)
-            acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, a[fi]), __builtin_bit_cast(bf16x8, b[fj]), acc[fi][fj], 0, 0, 0);
-          else
-            acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, a[fi]), __builtin_bit_cast(f16x8, b[fj]), acc[fi][fj], 0, 0, 0);
+    for (int f = 0; f < 4; ++f) {
+      a[f] = frag(SA, wm * 128 + f * 32, ks);
+      b[f] = frag(SB, wn * 128 + f * 32, ks);
     }
   };
-  for (int s = 0; s < NBUF - 1; ++s) dma(s);
+  auto mfma = [&](const s16x8 (&a)[4], const s16x8 (&b)[4]) {
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj) {
+        if constexpr (BF16)
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a[fi]), __builtin_bit_cast(bf16x8, b[fj]), acc[fi][fj], 0, 0, 0);
+        else
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, a[fi]), __builtin_bit_cast(f16x8, b[fj]), acc[fi][fj], 0, 0, 0);
+      }
+  };
+  static_assert(FK == 32, "a stage is two 16-token MFMA steps");
+  for (int s0 = 0; s0 < NBUF - 1; ++s0) dma(s0);
   for (int st = 0; st < nstage; ++st) {
     // this wave's copies for stage st are done when at most the next
     // NBUF-2 stages' (8 instructions each) are pending
     __builtin_amdgcn_s_waitcnt(kWaitStage);
     __builtin_amdgcn_s_barrier();
-    dma(st + NBUF - 1);
-    compute(st);
+    s16x8 a0[4], b0[4], a1[4], b1[4];
+    frags(st, 0, a0, b0);          // first: the reads that feed the first products
+    dma(st + NBUF - 1);            // then the copy into the buffer freed by the barrier
+    frags(st, 1, a1, b1);
+    mfma(a0, b0);
+    mfma(a1, b1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA may outlive the workgroup
   float* Pt = P + (int64_t)split * dp * dp;
