@@ -192,10 +192,13 @@ constexpr int FROW = FT * 2;            // bytes per LDS row (one token)
 constexpr int FOP = FK * FROW;          // bytes per operand per stage (16 KB)
 constexpr int FSTAGE = 2 * FOP;         // bytes per stage (32 KB)
 constexpr int NBUF = 4;                 // stage buffers in the LDS ring (128 KB)
-// s_waitcnt immediate for vmcnt(8·(NBUF-2)), expcnt/lgkmcnt not waited:
-// vmcnt is split over bits [3:0] and [15:14]
+// s_waitcnt immediates (vmcnt is split over bits [3:0] and [15:14];
+// expcnt/lgkmcnt not waited): in the loop, 2 stages of copies (8
+// instructions each) may stay pending; before it, one
 constexpr int kWaitCount = 8 * (NBUF - 2);
 constexpr int kWaitStage = ((kWaitCount >> 4) << 14) | (kWaitCount & 15) | 0x70 | 0xF00;
+constexpr int kWaitFirstCount = 8 * (NBUF - 3);   // before the loop: stages 0 and 1 done
+constexpr int kWaitFirst = ((kWaitFirstCount >> 4) << 14) | (kWaitFirstCount & 15) | 0x70 | 0xF00;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
@@ -340,16 +343,23 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
   };
   static_assert(FK == 32, "a stage is two 16-token MFMA steps");
   for (int s0 = 0; s0 < NBUF - 1; ++s0) dma(s0);
+  // Stage st's first-step fragments are read during stage st-1, so each
+  // stage waits for its wave's copies of stage st+1 (the copies of the two
+  // stages after it stay in flight), and the barrier makes both stages
+  // visible and frees the buffer read in stage st-1 for the next copy.
+  s16x8 a0[4], b0[4], a1[4], b1[4];
+  __builtin_amdgcn_s_waitcnt(kWaitFirst);
+  __builtin_amdgcn_s_barrier();
+  frags(0, 0, a0, b0);
   for (int st = 0; st < nstage; ++st) {
-    // this wave's copies for stage st are done when at most the next
-    // NBUF-2 stages' (8 instructions each) are pending
-    __builtin_amdgcn_s_waitcnt(kWaitStage);
-    __builtin_amdgcn_s_barrier();
-    s16x8 a0[4], b0[4], a1[4], b1[4];
-    frags(st, 0, a0, b0);          // first: the reads that feed the first products
-    dma(st + NBUF - 1);            // then the copy into the buffer freed by the barrier
+    dma(st + NBUF - 1);            // into the buffer the previous barrier freed
     frags(st, 1, a1, b1);
     mfma(a0, b0);
+    // lgkmcnt(0) as well: every wave's reads of this stage's buffer are
+    // complete before the barrier after which it is copied over again
+    __builtin_amdgcn_s_waitcnt(kWaitStage & ~0xF00);
+    __builtin_amdgcn_s_barrier();
+    frags(st + 1, 0, a0, b0);      // the next stage's first step
     mfma(a1, b1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA may outlive the workgroup
