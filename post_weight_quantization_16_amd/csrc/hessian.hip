@@ -384,9 +384,12 @@ __global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z
 
 // H[i][j] += 2·Σ_s P_s[i][j] over the upper triangle, and the mirrored
 // H[j][i] = H[i][j], one 128x128 upper tile (ti <= tj) per workgroup.  The
-// split partials are summed in a fixed order (deterministic); each thread
-// owns float4 runs of the tile, and the finished tile goes through LDS to
-// be written transposed, so both writes are coalesced.
+// split partials are summed in a fixed order (deterministic).  Each thread
+// owns 16 float4 runs of the tile and issues all of a split's loads before
+// adding them, and all of its H reads before any H write (reads after a
+// write through the same pointer would each wait a memory round trip); the
+// finished tile goes through LDS to be written transposed, so both writes
+// are coalesced.
 __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
                                                             const float* __restrict__ P,
                                                             int64_t dp, int splits, int nt,
@@ -395,33 +398,49 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
   tile_of(blockIdx.x, nt, ti, tj);
   __shared__ float T[HT][HT + 1];
   const int t = threadIdx.x;
+  constexpr int NR = HT * HT / (256 * 4);   // float4 runs per thread (16)
   const int64_t pstride = dp * dp;
-#pragma unroll 4
-  for (int it = 0; it < HT * HT / (256 * 4); ++it) {
-    const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
-    const int i = ti * HT + a, j = tj * HT + b4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const float* src = P + (int64_t)i * dp + j;   // i, j < dp: always inside the partials
-    for (int sp = 0; sp < splits; ++sp) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + sp * pstride);
+  const float* src = P + (int64_t)(ti * HT) * dp + tj * HT;   // always inside the partials
+  f32x4 acc[NR];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+  for (int it = 0; it < NR; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; ++sp) {
+    f32x4 v[NR];
+#pragma unroll
+    for (int it = 0; it < NR; ++it) {
+      const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+      v[it] = *reinterpret_cast<const f32x4*>(src + sp * pstride + (int64_t)a * dp + b4);
     }
-    if (vec_h && ti < tj && i < d && j + 3 < d) {
-      f32x4* hp = reinterpret_cast<f32x4*>(H + (int64_t)i * d + j);
-      f32x4 h = *hp;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = fmaf(2.f, acc[q], h[q]);
-      *hp = h;
+    for (int it = 0; it < NR; ++it) acc[it] += v[it];
+  }
+  const bool full = vec_h && ti < tj && (tj + 1) * HT <= d;
+  if (full) {
+    f32x4 h[NR];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) T[a][b4 + q] = h[q];
-    } else {
+    for (int it = 0; it < NR; ++it) {
+      const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+      h[it] = *reinterpret_cast<const f32x4*>(H + (int64_t)(ti * HT + a) * d + tj * HT + b4);
+    }
+#pragma unroll
+    for (int it = 0; it < NR; ++it) {
+      const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[it][q] = fmaf(2.f, acc[it][q], h[it][q]);
+      *reinterpret_cast<f32x4*>(H + (int64_t)(ti * HT + a) * d + tj * HT + b4) = h[it];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[a][b4 + q] = h[it][q];
+    }
+  } else {
+    for (int it = 0; it < NR; ++it) {
+      const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+      const int i = ti * HT + a;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int jq = j + q;
+        const int jq = tj * HT + b4 + q;
         float v = 0.f;
         if (i < d && jq < d && jq >= i) {
-          v = fmaf(2.f, acc[q], H[(int64_t)i * d + jq]);
+          v = fmaf(2.f, acc[it][q], H[(int64_t)i * d + jq]);
           H[(int64_t)i * d + jq] = v;
         }
         T[a][b4 + q] = v;
