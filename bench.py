@@ -43,6 +43,45 @@ def work_figures(m, d, n_tok, B=128):
     }
 
 
+# HBM bytes per gptq_hessian_accumulate call on the 4096x4096, 131072-token
+# workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
+# `bench.py --steps 2 --warmup 1 --no-cpu-baseline` (KiB per dispatch, summed
+# over the call's two kernels), each scaled by the counter's reading for a
+# plain copy of known size (`bench.py --copy-calibration 512`).  Valid only
+# for the Hessian source they were taken on: any change to it reports null.
+HESSIAN_TRAFFIC = {
+    "source_sha256": "4092bce7ddb8971f900c91bd63f01e28aa58efbb23b2226a4080af67cc8400a2",
+    # zero_chunk_kernel + syrk256_kernel + reduce_mirror_kernel, KiB per call
+    "fetch_kib": 1.5 + 1872704.4 + 134882.6, "fetch_scale": 524288 / 262159.6,
+    "write_kib": 0.2 + 243712.0 + 65651.3, "write_scale": 524288 / 524288.0,
+}
+
+
+def hessian_traffic():
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                       "post_weight_quantization_16_amd", "csrc", "hessian.hip")
+    t = HESSIAN_TRAFFIC
+    if t["source_sha256"] is None:
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["source_sha256"]:
+            return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {mib} MiB (read {mib} MiB, write {mib} MiB each)")
+
+
 def cpu_baseline(wl, W, X, tok_sample, row_sample):
     """Time the fp64 oracle as it stands on a bounded sample and scale to one layer."""
     import numpy as np
@@ -91,11 +130,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU path only (the layer runs on one MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -128,8 +172,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
-        if ev: ev[0].record(stream)
         H.zero_()
+        if ev: ev[0].record(stream)
         gq.hessian_accumulate(H, X, ws=ws_h)
         if ev: ev[1].record(stream)
         prep = gq.prepare_hinv(H, params, ws=ws_p)
@@ -178,13 +222,13 @@ def main():
             "quantize_update_tflops": wf["update_flop"] / (q_ms * 1e-3) / 1e12,
         },
         "roofline": {
-            "kernel": "hessian_accumulate (bf16 MFMA SYRK + split-K reduction)",
+            "kernel": "gptq_hessian_accumulate (syrk256_kernel + reduce_mirror_kernel)",
             "bound": "mfma",
             "achieved": h_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": h_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": hessian_traffic(),
         },
     }
     if not args.no_cpu_baseline:
