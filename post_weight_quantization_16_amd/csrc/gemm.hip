@@ -1,6 +1,6 @@
 // fp32 MFMA GEMM for gfx950: the lazy block updates of the GPTQ sweep and the
 // products of the triangular inverse (the tile itself is in gemm_tile.hpp).
-#include "gemm_tile.hpp"
+#include "gemm_dma.hpp"
 
 namespace gq {
 namespace gemm_detail {
@@ -21,10 +21,32 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g, int nx, int ny) 
   gemm_tile<T, TA, TB>(g, bx, by, blockIdx.z, gridDim.z, Sm);
 }
 
+// Ring depth of the DMA tile: four 16-KB stages for T = 128 (two
+// workgroups per CU), six 8-KB stages for T = 64 (three per CU).
+template <int T> constexpr int kRing = T == 128 ? 4 : 6;
+
+template <int T, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_dma_kernel(KArgs g, int nx, int ny) {
+  __shared__ __attribute__((aligned(1024))) char Sm[DTile<T, kRing<T>>::SMEM];
+  const int L = blockIdx.x;
+  int bx, by;
+  if (g.k_from_n) { bx = L / ny; by = L % ny; }
+  else if (g.k_to_m) { by = ny - 1 - L / nx; bx = L % nx; }
+  else { by = L / nx; bx = L % nx; }
+  gemm_tile_dma<T, kRing<T>, TA, TB>(g, bx, by, blockIdx.z, gridDim.z, Sm);
+}
+
 template <int T>
 void launch(const KArgs& k, const GemmArgs& a, hipStream_t s) {
   const int nx = (int)ceil_div(a.N, T), ny = (int)ceil_div(a.M, T);
   dim3 grid((unsigned)(nx * ny), 1, (unsigned)a.batch);
+  if (dma_ok(k, a.trans_a, a.trans_b)) {
+    if (!a.trans_a && !a.trans_b) gemm_dma_kernel<T, false, false><<<grid, 256, 0, s>>>(k, nx, ny);
+    else if (!a.trans_a && a.trans_b) gemm_dma_kernel<T, false, true><<<grid, 256, 0, s>>>(k, nx, ny);
+    else if (a.trans_a && !a.trans_b) gemm_dma_kernel<T, true, false><<<grid, 256, 0, s>>>(k, nx, ny);
+    else gemm_dma_kernel<T, true, true><<<grid, 256, 0, s>>>(k, nx, ny);
+    return;
+  }
   if (!a.trans_a && !a.trans_b) gemm_f32_kernel<T, false, false><<<grid, 256, 0, s>>>(k, nx, ny);
   else if (!a.trans_a && a.trans_b) gemm_f32_kernel<T, false, true><<<grid, 256, 0, s>>>(k, nx, ny);
   else if (a.trans_a && !a.trans_b) gemm_f32_kernel<T, true, false><<<grid, 256, 0, s>>>(k, nx, ny);

@@ -112,6 +112,69 @@ __device__ __forceinline__ float opread(const float* s, int a, int k) {
   return ALONG ? s[k * Tile<T>::SA + a] : s[a * Tile<T>::SK + k];
 }
 
+// C[m0.., n0..] = E + beta·C for one T x T tile staged in LDS (row stride
+// ES), honouring the edges and the triangle mask (tri 1: lower, 2: upper).
+// All of a thread's C reads are issued before any of its writes: C is read
+// and written through one pointer, so a read placed after a write would
+// wait for that write's full round trip.  In-range tiles move float4 (a
+// float4 straddling the diagonal is written element by element).
+template <int T, int ES>
+__device__ __forceinline__ void store_tile(const KArgs& g, const float* E, float* C, int m0,
+                                           int n0, int t) {
+  const bool has_beta = g.beta != 0.f;
+  const int mvalid = g.M - m0, nvalid = g.N - n0;
+  if (mvalid >= T && nvalid >= T && g.vec_c) {
+    constexpr int NE = T * T / 1024;
+    f32x4 cv[NE];
+    if (has_beta) {
+#pragma unroll
+      for (int u = 0; u < NE; ++u) {
+        const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
+        cv[u] = *reinterpret_cast<const f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
+      f32x4 v = *reinterpret_cast<const f32x4*>(E + row * ES + c4);
+      if (has_beta) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = fmaf(g.beta, cv[u][q], v[q]);
+      }
+      float* dst = C + (int64_t)(m0 + row) * g.ldc + n0 + c4;
+      const int gr = m0 + row, gc = n0 + c4;
+      const bool all = g.tri == 0 || (g.tri == 1 && gc + 3 <= gr) || (g.tri == 2 && gc >= gr);
+      if (all) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (g.tri == 1 ? gc + q <= gr : gc + q >= gr) dst[q] = v[q];
+      }
+    }
+  } else {
+    // edge tile: element-wise, every read (at a clamped, valid address)
+    // issued before the masked writes
+    constexpr int NE = T * T / 256;
+    float cs[NE];
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = t + 256 * u, row = e / T, col = e % T;
+      const int rr = min(row, mvalid - 1), cc = min(col, nvalid - 1);
+      cs[u] = has_beta ? C[(int64_t)(m0 + rr) * g.ldc + n0 + cc] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = t + 256 * u, row = e / T, col = e % T;
+      const int gr = m0 + row, gc = n0 + col;
+      bool ok = row < mvalid && col < nvalid;
+      if (g.tri == 1) ok = ok && gc <= gr;
+      if (g.tri == 2) ok = ok && gc >= gr;
+      if (ok) C[(int64_t)gr * g.ldc + gc] = fmaf(g.beta, cs[u], E[row * ES + col]);
+    }
+  }
+}
+
 // One T x T output tile (bx, by) of batch z; nz = number of batches.
 // Sm: GEMM_SMEM_FLOATS floats of LDS.  All 256 threads of the workgroup
 // must call it (it synchronizes).
@@ -189,12 +252,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
   }
 
   // Epilogue through LDS (the operand buffers are free after the loop's last
-  // barrier): the tile goes to LDS as alpha·acc, then every thread owns
-  // T·T/1024 float4 of it.  All of a thread's C reads are issued before any
-  // of its writes -- C is read and written through one pointer, so reads
-  // placed after writes would each wait for a full memory round trip.
+  // barrier): the tile goes to LDS as alpha·acc, then is merged into C.
   // MFMA layout: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32.
-  constexpr int ES = TL::ES, NE = T * T / 1024;
   float* E = Sm;
 #pragma unroll
   for (int i = 0; i < FI; ++i)
@@ -204,53 +263,10 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
       for (int r = 0; r < 16; ++r) {
         const int row = wm * WT + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int col = wn * WT + j * 32 + (lane & 31);
-        E[row * ES + col] = g.alpha * acc[i][j][r];
+        E[row * TL::ES + col] = g.alpha * acc[i][j][r];
       }
   __syncthreads();
-  const bool has_beta = g.beta != 0.f;
-  const bool tri_all = g.tri == 0 || (g.tri == 1 && n0 + T - 1 <= m0) ||
-                       (g.tri == 2 && n0 >= m0 + T - 1);
-  if (tri_all && mvalid >= T && nvalid >= T && g.vec_c) {
-    f32x4 cv[NE];
-    if (has_beta) {
-#pragma unroll
-      for (int u = 0; u < NE; ++u) {
-        const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
-        cv[u] = *reinterpret_cast<const f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NE; ++u) {
-      const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
-      f32x4 v = *reinterpret_cast<const f32x4*>(E + row * ES + c4);
-      if (has_beta) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = fmaf(g.beta, cv[u][q], v[q]);
-      }
-      *reinterpret_cast<f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4) = v;
-    }
-  } else {
-    // edge or diagonal tile: element-wise, reads (at clamped, valid
-    // addresses) batched ahead of the masked writes 16 at a time
-    for (int e0 = 0; e0 < T * T; e0 += 256 * 16) {
-      float cs[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = e0 + t + 256 * u, row = e / T, col = e % T;
-        const int rr = min(row, mvalid - 1), cc = min(col, nvalid - 1);
-        cs[u] = has_beta ? C[(int64_t)(m0 + rr) * g.ldc + n0 + cc] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = e0 + t + 256 * u, row = e / T, col = e % T;
-        const int gr = m0 + row, gc = n0 + col;
-        bool ok = row < mvalid && col < nvalid;
-        if (g.tri == 1) ok = ok && gc <= gr;
-        if (g.tri == 2) ok = ok && gc >= gr;
-        if (ok) C[(int64_t)gr * g.ldc + gc] = fmaf(g.beta, cs[u], E[row * ES + col]);
-      }
-    }
-  }
+  store_tile<T, TL::ES>(g, E, C, m0, n0, t);
 }
 
 // Kernel arguments for a host-side GemmArgs (vector-load eligibility included).

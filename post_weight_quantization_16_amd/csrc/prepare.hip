@@ -13,16 +13,19 @@
 // U = J·L⁻¹·J, the unique upper factor with positive diagonal.  Two O(d³)
 // steps, both fp32: a blocked right-looking Cholesky with 64-wide panels
 // (each diagonal block factored and inverted together, the panel below
-// solved with that inverse; one launch per panel that also runs the previous
-// panel's trailing update on fp32 MFMA GEMM tiles), then the rest of the
-// triangular inverse by recursive
+// solved with that inverse; one launch per panel that also runs trailing
+// updates on fp32 MFMA GEMM tiles: rank-64 near the panel, rank-128 tiles
+// further right spread over the launches), then the rest of the triangular
+// inverse by recursive
 // doubling ([[A,0],[B,C]]⁻¹ has off-diagonal block −C⁻¹·B·A⁻¹, products
 // skipping the zero triangles).
 #include <algorithm>
 #include <climits>
+#include <vector>
 
 #include "common.hpp"
-#include "gemm_tile.hpp"
+#include "chol_sched.hpp"
+#include "gemm_dma.hpp"
 
 namespace gq {
 namespace {
@@ -106,6 +109,7 @@ struct PanelArgs {
 };
 
 constexpr int LS = NB + 2;       // LDS row stride: the half-waves' MFMA reads hit disjoint banks
+constexpr int PXS = NB + 1;      // stride of the published x rows (strip MFMA reads of 16 rows)
 constexpr int BLK = NB * LS;     // one 64x64 block in LDS (floats)
 static_assert(4 * BLK + 4 * NB <= gemm_detail::GEMM_SMEM_FLOATS, "panel LDS exceeds the shared buffer");
 
@@ -129,41 +133,79 @@ __device__ __forceinline__ int acc_row(int mi, int lane, int e) {
 // One 64-wide Cholesky panel at column k0 (kb <= 64 columns), for workgroup
 // b of the panel's grid:
 //   first, the previous panel's contribution to this panel's columns,
-//     G[:, panel] −= L21ₚ·L21ₚ[panel rows]ᵀ (the trailing update of the
-//     previous step skips these columns so this launch can run it),
+//     G[:, panel] −= L21ₚ·L21ₚ[panel rows]ᵀ (the trailing updates of the
+//     previous launch skip these columns so this launch can run it),
 //   L11 = chol(G11),  X = L11⁻¹,  L21 = G21·Xᵀ.
 // Every workgroup (4 waves) factors and inverts the small diagonal block
 // itself, so no workgroup waits for another; workgroup b then solves the
-// 64 rows k0+kb+64b .. +63 of the panel with one 64x64x64 fp32 MFMA product,
-// in place in G, and workgroup 0 stores X into the diagonal block of Linv
-// (L11 itself is not needed later).  The block is padded to 64 with the
-// identity.
+// 64 rows k0+kb+64b .. +63 of the panel in place in G, and workgroup 0
+// stores X into the diagonal block of Linv (L11 itself is not needed
+// later).  The block is padded to 64 with the identity.
 //
 // The factor and the inverse are one right-looking sweep.  Lane i of wave w
 // holds A[i][16w..16w+15] (a) and X[16w..16w+15][i] (r).  Wave w owns steps
 // 16w..16w+15: step j takes the pivot from lane j, scales column j into
-// l_ij = a_ij / l_jj (zeroed for i <= j), finishes x_j = r_j / l_jj, applies
-// a_ik −= l_ij·l_kj and r_k −= l_kj·x_j to its own later columns (l_kj read
-// from lane k with readlane) and publishes l and x for step j in LDS with a
-// flag.  Before its own steps, wave w consumes steps 0 .. 16w−1 as their
-// flags appear, applying the same update to its 16 columns.  The owner of a
-// step never waits for another wave, so the serial chain carries no
-// workgroup barrier; every wait is on a step some wave has already begun or
-// will begin without waiting (wave 0 waits for nothing), and is bounded.
-// A non-positive (or NaN/inf) pivot is recorded in *status (smallest index
-// wins) and replaced by 1 so the arithmetic stays finite.
+// l_ij = a_ij / l_jj (zeroed for i <= j), finishes x_j = r_j / l_jj,
+// applies a_ik −= l_ij·l_kj and r_k −= l_kj·x_j to its next column at once
+// (l_kj from lane k by readlane: that column's pivot is next), publishes l
+// and x for step j in LDS, updates its remaining columns with l_kj read back
+// from the published row, and raises the step's flag.  Before its own
+// steps, wave w consumes steps 0 .. 16w−1 four at a time as their flags
+// appear, applying the same update to its 16 columns; the last four are
+// held in registers and applied to each column just before its pivot, so
+// the hand-over from wave w−1 waits for one batch of reads, not for the
+// whole batch's arithmetic.  The owner of a step never waits for another
+// wave, so the serial chain carries no workgroup barrier; every wait is on a
+// step some wave has already begun or will begin without waiting (wave 0
+// waits for nothing), and is bounded.  A non-positive (or NaN/inf) pivot is
+// recorded in *status (smallest index wins) and replaced by 1 so the
+// arithmetic stays finite.
+//
+// L21's 16-column strips: X's rows 16w..16w+15 are final once wave w's
+// steps are done, so wave w (w < 3) solves its strip L21[:, 16w..] =
+// G21·X[16w..16w+15, :]ᵀ (v_mfma_f32_16x16x4f32, 64 rows) while the later
+// waves are still sweeping, and workgroup 0's wave w stores those X rows to
+// Linv from its registers.  The last strip is split over the four waves
+// after the sweep.
+// L21[16rb.., 16c..16c+15] for row blocks rb in [rb0, rb1) of this
+// workgroup's 64 rows: G21 (BS, already reduced by the pre-update) times the
+// published X rows 16c..16c+15 (PX), v_mfma_f32_16x16x4f32 (A: lane holds
+// (row lane%16, k lane/16), B: (k lane/16, column lane%16), C: rows
+// 4·(lane/16) + v, column lane%16), stored to G.
+__device__ __forceinline__ void strip(const float* BS, const float* PX, float* G, int64_t d,
+                                      int64_t R0, int k0, int kb, int c, int rb0, int rb1,
+                                      int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  for (int rb = rb0; rb < rb1; ++rb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k4 = 0; k4 < NB; k4 += 4) {
+      const float av = BS[(16 * rb + m) * LS + k4 + kq];
+      const float bv = PX[(16 * c + m) * PXS + k4 + kq];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    }
+    const int col = 16 * c + m;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = R0 + 16 * rb + 4 * kq + v;
+      if (row < d && col < kb) G[row * d + k0 + col] = acc[v];
+    }
+  }
+}
+
 constexpr int kSpinLimit = 1 << 20;   // safety bound on a flag wait (never reached)
 
 __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __restrict__ smem) {
   float* AS = smem;              // G11 (lower, identity-padded)
   float* BS = smem + BLK;        // this workgroup's 64 rows of G21
-  float* XS = smem + 2 * BLK;    // X; before the sweep: the previous panel's rows k0..k0+63
-  float* QS = smem + 3 * BLK;    // the previous panel's values in this workgroup's rows
-  // during the sweep XS and QS hold the published steps: l [64][64], x [64][64], flags [64]
-  float* PL = smem + 2 * BLK;
-  float* PX = PL + NB * NB;
-  int* flag = reinterpret_cast<int*>(PX + NB * NB);
-  static_assert(2 * NB * NB + NB <= 2 * BLK, "published steps exceed their LDS region");
+  float* XS = smem + 2 * BLK;    // before the sweep: the previous panel's rows k0..k0+63
+  float* QS = smem + 3 * BLK;    // before the sweep: the previous panel's values in this workgroup's rows
+  // during and after the sweep: published l [64][64] in AS's place, x [64][PXS]
+  // (= X by rows) in XS's place, flags [64] in QS's place
+  float* PL = smem;
+  float* PX = smem + 2 * BLK;
+  int* flag = reinterpret_cast<int*>(smem + 3 * BLK);
+  static_assert(NB * NB <= BLK && NB * PXS <= BLK, "published steps exceed their LDS region");
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t d = p.d;
@@ -236,13 +278,16 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     r[q] = (16 * w + q == lane) ? 1.f : 0.f;
   }
   if (t < NB) flag[t] = 0;
-  __syncthreads();
+  __syncthreads();   // AS is read: PL may overwrite it
 
   // consume the steps of the waves before this one, four at a time: one
   // wait on the fourth step's flag covers all four (one wave publishes them
-  // in order, each flag a release of the writes before it)
+  // in order, each flag a release of the writes before it); the last four
+  // stay pending (pl, px, pc) and meet each column just before its pivot
   int bad_j = -1;
   bool stalled = false;   // after one expired wait, stop waiting (the result is flagged bad)
+  float pl[4], px[4];
+  f32x4 pc[4][4];
   for (int j0 = 0; j0 < 16 * w; j0 += 4) {
     int spin = 0;
     while (!stalled &&
@@ -253,30 +298,39 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    float li[4], xv[4];
-    f32x4 cv[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      li[u] = PL[(j0 + u) * NB + lane];
-      xv[u] = PX[(j0 + u) * NB + lane];
+      pl[u] = PL[(j0 + u) * NB + lane];
+      px[u] = PX[(j0 + u) * PXS + lane];
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        cv[u][h] = *reinterpret_cast<const f32x4*>(PL + (j0 + u) * NB + 16 * w + 4 * h);
+        pc[u][h] = *reinterpret_cast<const f32x4*>(PL + (j0 + u) * NB + 16 * w + 4 * h);
     }
+    if (j0 + 4 < 16 * w) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float c = cv[u][q >> 2][q & 3];
-        a[q] = fmaf(-li[u], c, a[q]);
-        r[q] = fmaf(-c, xv[u], r[q]);
-      }
+        for (int q = 0; q < 16; ++q) {
+          const float c = pc[u][q >> 2][q & 3];
+          a[q] = fmaf(-pl[u], c, a[q]);
+          r[q] = fmaf(-c, px[u], r[q]);
+        }
+    }
   }
-  // own steps: the next column's update first (it feeds the next pivot),
-  // then the publication, the remaining columns, and the step's flag
+  // own steps
 #pragma unroll
   for (int q0 = 0; q0 < 16; ++q0) {
     const int j = 16 * w + q0;
+    // the pending last batch meets column 0 here and column q0 + 1 below,
+    // so every column sees it exactly once, before its pivot
+    if (w > 0 && q0 == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float c = pc[u][q0 >> 2][q0 & 3];
+        a[q0] = fmaf(-pl[u], c, a[q0]);
+        r[q0] = fmaf(-c, px[u], r[q0]);
+      }
+    }
     const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
     const bool bad = !(piv > 0.f) || !(piv < INFINITY);
     bad_j = (bad && bad_j < 0) ? j : bad_j;
@@ -285,43 +339,51 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     const float l = lane > j ? a[q0] * inv : 0.f;
     const float x = r[q0] * inv;
     r[q0] = x;
-    if (q0 + 1 < 16) {
+    if (q0 + 1 < 16) {   // the next column feeds the next pivot
+      if (w > 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float c = pc[u][(q0 + 1) >> 2][(q0 + 1) & 3];
+          a[q0 + 1] = fmaf(-pl[u], c, a[q0 + 1]);
+          r[q0 + 1] = fmaf(-c, px[u], r[q0 + 1]);
+        }
+      }
       const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), j + 1));
       a[q0 + 1] = fmaf(-l, c, a[q0 + 1]);
       r[q0 + 1] = fmaf(-c, x, r[q0 + 1]);
     }
     PL[j * NB + lane] = l;
-    PX[j * NB + lane] = x;
+    PX[j * PXS + lane] = x;
+    if (q0 + 2 < 16) {
+      // l_kj of the remaining columns, read back from the row just
+      // published (this wave's own writes, in order)
+      f32x4 cv[4];
 #pragma unroll
-    for (int q = q0 + 2; q < 16; ++q) {
-      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 16 * w + q));
-      a[q] = fmaf(-l, c, a[q]);
-      r[q] = fmaf(-c, x, r[q]);
+      for (int h = (q0 + 2) >> 2; h < 4; ++h)
+        cv[h] = *reinterpret_cast<const f32x4*>(PL + j * NB + 16 * w + 4 * h);
+#pragma unroll
+      for (int q = q0 + 2; q < 16; ++q) {
+        const float c = cv[q >> 2][q & 3];
+        a[q] = fmaf(-l, c, a[q]);
+        r[q] = fmaf(-c, x, r[q]);
+      }
     }
+    // the flag goes up after the step's updates: its release then finds
+    // the published writes long done
+    __builtin_amdgcn_sched_barrier(0);
     __hip_atomic_store(&flag[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 16; ++q) XS[(16 * w + q) * LS + lane] = r[q];
-  __syncthreads();
   if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
-  if (b == 0) {
-    for (int e = t; e < kb * kb; e += 256) {
-      const int rr = e / kb, c = e % kb;
-      p.Linv[(int64_t)(k0 + rr) * d + k0 + c] = XS[rr * LS + c];
-    }
-  }
-  if (R0 >= d) return;
-  // L21 block = G21 block · Xᵀ, wave w the 32x32 tile (w/2, w%2)
-  f32x16 acc;
+  // X rows 16w..16w+15 are final: workgroup 0 stores them to Linv
+  if (b == 0 && lane < kb) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  mfma_abt(BS, XS, mi, ni, lane, acc);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int row = acc_row(mi, lane, e), col = 32 * ni + (lane & 31);
-    if (R0 + row < d && col < kb) G[(R0 + row) * d + k0 + col] = acc[e];
+    for (int q = 0; q < 16; ++q)
+      if (16 * w + q < kb) p.Linv[(int64_t)(k0 + 16 * w + q) * d + k0 + lane] = r[q];
   }
+  const bool rows = R0 < d;
+  if (rows && w < 3) strip(BS, PX, G, d, R0, k0, kb, w, 0, 4, lane);
+  __syncthreads();   // the last strip's X rows (published by wave 3) are visible
+  if (rows) strip(BS, PX, G, d, R0, k0, kb, 3, w, w + 1, lane);
 }
 
 // Lower-triangular tile enumeration: L -> (row by, column bx <= by).
@@ -367,23 +429,66 @@ __global__ __launch_bounds__(256) void write_hd_kernel(float* __restrict__ H, in
   }
 }
 
+// Trailing-update work beside one panel (the schedule is in chol_sched.hpp).
+// Near job: a product C −= A·Aᵀ over a region whose top-left corner lies on
+// G's diagonal, cut into tile x tile output tiles on or below the diagonal
+// and numbered column by column.
+struct TileJob {
+  gemm_detail::KArgs g;
+  int count, nby, tile;
+  int dma;   // the shapes suit the DMA tile
+};
+// Far tasks: 128x128 tiles of G −= Lₛ·Lₛᵀ for super-panels s, one packed
+// (row tile, column tile, super-panel) word per workgroup.
+constexpr int kMaxFar = 512;
+struct FarJob {
+  gemm_detail::KArgs g;   // A = B = C = G, K = 128; A and B move to super-panel s
+  int count, dma;
+  uint32_t task[kMaxFar];
+};
+constexpr int kRing64 = 8;    // DMA ring depths: 64 KB for 64-tiles, 64 KB for 128-tiles
+constexpr int kRing128 = 4;
+static_assert(gemm_detail::DTile<64, kRing64>::SMEM <= gemm_detail::GEMM_SMEM_FLOATS * 4, "");
+static_assert(gemm_detail::DTile<128, kRing128>::SMEM <= gemm_detail::GEMM_SMEM_FLOATS * 4, "");
+
+template <int T>
+__device__ __forceinline__ void job_tile(const gemm_detail::KArgs& g, bool dma, int bx, int by,
+                                         float* smem) {
+  constexpr int NS = T == 64 ? kRing64 : kRing128;
+  if (dma)
+    gemm_detail::gemm_tile_dma<T, NS, false, true>(g, bx, by, 0, 1, reinterpret_cast<char*>(smem));
+  else
+    gemm_detail::gemm_tile<T, false, true>(g, bx, by, 0, 1, smem);
+}
+
+__device__ __forceinline__ void run_near_tile(const TileJob& j, int idx, float* smem) {
+  int bx = 0;
+  while (idx >= j.nby - bx) { idx -= j.nby - bx; ++bx; }
+  if (j.tile == 64) job_tile<64>(j.g, j.dma, bx, bx + idx, smem);
+  else job_tile<128>(j.g, j.dma, bx, bx + idx, smem);
+}
+
+__device__ __forceinline__ void run_far_tile(const FarJob& f, int idx, float* smem) {
+  const uint32_t w = f.task[idx];   // chol_sched::far_word layout
+  const int r = (int)(w & 1023u), t = (int)((w >> 10) & 1023u), sp = (int)((w >> 20) & 1023u);
+  gemm_detail::KArgs g = f.g;
+  g.A += (int64_t)sp * chol_sched::kSW;
+  g.B += (int64_t)sp * chol_sched::kSW;
+  job_tile<128>(g, f.dma, t, r, smem);
+}
+
 // One step of the blocked Cholesky: workgroups [0, nP) run panel k (its
 // columns first receive the previous panel's update), the rest run the
-// previous panel's trailing update of the columns beyond panel k,
-// G22 −= L21ₚ·L21ₚᵀ (lower tiles only, fp32 MFMA GEMM tiles).  The two sets
-// touch disjoint parts of G: the panel reads the previous panel's columns
-// and writes its own, the update writes only columns right of the panel.
-__global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP,
-                                                        gemm_detail::KArgs tr) {
-  __shared__ __attribute__((aligned(16))) float smem[gemm_detail::GEMM_SMEM_FLOATS];
+// near job's tiles and then the far tasks listed for this launch.  The
+// schedule guarantees that they all write disjoint parts of G and read
+// only finished panels.  A launch with nP = 0 runs far tasks only.
+__global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP, TileJob nj,
+                                                        FarJob fj) {
+  __shared__ __attribute__((aligned(1024))) float smem[gemm_detail::GEMM_SMEM_FLOATS];
   const int L = blockIdx.x;
-  if (L < nP) {
-    panel_body(p, L, smem);
-  } else {
-    int by, bx;
-    lower_tile(L - nP, by, bx);
-    gemm_detail::gemm_tile<128, false, true>(tr, bx, by, 0, 1, smem);
-  }
+  if (L < nP) panel_body(p, L, smem);
+  else if (L < nP + nj.count) run_near_tile(nj, L - nP, smem);
+  else run_far_tile(fj, L - nP - nj.count, smem);
 }
 
 // U[a][b] = Linv[d-1-a][d-1-b] for b >= a, 0 below the diagonal.
@@ -399,6 +504,40 @@ __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ 
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     p[i] = 0.f;
+}
+
+TileJob near_job(float* G, int64_t d, int64_t k) {
+  const chol_sched::NearRegion n = chol_sched::near_region(d, k);
+  TileJob j{};
+  if (n.c1 <= n.c0) return j;
+  GemmArgs h{};  // G[c0:, c0:c1] −= G[c0:, a0:a0+K] · G[c0:c1, a0:a0+K]ᵀ  (lower part)
+  h.M = (int)(d - n.c0); h.N = (int)(n.c1 - n.c0); h.K = n.K; h.k_last = n.K; h.batch = 1;
+  h.alpha = -1.f; h.beta = 1.f;
+  h.A = G + n.c0 * d + n.a0; h.lda = d; h.trans_a = false;
+  h.B = G + n.c0 * d + n.a0; h.ldb = d; h.trans_b = true;
+  h.C = G + n.c0 * d + n.c0; h.ldc = d; h.tri = 1;
+  j.g = gemm_detail::make_kargs(h);
+  j.dma = gemm_detail::dma_ok(j.g, false, true) ? 1 : 0;
+  j.tile = n.tile;
+  j.nby = (int)ceil_div(d - n.c0, n.tile);
+  const int nbx = (int)ceil_div(n.c1 - n.c0, n.tile);
+  j.count = nbx * j.nby - nbx * (nbx - 1) / 2;
+  return j;
+}
+
+FarJob far_base(float* G, int64_t d) {
+  FarJob f;
+  GemmArgs h{};  // tile (r, t): G[128r:, 128t:] −= G[128r:, 128s:+128] · G[128t:, 128s:+128]ᵀ
+  h.M = (int)d; h.N = (int)d; h.K = chol_sched::kSW; h.k_last = chol_sched::kSW; h.batch = 1;
+  h.alpha = -1.f; h.beta = 1.f;
+  h.A = G; h.lda = d; h.trans_a = false;
+  h.B = G; h.ldb = d; h.trans_b = true;
+  h.C = G; h.ldc = d; h.tri = 1;
+  f.g = gemm_detail::make_kargs(h);
+  // the per-task offsets of A and B (128 floats) keep the alignment
+  f.dma = gemm_detail::dma_ok(f.g, false, true) ? 1 : 0;
+  f.count = 0;
+  return f;
 }
 
 struct PrepWs {
@@ -448,27 +587,29 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   GQ_CHECK();
 
   // blocked right-looking Cholesky of G (lower), 64-wide panels, one launch
-  // per panel: the panel itself and, beside it, the previous panel's
-  // trailing update of the columns beyond it
-  for (int64_t k0 = 0; k0 < d; k0 += NB) {
+  // per panel, with the trailing updates in two levels
+  const std::vector<std::vector<uint32_t>> far = chol_sched::far_schedule(d);
+  FarJob fj = far_base(w.G, d);
+  for (int64_t k = 0; k * NB < d; ++k) {
+    const int64_t k0 = k * NB;
     const int kb = (int)std::min<int64_t>(NB, d - k0);
-    const int64_t r0 = k0 + kb, nr = d - r0;
+    const int64_t nr = d - (k0 + kb);
     const int nP = (int)std::max<int64_t>(1, ceil_div(nr, NB));
     PanelArgs pa{w.G, d, (int)k0, kb, w.Linv, w.status};
-    gemm_detail::KArgs tr{};
-    int64_t nT = 0;
-    if (k0 > 0 && nr > 0) {
-      GemmArgs h{};  // G[r0:, r0:] −= L21ₚ · L21ₚᵀ  (lower triangle)
-      h.M = (int)nr; h.N = (int)nr; h.K = NB; h.k_last = NB; h.batch = 1;
-      h.alpha = -1.f; h.beta = 1.f;
-      h.A = w.G + r0 * d + (k0 - NB); h.lda = d; h.trans_a = false;
-      h.B = w.G + r0 * d + (k0 - NB); h.ldb = d; h.trans_b = true;
-      h.C = w.G + r0 * d + r0; h.ldc = d; h.tri = 1;
-      tr = gemm_detail::make_kargs(h);
-      const int64_t nb = ceil_div(nr, 128);
-      nT = nb * (nb + 1) / 2;
+    const TileJob nj = near_job(w.G, d, k);
+    const std::vector<uint32_t>& ft = far[(size_t)k];
+    // far tasks beyond one launch's list run first, in launches of their own
+    size_t done = 0;
+    while (ft.size() - done > (size_t)kMaxFar) {
+      fj.count = kMaxFar;
+      std::copy(ft.begin() + (ptrdiff_t)done, ft.begin() + (ptrdiff_t)(done + kMaxFar), fj.task);
+      chol_step_kernel<<<(unsigned)kMaxFar, 256, 0, s>>>(pa, 0, TileJob{}, fj);
+      GQ_CHECK();
+      done += kMaxFar;
     }
-    chol_step_kernel<<<(unsigned)(nP + nT), 256, 0, s>>>(pa, nP, tr);
+    fj.count = (int)(ft.size() - done);
+    std::copy(ft.begin() + (ptrdiff_t)done, ft.end(), fj.task);
+    chol_step_kernel<<<(unsigned)(nP + nj.count + fj.count), 256, 0, s>>>(pa, nP, nj, fj);
     GQ_CHECK();
   }
 
