@@ -36,6 +36,30 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(KArgs g, int nx, int ny) 
   gemm_tile_dma<T, kRing<T>, TA, TB>(g, bx, by, blockIdx.z, gridDim.z, Sm);
 }
 
+// Rectangular products whose 128-tiles fill whole rounds of the chip but
+// one: the last round's tiles run as four 64-tiles each (same launch, after
+// the 128-tiles), so that round takes about a quarter of a 128-tile's time
+// instead of a full one.  WG L < full: 128-tile L in row-major order; then
+// the remaining 128-tile positions, four 64-tile workgroups each.
+constexpr int kMixRing64 = 8;
+constexpr int kMixSmem = DTile<128, 4>::SMEM > DTile<64, kMixRing64>::SMEM
+                             ? DTile<128, 4>::SMEM : DTile<64, kMixRing64>::SMEM;
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_mixed_kernel(KArgs g, int nx, int full) {
+  __shared__ __attribute__((aligned(1024))) char Sm[kMixSmem];
+  const int L = blockIdx.x;
+  if (L < full) {
+    gemm_tile_dma<128, 4, TA, TB>(g, L % nx, L / nx, 0, 1, Sm);
+  } else {
+    const int j = L - full, q = full + j / 4, sub = j & 3;
+    gemm_tile_dma<64, kMixRing64, TA, TB>(g, 2 * (q % nx) + (sub & 1), 2 * (q / nx) + (sub >> 1),
+                                          0, 1, Sm);
+  }
+}
+
+// 128-tile workgroups resident at once (two per CU)
+constexpr int64_t kSlots128 = 2 * 256;
+
 template <int T>
 void launch(const KArgs& k, const GemmArgs& a, hipStream_t s) {
   const int nx = (int)ceil_div(a.N, T), ny = (int)ceil_div(a.M, T);
@@ -83,7 +107,19 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
   // or the K loop is long (the triangular products' tiles then differ a lot
   // in length, and small tiles spread the long ones over more CUs)
   const int64_t tiles128 = ceil_div(a.M, 128) * ceil_div(a.N, 128) * a.batch;
-  const bool small = tiles128 < 512 || ((a.k_from_n || a.k_to_m) && a.K >= 1024);
+  const bool rect = a.batch == 1 && !a.k_from_n && !a.k_to_m && a.tri == 0;
+  if (rect && tiles128 > kSlots128 && tiles128 % kSlots128 != 0 &&
+      dma_ok(k, a.trans_a, a.trans_b)) {
+    const int nx = (int)ceil_div(a.N, 128);
+    const int64_t full = tiles128 / kSlots128 * kSlots128;
+    const unsigned grid = (unsigned)(full + 4 * (tiles128 - full));
+    if (!a.trans_a && !a.trans_b) gemm_mixed_kernel<false, false><<<grid, 256, 0, s>>>(k, nx, (int)full);
+    else if (!a.trans_a && a.trans_b) gemm_mixed_kernel<false, true><<<grid, 256, 0, s>>>(k, nx, (int)full);
+    else if (a.trans_a && !a.trans_b) gemm_mixed_kernel<true, false><<<grid, 256, 0, s>>>(k, nx, (int)full);
+    else gemm_mixed_kernel<true, true><<<grid, 256, 0, s>>>(k, nx, (int)full);
+    return hipGetLastError();
+  }
+  const bool small = tiles128 < kSlots128 || ((a.k_from_n || a.k_to_m) && a.K >= 1024);
   if (small) launch<64>(k, a, s);
   else launch<128>(k, a, s);
   return hipGetLastError();

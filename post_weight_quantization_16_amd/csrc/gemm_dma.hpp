@@ -153,6 +153,7 @@ __device__ __forceinline__ void gemm_tile_dma(const KArgs& g, int bx, int by, in
   constexpr int FI = T / 64, WT = T / 2, NW = DT::NW;
   constexpr bool KA = !TA, KB = TB;   // k-contiguous operands
   const int m0 = by * T, n0 = bx * T;
+  if (m0 >= g.M || n0 >= g.N) return;   // a sub-tile wholly past the edge
   if (g.tri == 1 && n0 > m0 + T - 1) return;
   if (g.tri == 2 && n0 + T - 1 < m0) return;
   const int Kz = (z == nz - 1) ? g.k_last : g.K;
@@ -186,6 +187,12 @@ __device__ __forceinline__ void gemm_tile_dma(const KArgs& g, int bx, int by, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // C's share of a vector-epilogue tile is read first: it arrives with the
+  // first stage instead of after the K loop (loads complete in issue order,
+  // so the stage waits below cover it)
+  f32x4 cv[T * T / 1024];
+  const bool early_c = g.beta != 0.f && c_vec<T>(g, m0, n0);
+  if (early_c) load_c<T>(g, C, m0, n0, t, cv);
   for (int s0 = 0; s0 < NS - 1 && s0 < nst; ++s0) copy(s0);
   wait_stages<NW>(min(nst - 1, NS - 2));
   __syncthreads();
@@ -222,7 +229,7 @@ __device__ __forceinline__ void gemm_tile_dma(const KArgs& g, int bx, int by, in
         E[row * DT::ES + col] = g.alpha * acc[i][j][r];
       }
   __syncthreads();
-  store_tile<T, DT::ES>(g, E, C, m0, n0, t);
+  store_tile<T, DT::ES>(g, E, C, m0, n0, t, cv, early_c);
 }
 
 }  // namespace gemm_detail

@@ -112,27 +112,39 @@ __device__ __forceinline__ float opread(const float* s, int a, int k) {
   return ALONG ? s[k * Tile<T>::SA + a] : s[a * Tile<T>::SK + k];
 }
 
+// Whether the tile (m0, n0) takes the vector epilogue (in range, float4 C).
+template <int T>
+__device__ __forceinline__ bool c_vec(const KArgs& g, int m0, int n0) {
+  return g.M - m0 >= T && g.N - n0 >= T && g.vec_c;
+}
+// This thread's float4 share of a vector-epilogue tile of C (issued early by
+// callers that can hide the read).
+template <int T>
+__device__ __forceinline__ void load_c(const KArgs& g, const float* C, int m0, int n0, int t,
+                                       f32x4 (&cv)[T * T / 1024]) {
+#pragma unroll
+  for (int u = 0; u < T * T / 1024; ++u) {
+    const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
+    cv[u] = *reinterpret_cast<const f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4);
+  }
+}
+
 // C[m0.., n0..] = E + beta·C for one T x T tile staged in LDS (row stride
 // ES), honouring the edges and the triangle mask (tri 1: lower, 2: upper).
 // All of a thread's C reads are issued before any of its writes: C is read
 // and written through one pointer, so a read placed after a write would
 // wait for that write's full round trip.  In-range tiles move float4 (a
-// float4 straddling the diagonal is written element by element).
+// float4 straddling the diagonal is written element by element); their C
+// values come in cv when the caller loaded them already (have_c).
 template <int T, int ES>
 __device__ __forceinline__ void store_tile(const KArgs& g, const float* E, float* C, int m0,
-                                           int n0, int t) {
+                                           int n0, int t, f32x4 (&cv)[T * T / 1024],
+                                           bool have_c) {
   const bool has_beta = g.beta != 0.f;
   const int mvalid = g.M - m0, nvalid = g.N - n0;
-  if (mvalid >= T && nvalid >= T && g.vec_c) {
+  if (c_vec<T>(g, m0, n0)) {
     constexpr int NE = T * T / 1024;
-    f32x4 cv[NE];
-    if (has_beta) {
-#pragma unroll
-      for (int u = 0; u < NE; ++u) {
-        const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
-        cv[u] = *reinterpret_cast<const f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4);
-      }
-    }
+    if (has_beta && !have_c) load_c<T>(g, C, m0, n0, t, cv);
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
       const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
@@ -266,7 +278,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, int bx, int by, int z,
         E[row * TL::ES + col] = g.alpha * acc[i][j][r];
       }
   __syncthreads();
-  store_tile<T, TL::ES>(g, E, C, m0, n0, t);
+  f32x4 cv[T * T / 1024];
+  store_tile<T, TL::ES>(g, E, C, m0, n0, t, cv, false);
 }
 
 // Kernel arguments for a host-side GemmArgs (vector-load eligibility included).

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void build_g_kernel(const float* __restrict__ 
 struct PanelArgs {
   float* G; int64_t d; int k0, kb;
   float* Linv; int* status;
+  int np;   // panel workgroups in the launch
 };
 
 constexpr int LS = NB + 2;       // LDS row stride: the half-waves' MFMA reads hit disjoint banks
@@ -354,36 +355,24 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     }
     PL[j * NB + lane] = l;
     PX[j * PXS + lane] = x;
-    if (q0 + 2 < 16) {
-      // l_kj of the remaining columns, read back from the row just
-      // published (this wave's own writes, in order)
-      f32x4 cv[4];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __hip_atomic_store(&flag[j], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-      for (int h = (q0 + 2) >> 2; h < 4; ++h)
-        cv[h] = *reinterpret_cast<const f32x4*>(PL + j * NB + 16 * w + 4 * h);
-#pragma unroll
-      for (int q = q0 + 2; q < 16; ++q) {
-        const float c = cv[q >> 2][q & 3];
-        a[q] = fmaf(-l, c, a[q]);
-        r[q] = fmaf(-c, x, r[q]);
-      }
+    for (int q = q0 + 2; q < 16; ++q) {
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 16 * w + q));
+      a[q] = fmaf(-l, c, a[q]);
+      r[q] = fmaf(-c, x, r[q]);
     }
-    // the flag goes up after the step's updates: its release then finds
-    // the published writes long done
-    __builtin_amdgcn_sched_barrier(0);
-    __hip_atomic_store(&flag[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
-  // X rows 16w..16w+15 are final: workgroup 0 stores them to Linv
-  if (b == 0 && lane < kb) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (16 * w + q < kb) p.Linv[(int64_t)(k0 + 16 * w + q) * d + k0 + lane] = r[q];
-  }
   const bool rows = R0 < d;
   if (rows && w < 3) strip(BS, PX, G, d, R0, k0, kb, w, 0, 4, lane);
   __syncthreads();   // the last strip's X rows (published by wave 3) are visible
   if (rows) strip(BS, PX, G, d, R0, k0, kb, 3, w, w + 1, lane);
+  // X = L11⁻¹ to Linv's diagonal block, its rows spread over the panel's
+  // workgroups and waves (row j by workgroup j % np)
+  for (int jr = b + p.np * w; jr < kb; jr += 4 * p.np)
+    if (lane < kb) p.Linv[(int64_t)(k0 + jr) * d + k0 + lane] = PX[jr * PXS + lane];
 }
 
 // Lower-triangular tile enumeration: L -> (row by, column bx <= by).
@@ -595,7 +584,7 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     const int kb = (int)std::min<int64_t>(NB, d - k0);
     const int64_t nr = d - (k0 + kb);
     const int nP = (int)std::max<int64_t>(1, ceil_div(nr, NB));
-    PanelArgs pa{w.G, d, (int)k0, kb, w.Linv, w.status};
+    PanelArgs pa{w.G, d, (int)k0, kb, w.Linv, w.status, nP};
     const TileJob nj = near_job(w.G, d, k);
     const std::vector<uint32_t>& ft = far[(size_t)k];
     // far tasks beyond one launch's list run first, in launches of their own

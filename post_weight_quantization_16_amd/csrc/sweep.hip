@@ -78,28 +78,43 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   // per wave: err [4][SROW] fp32 and codes [4][QROW] u8 of the block's columns
   __shared__ __attribute__((aligned(16))) char stage[4][4 * SROW * 4 + 4 * QROW];
   const int nthr = blockDim.x, t = threadIdx.x;
-  {
-    const bool vec = (((uintptr_t)a.Ublk) % 16 == 0) && (a.ldu % 4 == 0);
-    for (int e = t * 4; e < kBlock * kBlock; e += nthr * 4) {
-      const int i = e / kBlock, j = e % kBlock;
-      f32x4 v;
-      if (vec) {
-        v = *reinterpret_cast<const f32x4*>(a.Ublk + (int64_t)i * a.ldu + j);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = a.Ublk[(int64_t)i * a.ldu + j + q];
-      }
-      *reinterpret_cast<f32x4*>(&Us[e]) = v;
-    }
-  }
-  __syncthreads();
-  for (int j = t; j < kBlock; j += nthr) rud[j] = 1.f / Us[j * kBlock + j];
-  __syncthreads();
-
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int c = lane & 15, rloc = lane >> 4;          // lane within the row, row in the wave
   const int64_t r = ((int64_t)blockIdx.x * (nthr >> 6) + wave) * 4 + (lane >> 4);
   const bool live = r < a.m;
+  // Stage the block's U (64 KB) in LDS.  With 16-byte aligned rows it goes
+  // from memory straight into LDS (global_load_lds_dwordx4, 1 KB = two U
+  // rows per instruction, every copy in flight at once); otherwise all of a
+  // thread's loads are issued before its stores.  The weights are loaded
+  // meanwhile.
+  const bool vec = (((uintptr_t)a.Ublk) % 16 == 0) && (a.ldu % 4 == 0);
+  if (vec) {
+    const unsigned sbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)Us;
+    for (int seg = wave; seg < kBlock * kBlock / 256; seg += nthr >> 6) {
+      const int e = seg * 256 + lane * 4, i = e / kBlock, j = e % kBlock;
+      const float* src = a.Ublk + (int64_t)i * a.ldu + j;
+      // 16 bytes per lane to LDS M0 + 16·lane; no register result, waited
+      // for by the vmcnt wait below
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(sbase + (unsigned)seg * 1024u), "v"(src) : "memory");
+    }
+  } else {
+    for (int e0 = t * 4; e0 < kBlock * kBlock; e0 += nthr * 4 * 16) {
+      f32x4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = e0 + u * nthr * 4, i = e / kBlock, j = e % kBlock;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[u][q] = e < kBlock * kBlock ? a.Ublk[(int64_t)i * a.ldu + j + q] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = e0 + u * nthr * 4;
+        if (e < kBlock * kBlock) *reinterpret_cast<f32x4*>(&Us[e]) = v[u];
+      }
+    }
+  }
   // slot sl < 4: column 4c+sl; slot sl >= 4: column 64+4c+sl-4
   float w[QC];
   float* SE = reinterpret_cast<float*>(stage[wave]);
@@ -113,6 +128,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       w[q] = lo[q]; w[4 + q] = hi[q];
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): U copies and weights have landed
+  __syncthreads();
+  for (int j = t; j < kBlock; j += nthr) rud[j] = 1.f / Us[j * kBlock + j];
+  __syncthreads();
 
   float s = 1.f, z = 0.f, rs = 1.f;
   if (G == 0) {
