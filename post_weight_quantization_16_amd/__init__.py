@@ -59,6 +59,7 @@ class Prepared:
     U: "object"        # [d, d] fp32 upper factor of H_d⁻¹ (quantization order)
     perm: "object"     # [d] int32 quantization order
     dead: "object"     # [d] uint8 dead-channel mask (original order)
+    natural: bool = False   # perm is the identity (prepared without act-order)
 
 
 @dataclasses.dataclass
@@ -149,7 +150,7 @@ def prepare_hinv(H, params: GPTQParams, ws=None) -> Prepared:
     if rc == _native.ERR_NOT_SPD:
         raise NotPositiveDefinite(rc, _native.last_error(), info.value)
     _check(rc)
-    return Prepared(U, perm, dead)
+    return Prepared(U, perm, dead, natural=not params.act_order)
 
 
 def quantize_layer(W, prep: Prepared, params: GPTQParams, want_what: bool = True,
@@ -173,7 +174,8 @@ def quantize_layer(W, prep: Prepared, params: GPTQParams, want_what: bool = True
     if ws is None:
         ws = _workspace(L.gptq_workspace_bytes(_native.WS_QUANTIZE, m, d, 0, ctypes.byref(p)), dev)
     _check(L.gptq_quantize_layer(
-        _dev(W, "W"), _dtype_code(W), m, d, W.stride(0), _dev(prep.U, "U"), _dev(prep.perm, "perm"),
+        _dev(W, "W"), _dtype_code(W), m, d, W.stride(0), _dev(prep.U, "U"),
+        None if prep.natural else _dev(prep.perm, "perm"),
         _dev(prep.dead, "dead"), ctypes.byref(p), _dev(qweight, "qweight"), _dev(scales, "scales"),
         _dev(zeros, "zeros"), _dev(W_hat, "W_hat"), _dev(g_idx, "g_idx"), _dev(row_loss, "row_loss"),
         _dev(ws, "ws"), ws.numel(), _stream(dev)))

@@ -60,11 +60,17 @@ __global__ __launch_bounds__(1024) void diag_kernel(float* __restrict__ H, int64
 }
 
 // Rank sort: position of i = #{j : key_j > key_i or (key_j == key_i and j < i)}.
+// The order is written to the workspace and, when given, to the caller's
+// perm_out as well (no separate copy).
 __global__ __launch_bounds__(256) void rank_kernel(const float* __restrict__ diag, int d,
-                                                   int act_order, int* __restrict__ perm) {
+                                                   int act_order, int* __restrict__ perm,
+                                                   int* __restrict__ perm_out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (!act_order) {
-    if (i < d) perm[i] = i;
+    if (i < d) {
+      perm[i] = i;
+      if (perm_out) perm_out[i] = i;
+    }
     return;
   }
   __shared__ float kj[256];
@@ -84,21 +90,54 @@ __global__ __launch_bounds__(256) void rank_kernel(const float* __restrict__ dia
       rank += (v2 > ki) || (v2 == ki && j0 + k < i);
     }
   }
-  if (i < d) perm[rank] = i;
+  if (i < d) {
+    perm[rank] = i;
+    if (perm_out) perm_out[rank] = i;
+  }
 }
 
-// G[a][b] = H[π(d-1-a)][π(d-1-b)] + λ·[a == b]   (reversed, permuted, damped)
+// G[a][b] = H[π(d−1−a)][π(d−1−b)] + λ·[a == b]: the damped, permuted and
+// index-reversed Hessian.  Each thread writes 4 consecutive columns of one
+// row (one float4 when d is a multiple of 4); its 4 source indices are
+// loaded together, then its 4 sources.
 __global__ __launch_bounds__(256) void build_g_kernel(const float* __restrict__ H, int64_t d,
                                                       const int* __restrict__ perm,
                                                       const float* __restrict__ lam,
-                                                      float* __restrict__ G) {
+                                                      float* __restrict__ G, int ident) {
   const float l = lam[0];
-  for (int64_t a = blockIdx.y; a < d; a += gridDim.y) {
-    const int pa = perm[d - 1 - a];
-    for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < d; b += (int64_t)gridDim.x * 256) {
-      float v = H[(int64_t)pa * d + perm[d - 1 - b]];
-      if (a == b) v += l;
-      G[a * d + b] = v;
+  const bool vec = (d & 3) == 0;
+  if (ident && vec) {   // π = identity: row d−1−a of H read backwards, a float4 at a time
+    for (int64_t b0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; b0 < d;
+         b0 += (int64_t)gridDim.x * 1024)
+      for (int64_t a = blockIdx.y; a < d; a += gridDim.y) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(H + (d - 1 - a) * d + d - 4 - b0);
+        f32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = v[3 - q] + ((a == b0 + q) ? l : 0.f);
+        *reinterpret_cast<f32x4*>(G + a * d + b0) = o;
+      }
+    return;
+  }
+  for (int64_t b0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; b0 < d;
+       b0 += (int64_t)gridDim.x * 1024) {
+    int pb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pb[q] = b0 + q < d ? perm[d - 1 - b0 - q] : 0;
+    for (int64_t a = blockIdx.y; a < d; a += gridDim.y) {
+      const float* hr = H + (int64_t)perm[d - 1 - a] * d;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = b0 + q < d ? hr[pb[q]] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] += (a == b0 + q) ? l : 0.f;
+      if (vec) {
+        const f32x4 o = {v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(G + a * d + b0) = o;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (b0 + q < d) G[a * d + b0 + q] = v[q];
+      }
     }
   }
 }
@@ -480,12 +519,30 @@ __global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP, Til
   else run_far_tile(fj, L - nP - nj.count, smem);
 }
 
-// U[a][b] = Linv[d-1-a][d-1-b] for b >= a, 0 below the diagonal.
+// U[a][b] = Linv[d-1-a][d-1-b] for b >= a, 0 below the diagonal; four
+// columns per thread (one reversed float4 of Linv when d is a multiple of 4).
 __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ Linv, int64_t d,
                                                       float* __restrict__ U) {
-  for (int64_t a = blockIdx.y; a < d; a += gridDim.y)
-    for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < d; b += (int64_t)gridDim.x * 256)
-      U[a * d + b] = (b >= a) ? Linv[(d - 1 - a) * d + (d - 1 - b)] : 0.f;
+  const bool vec = (d & 3) == 0;
+  for (int64_t a = blockIdx.y; a < d; a += gridDim.y) {
+    const float* lr = Linv + (d - 1 - a) * d;
+    for (int64_t b0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; b0 < d;
+         b0 += (int64_t)gridDim.x * 1024) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      if (vec) {
+        if (b0 + 3 >= a) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(lr + d - 4 - b0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = b0 + q >= a ? v[3 - q] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(U + a * d + b0) = o;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (b0 + q < d) U[a * d + b0 + q] = b0 + q >= a ? lr[d - 1 - b0 - q] : 0.f;
+      }
+    }
+  }
 }
 
 // Linv starts as zeros: the doubling products read whole diagonal blocks,
@@ -566,11 +623,12 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   } while (0)
   diag_kernel<<<1, 1024, 0, s>>>(H, d, dead_mask, w.diag, percdamp, w.lam, w.status);
   GQ_CHECK();
-  rank_kernel<<<(unsigned)ceil_div(d, 256), 256, 0, s>>>(w.diag, (int)d, act_order, w.perm);
+  rank_kernel<<<(unsigned)ceil_div(d, 256), 256, 0, s>>>(w.diag, (int)d, act_order, w.perm,
+                                                          perm_out);
   GQ_CHECK();
-  const unsigned gx = (unsigned)std::min<int64_t>(ceil_div(d, 256), 16);
   const unsigned gy = (unsigned)std::min<int64_t>(d, 65535);
-  build_g_kernel<<<dim3(gx, gy), 256, 0, s>>>(H, d, w.perm, w.lam, w.G);
+  build_g_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(H, d, w.perm, w.lam, w.G,
+                                                                      act_order ? 0 : 1);
   GQ_CHECK();
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();
@@ -632,7 +690,7 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     }
   }
 
-  write_u_kernel<<<dim3(gx, gy), 256, 0, s>>>(w.Linv, d, U);
+  write_u_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(w.Linv, d, U);
   GQ_CHECK();
   {
     const int64_t nb64 = ceil_div(d, 64);
@@ -640,10 +698,6 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
                                                                       w.lam);
   }
   GQ_CHECK();
-  if (perm_out) {
-    e = hipMemcpyAsync(perm_out, w.perm, (size_t)d * 4, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return e;
-  }
 #undef GQ_CHECK
   return hipSuccess;
 }

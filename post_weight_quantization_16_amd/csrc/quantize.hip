@@ -53,32 +53,88 @@ __device__ __forceinline__ float load_w(const void* W, int dt, int64_t i) {
 }
 
 // Wk[r][a] = W[r][π(a)] (0 for dead channels and padding a >= d);
-// inv[π(a)] = a; row_loss = 0.  Each thread writes 4 consecutive columns
-// (one float4: dp is a multiple of 128).
+// inv[π(a)] = a; row_loss = 0.  Each thread writes 8 consecutive working
+// columns (two float4: dp is a multiple of 128), every load issued before
+// the stores; without a permutation (perm null) the row is read
+// contiguously (vec_in: 16-byte loads are aligned).
 __global__ __launch_bounds__(256) void init_kernel(const void* __restrict__ W, int dt, int64_t ld_w,
                                                    int64_t m, int64_t d, int64_t dp,
                                                    const int* __restrict__ perm,
                                                    const uint8_t* __restrict__ dead,
                                                    float* __restrict__ Wk, int* __restrict__ inv,
-                                                   float* __restrict__ row_loss) {
-  const int64_t a0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
-    if (row_loss && blockIdx.x == 0 && threadIdx.x == 0) row_loss[r] = 0.f;
-    if (a0 >= dp) continue;
-    f32x4 v;
+                                                   float* __restrict__ row_loss, int vec_in) {
+  const int64_t a0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  int c[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t a = a0 + q;
-      float x = 0.f;
-      if (a < d) {
-        const int c = perm ? perm[a] : (int)a;
-        x = load_w(W, dt, r * ld_w + c);
-        if (dead && dead[c]) x = 0.f;
-        if (r == 0) inv[c] = (int)a;
-      }
-      v[q] = x;
+  for (int q = 0; q < 8; ++q) c[q] = (int)(a0 + q);
+  if (perm && a0 < d) {
+    if (a0 + 7 < d && ((uintptr_t)perm & 15) == 0) {
+      const int4 p0 = *reinterpret_cast<const int4*>(perm + a0);
+      const int4 p1 = *reinterpret_cast<const int4*>(perm + a0 + 4);
+      c[0] = p0.x; c[1] = p0.y; c[2] = p0.z; c[3] = p0.w;
+      c[4] = p1.x; c[5] = p1.y; c[6] = p1.z; c[7] = p1.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) c[q] = a0 + q < d ? perm[a0 + q] : 0;
     }
-    *reinterpret_cast<f32x4*>(Wk + r * dp + a0) = v;
+  }
+  bool dz[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dz[q] = a0 + q >= d || (dead && dead[c[q]]);
+  // rows blockIdx.y·RB .. +RB−1 per step of the grid: every row's loads
+  // are issued before the first store
+  constexpr int RB = 4;
+  for (int64_t r0 = (int64_t)blockIdx.y * RB; r0 < m; r0 += (int64_t)gridDim.y * RB) {
+    if (a0 >= dp) {
+      if (row_loss && threadIdx.x == 0 && blockIdx.x == 0)
+        for (int64_t r = r0; r < r0 + RB && r < m; ++r) row_loss[r] = 0.f;
+      continue;
+    }
+    float xs[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int64_t r = r0 + rb < m ? r0 + rb : r0;
+      float* x = xs[rb];
+      const bool contig = !perm && vec_in && a0 + 7 < d;
+      if (contig && dt == GPTQ_F32) {
+        const float* src = static_cast<const float*>(W) + r * ld_w + a0;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { x[q] = lo[q]; x[4 + q] = hi[q]; }
+      } else if (contig) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + r * ld_w + a0);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint16_t h = (uint16_t)(wd[q >> 1] >> (16 * (q & 1)));
+          x[q] = dt == GPTQ_BF16 ? __uint_as_float((uint32_t)h << 16)
+                                 : (float)__builtin_bit_cast(_Float16, h);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = a0 + q < d ? load_w(W, dt, r * ld_w + c[q]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int64_t r = r0 + rb;
+      if (r >= m) break;
+      if (row_loss && blockIdx.x == 0 && threadIdx.x == 0) row_loss[r] = 0.f;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo[q] = dz[q] ? 0.f : xs[rb][q];
+        hi[q] = dz[4 + q] ? 0.f : xs[rb][4 + q];
+      }
+      *reinterpret_cast<f32x4*>(Wk + r * dp + a0) = lo;
+      *reinterpret_cast<f32x4*>(Wk + r * dp + a0 + 4) = hi;
+      if (r == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (a0 + q < d) inv[c[q]] = (int)(a0 + q);
+      }
+    }
   }
 }
 
@@ -123,53 +179,93 @@ __global__ __launch_bounds__(256) void pad_u_kernel(const float* __restrict__ U,
   }
 }
 
-// Write Ŵ / g_idx and pack the codes, in the original column order.  The
-// first loop gives each thread 4 consecutive output columns of Ŵ (gathered
-// through inv, which is contiguous without act-order); the second gives
-// each thread one packed word.
+// Outputs in the original column order: Ŵ[r][c] = Wk[r][inv[c]], codes
+// packed little-end first (8 per 32-bit word up to 4 bits, else 4), g_idx
+// (row 0).  Each thread handles 8 consecutive output columns, every load
+// issued before the stores; without a permutation (ident) the working row
+// is read contiguously.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ Wk,
                                                        const uint8_t* __restrict__ codes,
                                                        const int* __restrict__ inv, int64_t m,
                                                        int64_t d, int64_t dp, int bits, int64_t g,
                                                        uint32_t* __restrict__ qweight,
                                                        float* __restrict__ W_hat,
-                                                       int32_t* __restrict__ g_idx, int vec_w) {
+                                                       int32_t* __restrict__ g_idx, int vec_w,
+                                                       int ident) {
   const int cpw = bits <= 4 ? 8 : 4, cwid = 32 / cpw;
   const int64_t nw = (d + cpw - 1) / cpw;
-  const int64_t lin = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c0 >= d) return;
+  const bool full = c0 + 7 < d;
+  int a[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) a[q] = (int)(c0 + q);
+  if (!ident) {
+    if (full) {   // inv sits 256-byte aligned in the workspace
+      const int4 p0 = *reinterpret_cast<const int4*>(inv + c0);
+      const int4 p1 = *reinterpret_cast<const int4*>(inv + c0 + 4);
+      a[0] = p0.x; a[1] = p0.y; a[2] = p0.z; a[3] = p0.w;
+      a[4] = p1.x; a[5] = p1.y; a[6] = p1.z; a[7] = p1.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[q] = c0 + q < d ? inv[c0 + q] : 0;
+    }
+  }
+  if (g_idx && blockIdx.y == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (c0 + q < d) g_idx[c0 + q] = (int32_t)(a[q] / g);
+  }
   for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
-    const int64_t c0 = lin * 4;
-    if ((W_hat || (g_idx && r == 0)) && c0 < d) {
-      float v[4];
+    float v[8];
+    uint32_t cd[8];
+    const float* wr = Wk + r * dp;
+    const uint8_t* qr = codes + r * dp;
+    if (ident && full) {   // dp is a multiple of 128: these loads are aligned
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(wr + c0);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(wr + c0 + 4);
+      const uint2 qq = *reinterpret_cast<const uint2*>(qr + c0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t c = c0 + q;
-        v[q] = 0.f;
-        if (c < d) {
-          const int a = inv[c];
-          v[q] = Wk[r * dp + a];
-          if (g_idx && r == 0) g_idx[c] = (int32_t)(a / g);
-        }
+        v[q] = lo[q]; v[4 + q] = hi[q];
+        cd[q] = (qq.x >> (8 * q)) & 255u;
+        cd[4 + q] = (qq.y >> (8 * q)) & 255u;
       }
-      if (W_hat) {
-        if (vec_w && c0 + 3 < d) {
-          const f32x4 o = {v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4*>(W_hat + r * d + c0) = o;
-        } else {
+    } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (c0 + q < d) W_hat[r * d + c0 + q] = v[q];
-        }
+      for (int q = 0; q < 8; ++q) {
+        const bool in = c0 + q < d;
+        v[q] = in ? wr[a[q]] : 0.f;
+        cd[q] = in ? qr[a[q]] : 0u;
       }
     }
-    for (int64_t k = lin; k < nw; k += (int64_t)gridDim.x * 256) {
-      uint32_t word = 0;
-      for (int i = 0; i < cpw; ++i) {
-        const int64_t c = k * cpw + i;
-        if (c >= d) break;
-        word |= (uint32_t)codes[r * dp + inv[c]] << (cwid * i);
+    if (W_hat) {
+      float* dst = W_hat + r * d + c0;
+      if (vec_w && full) {
+        const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<f32x4*>(dst) = lo;
+        *reinterpret_cast<f32x4*>(dst + 4) = hi;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (c0 + q < d) dst[q] = v[q];
       }
-      qweight[r * nw + k] = word;
+    }
+    // 8 columns = one word (cpw 8) or two (cpw 4); columns past d pack as 0
+    if (cpw == 8) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) word |= cd[q] << (cwid * q);
+      qweight[r * nw + c0 / 8] = word;
+    } else {
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w0 |= cd[q] << (cwid * q);
+        w1 |= cd[4 + q] << (cwid * q);
+      }
+      qweight[r * nw + c0 / 4] = w0;
+      if (c0 + 4 < d) qweight[r * nw + c0 / 4 + 1] = w1;
     }
   }
 }
@@ -253,9 +349,12 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
   const int ng = (int)ceil_div(d, g);
   const unsigned gy = (unsigned)std::min<int64_t>(m, 65535);
   const int64_t dp = ceil_div(d, kBlock) * kBlock;
-  init_kernel<<<dim3((unsigned)ceil_div(dp, 1024), gy), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp,
+  const int esz = w_dtype == GPTQ_F32 ? 4 : 2;
+  const int vec_in = ((uintptr_t)W % 16 == 0) && ((ld_w * esz) % 16 == 0);
+  const unsigned gy4 = (unsigned)std::min<int64_t>(ceil_div(m, 4), 65535);
+  init_kernel<<<dim3((unsigned)ceil_div(dp, 2048), gy4), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp,
                                                                     perm, dead, w.Wk, w.inv,
-                                                                    row_loss);
+                                                                    row_loss, vec_in);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g) {
@@ -266,8 +365,8 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
   }
   if (e != hipSuccess) return e;
   const int vec_w = W_hat && ((uintptr_t)W_hat % 16 == 0) && (d % 4 == 0);
-  finalize_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(
-      w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight, W_hat, g_idx, vec_w);
+  finalize_kernel<<<dim3((unsigned)ceil_div(d, 2048), gy), 256, 0, s>>>(
+      w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight, W_hat, g_idx, vec_w, perm ? 0 : 1);
   return hipGetLastError();
 }
 
