@@ -120,25 +120,26 @@ struct OpCopy {
   }
 };
 
-// The 8 values of rows (or columns) base + i·32 + lane%32, i < FI, for this
-// lane's k half, from one operand's stage buffer.
+// Four of a lane's 8 k values (half hf: k = 8·(lane/32) + 4·hf + 0..3) of
+// rows (or columns) base + i·32 + lane%32, i < FI, from one operand's stage
+// buffer.
 template <int T, bool KCONT, int FI>
-__device__ __forceinline__ void read_op(const char* S, int base, int lane, float (&v)[FI][8]) {
+__device__ __forceinline__ void read_half(const char* S, int base, int lane, int hf,
+                                          float (&v)[FI][4]) {
   const int h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int r = base + i * 32 + (lane & 31);
     if (KCONT) {
       const int sw = (r >> 2) & 3;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(S + r * 64 + (((2 * h) ^ sw) << 4));
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(S + r * 64 + (((2 * h + 1) ^ sw) << 4));
+      const f32x4 x = *reinterpret_cast<const f32x4*>(S + r * 64 + (((2 * h + hf) ^ sw) << 4));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { v[i][q] = lo[q]; v[i][4 + q] = hi[q]; }
+      for (int q = 0; q < 4; ++q) v[i][q] = x[q];
     } else {
       const int off = ((((r >> 2) ^ (8 * h)) << 4)) + ((r & 3) << 2);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        v[i][kk] = *reinterpret_cast<const float*>(S + (8 * h + kk) * (T * 4) + off);
+      for (int kk = 0; kk < 4; ++kk)
+        v[i][kk] = *reinterpret_cast<const float*>(S + (8 * h + 4 * hf + kk) * (T * 4) + off);
     }
   }
 }
@@ -196,24 +197,39 @@ __device__ __forceinline__ void gemm_tile_dma(const KArgs& g, int bx, int by, in
   for (int s0 = 0; s0 < NS - 1 && s0 < nst; ++s0) copy(s0);
   wait_stages<NW>(min(nst - 1, NS - 2));
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + NS - 1 < nst) copy(st + NS - 1);   // into the buffer the last barrier freed
-    const char* SA = Sm + (st % NS) * DT::SB;
-    const char* SB = SA + DT::OPB;
-    float av[FI][8], bv[FI][8];
-    read_op<T, KA, FI>(SA, wm * WT, lane, av);
-    read_op<T, KB, FI>(SB, wn * WT, lane, bv);
+  // Each stage is two halves of 4 k: the second half of stage st is
+  // multiplied after the barrier, while the first half of stage st+1 is
+  // read, so the MFMAs do not start each stage waiting for LDS.
+  float al[FI][4], bl[FI][4], ah[FI][4], bh[FI][4];
+  auto mfma4 = [&](const float (&av)[FI][4], const float (&bv)[FI][4]) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][kk], bv[j][kk], acc[i][j], 0, 0, 0);
+  };
+  if (nst > 0) {
+    read_half<T, KA, FI>(Sm, wm * WT, lane, 0, al);
+    read_half<T, KB, FI>(Sm + DT::OPB, wn * WT, lane, 0, bl);
+  }
+  for (int st = 0; st < nst; ++st) {
+    if (st + NS - 1 < nst) copy(st + NS - 1);   // into the buffer the last barrier freed
+    const char* SA = Sm + (st % NS) * DT::SB;
+    read_half<T, KA, FI>(SA, wm * WT, lane, 1, ah);
+    read_half<T, KB, FI>(SA + DT::OPB, wn * WT, lane, 1, bh);
+    mfma4(al, bl);
     // stage st+1 copied (later stages may stay in flight) and this wave's
     // reads of stage st done before the barrier frees its buffer
     wait_stages<NW>(min(nst - 1, st + NS - 1) - (st + 1));
     __syncthreads();
+    if (st + 1 < nst) {
+      const char* SN = Sm + ((st + 1) % NS) * DT::SB;
+      read_half<T, KA, FI>(SN, wm * WT, lane, 0, al);
+      read_half<T, KB, FI>(SN + DT::OPB, wn * WT, lane, 0, bl);
+    }
+    mfma4(ah, bh);
   }
 
   // Epilogue through LDS, as in the register-staged tile.
