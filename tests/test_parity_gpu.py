@@ -124,7 +124,11 @@ def test_prepare_reports_not_positive_definite():
 # ---------------------------------------------------------------- sweep (fed the oracle's U)
 @pytest.mark.parametrize("m,d,bits,g", [(300, 512, 4, 128), (64, 300, 3, 128), (129, 256, 4, 64),
                                         (100, 384, 2, 32), (70, 520, 4, 256), (33, 200, 4, -1),
-                                        (65, 256, 8, 128)])
+                                        (65, 256, 8, 128),
+                                        # >= 4096 rows: the rest of each 512-column super-block
+                                        # is updated in the sweep's epilogue (ragged rows and
+                                        # a ragged last super-block included)
+                                        (4096, 640, 4, 128), (4100, 1000, 3, 64)])
 def test_sweep_matches_oracle_given_oracle_factor(m, d, bits, g):
     rng = np.random.default_rng(m * d + bits)
     x = rng.standard_normal((4 * d, d))
