@@ -172,9 +172,11 @@ __device__ __forceinline__ int acc_row(int mi, int lane, int e) {
 
 // One 64-wide Cholesky panel at column k0 (kb <= 64 columns), for workgroup
 // b of the panel's grid:
-//   first, the previous panel's contribution to this panel's columns,
+//   the previous panel's contribution to this panel's columns,
 //     G[:, panel] −= L21ₚ·L21ₚ[panel rows]ᵀ (the trailing updates of the
-//     previous launch skip these columns so this launch can run it),
+//     previous launch skip these columns so this launch can run it): the
+//     diagonal block's part before the sweep, the workgroup's rows' part
+//     (only the L21 solve needs it) by wave 0 after its own steps,
 //   L11 = chol(G11),  X = L11⁻¹,  L21 = G21·Xᵀ.
 // Every workgroup (4 waves) factors and inverts the small diagonal block
 // itself, so no workgroup waits for another; workgroup b then solves the
@@ -233,15 +235,65 @@ __device__ __forceinline__ void strip(const float* BS, const float* PX, float* G
   }
 }
 
+// The rows' share of the pre-update, BS −= Q·Pᵀ with Q = the previous
+// panel's values in this workgroup's 64 rows and P = its values in the
+// panel's rows, by one wave from registers (v_mfma_f32_32x32x2f32; lanes
+// 0-31 take k in [0, 32), lanes 32-63 k in [32, 64), so each lane's 32
+// values of a row are contiguous).  Rows past d or kb count as zero.
+__device__ __forceinline__ void rows_preupdate(const float* G, int64_t d, int64_t R0, int k0,
+                                               int kb, int kp, float* BS, int lane) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const bool vec = (d & 3) == 0;
+  float qv[2][32], pv[2][32];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int64_t qr = R0 + 32 * x + l32;
+    const int pr = 32 * x + l32;
+    const bool qok = qr < d, pok = pr < kb;
+    const float* qs = G + (qok ? qr : 0) * d + kp + 32 * h;
+    const float* ps = G + (int64_t)(k0 + (pok ? pr : 0)) * d + kp + 32 * h;
+    if (vec) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(qs + 4 * j);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(ps + 4 * j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          qv[x][4 * j + u] = qok ? q4[u] : 0.f;
+          pv[x][4 * j + u] = pok ? p4[u] : 0.f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) {
+        qv[x][kk] = qok ? qs[kk] : 0.f;
+        pv[x][kk] = pok ? ps[kk] : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[mi][kk], pv[ni][kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) BS[acc_row(mi, lane, e) * LS + 32 * ni + l32] -= acc[e];
+    }
+}
+
 constexpr int kSpinLimit = 1 << 20;   // safety bound on a flag wait (never reached)
 
 __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __restrict__ smem) {
   float* AS = smem;              // G11 (lower, identity-padded)
   float* BS = smem + BLK;        // this workgroup's 64 rows of G21
   float* XS = smem + 2 * BLK;    // before the sweep: the previous panel's rows k0..k0+63
-  float* QS = smem + 3 * BLK;    // before the sweep: the previous panel's values in this workgroup's rows
   // during and after the sweep: published l [64][64] in AS's place, x [64][PXS]
-  // (= X by rows) in XS's place, flags [64] in QS's place
+  // (= X by rows) in XS's place, flags [65] after it
   float* PL = smem;
   float* PX = smem + 2 * BLK;
   int* flag = reinterpret_cast<int*>(smem + 3 * BLK);
@@ -270,22 +322,18 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
       vb[u] = okb ? vb[u] : 0.f;
     }
     if (upd) {
-      float vp[16], vq[16];
+      float vp[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
         const bool okp = i < kb;
         vp[u] = G[(int64_t)(k0 + (okp ? i : 0)) * d + kp + k];
         vp[u] = okp ? vp[u] : 0.f;
-        const bool okq = R0 + i < d;
-        vq[u] = G[(okq ? R0 + i : 0) * d + kp + k];
-        vq[u] = okq ? vq[u] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
         XS[i * LS + k] = vp[u];
-        QS[i * LS + k] = vq[u];
       }
     }
 #pragma unroll
@@ -297,18 +345,16 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   }
   __syncthreads();
   const int mi = w >> 1, ni = w & 1;
-  if (upd) {
-    f32x16 dacc, eacc;
+  // the diagonal block's pre-update, lower 32x32 tiles only (wave 1's tile
+  // is above the diagonal); the rows' pre-update (E) waits for wave 0's
+  // idle time after its own steps, as only the L21 strips need it
+  if (upd && !(mi == 0 && ni == 1)) {
+    f32x16 dacc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { dacc[e] = 0.f; eacc[e] = 0.f; }
+    for (int e = 0; e < 16; ++e) dacc[e] = 0.f;
     mfma_abt(XS, XS, mi, ni, lane, dacc);
-    mfma_abt(QS, XS, mi, ni, lane, eacc);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int o = acc_row(mi, lane, e) * LS + 32 * ni + (lane & 31);
-      AS[o] -= dacc[e];
-      BS[o] -= eacc[e];
-    }
+    for (int e = 0; e < 16; ++e) AS[acc_row(mi, lane, e) * LS + 32 * ni + (lane & 31)] -= dacc[e];
   }
   __syncthreads();
   float a[16], r[16];
@@ -317,7 +363,7 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     a[q] = AS[lane * LS + 16 * w + q];
     r[q] = (16 * w + q == lane) ? 1.f : 0.f;
   }
-  if (t < NB) flag[t] = 0;
+  if (t <= NB) flag[t] = 0;   // steps 0..63 and, at NB, "E applied"
   __syncthreads();   // AS is read: PL may overwrite it
 
   // consume the steps of the waves before this one, four at a time: one
@@ -403,8 +449,25 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
       r[q] = fmaf(-c, x, r[q]);
     }
   }
-  if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
   const bool rows = R0 < d;
+  if (upd && rows) {
+    if (w == 0) {
+      rows_preupdate(G, d, R0, k0, kb, kp, BS, lane);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __hip_atomic_store(&flag[NB], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else if (w < 3) {
+      int spin = 0;
+      while (!stalled &&
+             __hip_atomic_load(&flag[NB], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+        if (++spin > kSpinLimit) {
+          stalled = true;
+          bad_j = (bad_j < 0) ? 0 : bad_j;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
   if (rows && w < 3) strip(BS, PX, G, d, R0, k0, kb, w, 0, 4, lane);
   __syncthreads();   // the last strip's X rows (published by wave 3) are visible
   if (rows) strip(BS, PX, G, d, R0, k0, kb, 3, w, w + 1, lane);
