@@ -17,7 +17,7 @@
 //   err = (w_j − ŵ)·(1/U_jj);  every lane: w_k −= err·U_jk for its 8 columns
 // (U is upper triangular, so columns left of j receive zeros and the update
 // needs no per-lane bounds); the owner lane then keeps ŵ, err and q in the
-// column's register slot, and the block is written back coalesced from the
+// column's register slots, and the block is written back coalesced from the
 // registers.  Every lane of a row computes the same v, q, ŵ and err.  The
 // working copy is padded to whole blocks: padded columns hold 0 and their U
 // rows/columns are 0 with a unit diagonal, so they quantize to 0 with err 0.
@@ -31,8 +31,6 @@ namespace gq {
 namespace {
 
 constexpr int QC = kBlock / 16;   // columns per lane
-constexpr int SROW = kBlock + 1;  // err staging row stride (odd: the rows' writes hit distinct banks)
-constexpr int QROW = kBlock + 4;  // code staging row stride (bytes)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -75,8 +73,6 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   constexpr int GG = G > 0 ? G : 1;
   __shared__ __attribute__((aligned(16))) float Us[kBlock * kBlock];
   __shared__ float rud[kBlock];
-  // per wave: err [4][SROW] fp32 and codes [4][QROW] u8 of the block's columns
-  __shared__ __attribute__((aligned(16))) char stage[4][4 * SROW * 4 + 4 * QROW];
   const int nthr = blockDim.x, t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int c = lane & 15, rloc = lane >> 4;          // lane within the row, row in the wave
@@ -115,10 +111,11 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       }
     }
   }
-  // slot sl < 4: column 4c+sl; slot sl >= 4: column 64+4c+sl-4
-  float w[QC];
-  float* SE = reinterpret_cast<float*>(stage[wave]);
-  uint8_t* SQ = reinterpret_cast<uint8_t*>(SE + 4 * SROW);
+  // slot sl < 4: column 4c+sl; slot sl >= 4: column 64+4c+sl-4; after
+  // column j the owner lane's slot holds ŵ (w), err (e) and the code (qc)
+  float w[QC], e[QC], qc[QC];
+#pragma unroll
+  for (int k = 0; k < QC; ++k) { e[k] = 0.f; qc[k] = 0.f; }
   {
     const float* src = a.Wk + (live ? r : 0) * a.ldw + a.b0 + 4 * c;
     const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
@@ -200,15 +197,16 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       w[q4] = fmaf(-err, u0[q4], w[q4]);
       w[4 + q4] = fmaf(-err, u1[q4], w[4 + q4]);
     }
+    // every lane of the row holds the same ŵ, err and q; the owner keeps
+    // them (a store to one LDS address from 16 lanes would serialize)
     w[slot] = (c == o) ? wq : w[slot];
-    // every lane of the row holds the same err and q: same-address writes
-    SE[rloc * SROW + j] = err;
-    SQ[rloc * QROW + j] = (uint8_t)q;
+    e[slot] = (c == o) ? err : e[slot];
+    qc[slot] = (c == o) ? q : qc[slot];
     // keep the compiler from deferring column updates to the end of the
     // block (which holds every column's err in registers): the updated
-    // weights must exist here
+    // weights and the kept values must exist here
 #pragma unroll
-    for (int k = 0; k < QC; ++k) asm volatile("" : "+v"(w[k]));
+    for (int k = 0; k < QC; ++k) asm volatile("" : "+v"(w[k]), "+v"(e[k]), "+v"(qc[k]));
     __builtin_amdgcn_sched_barrier(0);
   }
   if (G > 0 && live && c == 0) {
@@ -221,16 +219,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       a.zeros[r * a.ng + gi] = (uint8_t)zv;
     }
   }
-  __builtin_amdgcn_wave_barrier();   // the row's staged err / codes are complete
-  // row loss ½·Σ err² from the staged errors: 8 columns per lane, then the row
+  // row loss ½·Σ err²: the lane's 8 columns, then the row
   float loss = 0.f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float e = SE[rloc * SROW + 64 * h + 4 * c + q];
-      loss = fmaf(e, e, loss);
-    }
+  for (int k = 0; k < QC; ++k) loss = fmaf(e[k], e[k], loss);
   loss += dpp<0xB1>(loss);
   loss += dpp<0x4E>(loss);
   loss += dpp<0x141>(loss);
@@ -244,12 +236,13 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 vw, ve;
+      uint32_t pk = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         vw[q] = w[4 * h + q];
-        ve[q] = SE[rloc * SROW + 64 * h + 4 * c + q];
+        ve[q] = e[4 * h + q];
+        pk |= (uint32_t)qc[4 * h + q] << (8 * q);
       }
-      const uint32_t pk = *reinterpret_cast<const uint32_t*>(SQ + rloc * QROW + 64 * h + 4 * c);
       *reinterpret_cast<f32x4*>(dw + 64 * h) = vw;
       *reinterpret_cast<f32x4*>(de + 64 * h) = ve;
       *reinterpret_cast<uint32_t*>(dq + 64 * h) = pk;
