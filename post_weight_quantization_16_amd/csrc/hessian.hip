@@ -192,6 +192,7 @@ constexpr int FROW = FT * 2;            // bytes per LDS row (one token)
 constexpr int FOP = FK * FROW;          // bytes per operand per stage (16 KB)
 constexpr int FSTAGE = 2 * FOP;         // bytes per stage (32 KB)
 constexpr int NBUF = 4;                 // stage buffers in the LDS ring (128 KB)
+constexpr int kPre = 1;                 // MFMAs of the second batch issued before the barrier
 // s_waitcnt immediates (vmcnt is split over bits [3:0] and [15:14];
 // expcnt/lgkmcnt not waited): in the loop, 2 stages of copies (8
 // instructions each) may stay pending; before it, one
@@ -287,82 +288,110 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
   }
   const unsigned sbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)S;
   const int nrows = (int)(t_end - t_begin);
-  auto dma = [&](int st) {
+  // copy instruction i of stage st (the wave's 1 KB piece i of the stage)
+  auto dma_one = [&](int st, int i) {
     const int rem = min(max(nrows - st * FK, 0), FK);   // valid token rows of the stage
     const int64_t soff = (int64_t)st * FK * ld * 2;
-    const unsigned lb = sbase + (unsigned)((st % NBUF) * FSTAGE) + (unsigned)(w * NI) * 1024u;
+    const unsigned lb = sbase + (unsigned)((st % NBUF) * FSTAGE) + (unsigned)(w * NI + i) * 1024u;
+    const bool ok = colok[i] && rrow[i] < rem;
+    const char* a = ok ? pbase[i] + soff : reinterpret_cast<const char*>(zero16);
+    // global_load_lds_dwordx4: 16 bytes per lane from address a to LDS
+    // M0 + 16·lane.  It has no register result; the stage's wait
+    // (s_waitcnt vmcnt) is what orders it before the reads.
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lb), "v"(a) : "memory");
+  };
+  auto dma = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const bool ok = colok[i] && rrow[i] < rem;
-      const char* a = ok ? pbase[i] + soff : reinterpret_cast<const char*>(zero16);
-      // global_load_lds_dwordx4: 16 bytes per lane from address a to LDS
-      // M0 + 16·lane.  It has no register result; the stage's wait below
-      // (s_waitcnt vmcnt) is what orders it before the reads.
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :: "s"(lb + (unsigned)i * 1024u), "v"(a) : "memory");
-    }
+    for (int i = 0; i < NI; ++i) dma_one(st, i);
   };
   const int g = lane >> 4, j16 = lane & 15;
   const int rsub = 8 * (g >> 1) + (j16 >> 2);
   const int csub = 16 * (g & 1) + 4 * (j16 & 3);
-  auto frag = [&](const char* base, int colbase, int ks) {
-    s16x4 lo, hi;
-    {
-      const int row = ks * 16 + rsub, col = colbase + csub;
-      const int off = row * FROW + (((col >> 3) ^ fswz(row)) << 4) + ((col & 7) << 1);
-      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
-    }
-    {
-      const int row = ks * 16 + 4 + rsub, col = colbase + csub;
-      const int off = row * FROW + (((col >> 3) ^ fswz(row)) << 4) + ((col & 7) << 1);
-      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
-    }
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  // Operand pieces of one 16-token step: piece n = 2f + h is half h (tokens
+  // 4h.. of each 8) of fragment f, f = 0..3 the A fragments, 4..7 the B
+  // fragments.  They are read in the order the MFMAs first need them.
+  constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+  auto rd = [&](const char* stage, int ks, int n) {
+    const int f = kOrder[n >> 1], h = n & 1;
+    const char* base = stage + (f < 4 ? 0 : FOP);
+    const int col = (f < 4 ? wm : wn) * 128 + (f & 3) * 32 + csub;
+    const int row = ks * 16 + 4 * h + rsub;
+    const int off = row * FROW + (((col >> 3) ^ fswz(row)) << 4) + ((col & 7) << 1);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
   };
-  auto frags = [&](int st, int ks, s16x8 (&a)[4], s16x8 (&b)[4]) {
-    const char* SA = S + (st % NBUF) * FSTAGE;
-    const char* SB = SA + FOP;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      a[f] = frag(SA, wm * 128 + f * 32, ks);
-      b[f] = frag(SB, wn * 128 + f * 32, ks);
-    }
-  };
-  auto mfma = [&](const s16x8 (&a)[4], const s16x8 (&b)[4]) {
-#pragma unroll
-    for (int fi = 0; fi < 4; ++fi)
-#pragma unroll
-      for (int fj = 0; fj < 4; ++fj) {
-        if constexpr (BF16)
-          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a[fi]), __builtin_bit_cast(bf16x8, b[fj]), acc[fi][fj], 0, 0, 0);
-        else
-          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, a[fi]), __builtin_bit_cast(f16x8, b[fj]), acc[fi][fj], 0, 0, 0);
-      }
+  // slot of fragment f in the piece array
+  constexpr int kSlot[8] = {0, 5, 6, 7, 1, 2, 3, 4};
+  auto mm = [&](int n, const s16x4 (&p)[16]) {
+    const int fi = n >> 2, fj = n & 3;
+    const int sa = kSlot[fi], sb = kSlot[4 + fj];
+    const s16x8 a = __builtin_shufflevector(p[2 * sa], p[2 * sa + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const s16x8 b = __builtin_shufflevector(p[2 * sb], p[2 * sb + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (BF16)
+      acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[fi][fj], 0, 0, 0);
+    else
+      acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc[fi][fj], 0, 0, 0);
   };
   static_assert(FK == 32, "a stage is two 16-token MFMA steps");
+  auto stage_ptr = [&](int st) { return (const char*)S + (st % NBUF) * FSTAGE; };
   for (int s0 = 0; s0 < NBUF - 1; ++s0) dma(s0);
-  // Stage st's first-step fragments are read during stage st-1, so each
-  // stage waits for its wave's copies of stage st+1 (the copies of the two
-  // stages after it stay in flight), and the barrier makes both stages
-  // visible and frees the buffer read in stage st-1 for the next copy.
-  s16x8 a0[4], b0[4], a1[4], b1[4];
+  // Each stage is two batches of 16 MFMAs.  Batch A multiplies the pieces of
+  // the stage's first step (p0) while reading those of its second step (p1)
+  // and issuing the copies of stage st+3; batch B multiplies p1 while
+  // reading the next stage's first step into p0.  One MFMA and one LDS read
+  // alternate (scheduling barriers keep the order), so the reads run under
+  // the MFMAs.  Between the batches each wave waits for its copies of stage
+  // st+1 (the copies of the two stages after it stay in flight) and for its
+  // LDS reads, and the barrier makes stage st+1 visible and frees the buffer
+  // of stage st (read completely by now) for the next copy.
+  // On a diagonal tile only the upper triangle is read by the reduction, so
+  // the wave below the diagonal (wm = 1, wn = 0) multiplies nothing: it
+  // copies its share of every stage and takes part in the barriers.
+  const bool idle = ti == tj && wm > wn;
   __builtin_amdgcn_s_waitcnt(kWaitFirst);
   __builtin_amdgcn_s_barrier();
-  frags(0, 0, a0, b0);
-  for (int st = 0; st < nstage; ++st) {
-    dma(st + NBUF - 1);            // into the buffer the previous barrier freed
-    frags(st, 1, a1, b1);
-    mfma(a0, b0);
-    // lgkmcnt(0) as well: every wave's reads of this stage's buffer are
-    // complete before the barrier after which it is copied over again
-    __builtin_amdgcn_s_waitcnt(kWaitStage & ~0xF00);
-    __builtin_amdgcn_s_barrier();
-    frags(st + 1, 0, a0, b0);      // the next stage's first step
-    mfma(a1, b1);
+  if (idle) {
+    for (int st = 0; st < nstage; ++st) {
+      dma(st + NBUF - 1);
+      __builtin_amdgcn_s_waitcnt(kWaitStage & ~0xF00);
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    s16x4 p0[16], p1[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) p0[n] = rd(stage_ptr(0), 0, n);
+    for (int st = 0; st < nstage; ++st) {
+      const char* cur = stage_ptr(st);
+      const char* nxt = stage_ptr(st + 1);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        mm(n, p0);
+        p1[n] = rd(cur, 1, n);
+        if (n & 1) dma_one(st + NBUF - 1, n >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int n = 0; n < kPre; ++n) {
+        mm(n, p1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lgkmcnt(0) as well: every wave's reads of this stage's buffer are
+      // complete before the barrier after which it is copied over again
+      __builtin_amdgcn_s_waitcnt(kWaitStage & ~0xF00);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        if (n + kPre < 16) mm(n + kPre, p1);
+        p0[n] = rd(nxt, 0, n);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA may outlive the workgroup
+  if (idle) return;
   float* Pt = P + (int64_t)split * dp * dp;
 #pragma unroll
   for (int fi = 0; fi < 4; ++fi)
