@@ -136,6 +136,9 @@ WORKLOADS = {
     "llama7b-up": Workload(
         name="llama7b-mlp-up (11008x4096, 131072 tok, bf16)", seed=1003, d_out=11008, d_in=4096,
         n_tok=131072, x_outlier_scale=15.0),
+    "llama7b-up-actorder": Workload(
+        name="llama7b-mlp-up act-order (11008x4096, 131072 tok, bf16)", seed=1003, d_out=11008,
+        d_in=4096, n_tok=131072, x_outlier_scale=15.0, act_order=True),
     "llama7b-down": Workload(
         name="llama7b-mlp-down (4096x11008, 131072 tok, bf16, 3-bit)", seed=1004, d_out=4096,
         d_in=11008, n_tok=131072, x_kind="abs_lognormal", bits=3),

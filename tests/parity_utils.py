@@ -128,8 +128,12 @@ def check_perm(gpu_perm, H_exact, dead_tol=1e-5):
 
 
 def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, check_u=True,
-                  perm_follow=True):
-    """Full comparison; returns a dict of measured figures and asserts the bar."""
+                  perm_follow=True, free_run=True, tie_tol=TIE_TOL, scale_tol=None):
+    """Full comparison; returns a dict of measured figures and asserts the bar.
+
+    free_run=False skips the informational second oracle run without
+    following the GPU's decisions (at large d it costs a second factorization).
+    """
     t0 = time.time()
     rep = {"label": label}
     d = W.shape[1]
@@ -143,7 +147,7 @@ def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, che
         perm = gpu["perm"] if perm_follow else None
     ora = oracle.gptq_layer(W, H_exact, oparams, w_dtype=w_dtype, perm=perm,
                             follow={"q": gpu["codes"], "z": gpu["zeros"].astype(np.float64)},
-                            tie_tol=TIE_TOL)
+                            tie_tol=tie_tol)
     if check_u:
         rep["U_rel"] = rel_fro(gpu["U"], ora["U"])
         assert rep["U_rel"] <= U_TOL, rep
@@ -151,13 +155,14 @@ def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, che
     rep.update(code_allowed=r.code_allowed, code_hard=r.code_hard, zero_allowed=r.zero_allowed,
                zero_hard=r.zero_hard, frac_identical=r.frac_codes_identical,
                max_tie_dist=r.max_tie_dist)
-    rep["free_run_identical"] = float(np.mean(
-        oracle.gptq_layer(W, H_exact, oparams, w_dtype=w_dtype, perm=perm)["q"] == gpu["codes"]))
+    if free_run:
+        rep["free_run_identical"] = float(np.mean(
+            oracle.gptq_layer(W, H_exact, oparams, w_dtype=w_dtype, perm=perm)["q"] == gpu["codes"]))
     assert r.ok, (rep, r.hard_examples[:5])
     assert r.frac_codes_identical >= MIN_IDENTICAL, rep
     s_rel = np.abs(gpu["scales"] - ora["s"]) / np.abs(ora["s"])
     rep["scale_rel_max"] = float(s_rel.max())
-    assert rep["scale_rel_max"] <= SCALE_TOL, rep
+    assert rep["scale_rel_max"] <= (SCALE_TOL if scale_tol is None else scale_tol), rep
     assert np.array_equal(gpu["zeros"], ora["z"].astype(np.uint8))
     e_gpu = oracle.layer_error(ora["W"], gpu["what"], H_exact)
     e_ora = oracle.layer_error(ora["W"], ora["what"], H_exact)

@@ -1,10 +1,24 @@
-"""Parity at the full size of the benchmarked layer (4096 x 4096, 131072
-tokens, bf16, 4-bit g128), in the same launch configuration bench.py times.
+"""Parity at the full sizes of the five layer workloads, in the same launch
+configuration bench.py times: the 4096 x 4096 attention projection (the
+benchmarked layer), the 11008 x 4096 MLP up-projection in natural and
+act-order, the 4096 x 11008 3-bit down-projection and the 28672 x 8192
+act-order MLP layer (131072 or 262144 bf16 tokens).
 
 The oracle computes the exact H (fp64 over all tokens) and its own U; the
 sweep, whose rows are independent problems sharing H, is checked on a
 sample of rows: the oracle quantizes exactly those rows with the full
 factor and follows the GPU's decisions as in the small-size tests.
+
+The down-projection's Hessian is ill-conditioned (|N(0,1)| activations
+with log-normal channel scales: cond(H_d) about 3e4).  There U moves about
+100 times the relative error of H, so the fp32-accumulated Hessian (5e-7
+from the exact one, far inside the 1e-3 bar) moves U by about 6e-5, and a
+handful of pre-round values by up to ~2e-4 code units and group scales by
+up to ~5e-5; an exact fp64 factorization of the GPU's H moves them the same
+way.  For that layer the end-to-end run keeps the other bars but takes flips
+within 5e-4 of a boundary as allowed and scales within 1e-4, and the sweep
+is held to the strict bars (1e-4 window, 1e-5 scales) on its own, fed the
+oracle's factor of the exact H.
 """
 import time
 
@@ -13,29 +27,61 @@ import pytest
 
 import oracle
 import synth
-from parity_utils import compare_layer, log, params_of, rel_fro, run_gpu, torch_mod
+from parity_utils import TIE_TOL, compare_layer, log, params_of, rel_fro, run_gpu, torch_mod
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-@pytest.mark.timeout(900)
-def test_full_size_attention_projection():
+# end-to-end tie window (code units) and scale bar of the ill-conditioned layer
+ILL_CONDITIONED = {"llama7b-down": (5e-4, 1e-4)}
+
+
+def _full_size(name, n_rows=96):
     torch = torch_mod()
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    wl = synth.WORKLOADS["llama7b-attn"]
+    wl = synth.WORKLOADS[name]
     t0 = time.time()
     W = synth.make_weights(wl)
     X = synth.make_activations(wl)
-    log(f"FULL inputs generated in {time.time() - t0:.1f}s: W{W.shape} X{X.shape}")
+    log(f"FULL {name}: inputs generated in {time.time() - t0:.1f}s: W{W.shape} X{X.shape}")
     gp, op = params_of(wl)
     gpu = run_gpu(W, wl.w_dtype, X, wl.x_dtype, gp)
-    log(f"FULL gpu done at {time.time() - t0:.1f}s")
-    H_ex = oracle.hessian(X, wl.x_dtype, chunk=4096)
+    log(f"FULL {name}: gpu done at {time.time() - t0:.1f}s")
+    # H is a sum over tokens: the oracle runs on slices (a progress line each)
+    H_ex = None
+    for t in range(0, X.shape[0], 32768):
+        Hs = oracle.hessian(X[t:t + 32768], wl.x_dtype, chunk=4096)
+        H_ex = Hs if H_ex is None else H_ex + Hs
+        log(f"FULL {name}: oracle H through token {min(t + 32768, X.shape[0])} at {time.time() - t0:.1f}s")
     del X
-    log(f"FULL oracle H done at {time.time() - t0:.1f}s; H rel_fro={rel_fro(gpu['H'], H_ex):.3e}")
-    rows = np.sort(np.random.default_rng(0).choice(wl.d_out, 96, replace=False))
+    log(f"FULL {name}: oracle H done at {time.time() - t0:.1f}s; "
+        f"H rel_fro={rel_fro(gpu['H'], H_ex):.3e}")
+    rows = np.sort(np.random.default_rng(0).choice(wl.d_out, n_rows, replace=False))
     sub = {k: (v[rows] if k in ("qweight", "scales", "zeros", "what", "row_loss", "codes") else v)
            for k, v in gpu.items()}
-    compare_layer(sub, W[rows], wl.w_dtype, H_ex, op, label="full-size attn (96 sampled rows)")
-    log(f"FULL compare done at {time.time() - t0:.1f}s")
+    del gpu
+    tie = ILL_CONDITIONED.get(name)
+    compare_layer(sub, W[rows], wl.w_dtype, H_ex, op, label=f"full-size {name} ({n_rows} sampled rows)",
+                  free_run=name == "llama7b-attn", tie_tol=tie[0] if tie else TIE_TOL,
+                  scale_tol=tie[1] if tie else None)
+    if tie:
+        # the sweep alone at the strict window, fed the oracle's factor
+        P = oracle.prepare(H_ex, op.percdamp)
+        g2 = run_gpu(W, wl.w_dtype, None, None, gp, H_in=H_ex, U_in=P["U"], perm_in=P["perm"])
+        sub2 = {k: (v[rows] if k in ("qweight", "scales", "zeros", "what", "row_loss", "codes") else v)
+                for k, v in g2.items()}
+        compare_layer(sub2, W[rows], wl.w_dtype, H_ex, op, check_h=False, check_u=False, free_run=False,
+                      label=f"full-size {name} sweep given the oracle factor ({n_rows} sampled rows)")
+    log(f"FULL {name}: compare done at {time.time() - t0:.1f}s")
+
+
+@pytest.mark.timeout(900)
+def test_full_size_attention_projection():
+    _full_size("llama7b-attn")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama7b-up", "llama7b-up-actorder", "llama7b-down", "llama70b-mlp"])
+def test_full_size_other_layers(name):
+    _full_size(name)

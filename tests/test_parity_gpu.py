@@ -125,10 +125,11 @@ def test_prepare_reports_not_positive_definite():
 @pytest.mark.parametrize("m,d,bits,g", [(300, 512, 4, 128), (64, 300, 3, 128), (129, 256, 4, 64),
                                         (100, 384, 2, 32), (70, 520, 4, 256), (33, 200, 4, -1),
                                         (65, 256, 8, 128),
-                                        # >= 4096 rows: the rest of each 512-column super-block
-                                        # is updated in the sweep's epilogue (ragged rows and
-                                        # a ragged last super-block included)
-                                        (4096, 640, 4, 128), (4100, 1000, 3, 64)])
+                                        # >= 4096 rows: four-wave workgroups of 16-lane rows
+                                        # (ragged last workgroup and super-block included)
+                                        (4096, 640, 4, 128), (4100, 1000, 3, 64),
+                                        # several super-blocks, ragged last one included
+                                        (200, 2100, 4, 128), (96, 1536, 3, 64), (130, 1800, 4, 32)])
 def test_sweep_matches_oracle_given_oracle_factor(m, d, bits, g):
     rng = np.random.default_rng(m * d + bits)
     x = rng.standard_normal((4 * d, d))
@@ -150,6 +151,7 @@ CASES = {
                                                                  act_order=True),
     "down-3bit@256x1000": synth.WORKLOADS["llama7b-down"].scaled(d_out=256, d_in=1000, n_tok=8192),
     "70b-actorder@384x768": synth.WORKLOADS["llama70b-mlp"].scaled(d_out=384, d_in=768, n_tok=8192),
+    "attn@256x2560": synth.WORKLOADS["llama7b-attn"].scaled(d_out=256, d_in=2560, n_tok=8192),
 }
 
 
