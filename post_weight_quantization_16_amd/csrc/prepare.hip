@@ -59,41 +59,58 @@ __global__ __launch_bounds__(1024) void diag_kernel(float* __restrict__ H, int64
   }
 }
 
-// Rank sort: position of i = #{j : key_j > key_i or (key_j == key_i and j < i)}.
-// The order is written to the workspace and, when given, to the caller's
-// perm_out as well (no separate copy).
-__global__ __launch_bounds__(256) void rank_kernel(const float* __restrict__ diag, int d,
-                                                   int act_order, int* __restrict__ perm,
-                                                   int* __restrict__ perm_out) {
+// Stable descending rank sort: the position of i is
+// #{j : key_j > key_i or (key_j == key_i and j < i)} (a NaN key counts as
+// −inf).  Without act-order the order is the identity.  With it, workgroup
+// (x, y) counts keys y·256.. against keys x·256.. from LDS and adds its
+// partial counts atomically (integers: the sums do not depend on their
+// order), then rank_scatter_kernel writes the order to the workspace and,
+// when given, to the caller's perm_out.
+__device__ __forceinline__ float rank_key(const float* diag, int j, int d) {
+  const float v = j < d ? diag[j] : -INFINITY;
+  return v != v ? -INFINITY : v;
+}
+
+__global__ __launch_bounds__(256) void rank_identity_kernel(int d, int* __restrict__ perm,
+                                                            int* __restrict__ perm_out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (!act_order) {
-    if (i < d) {
-      perm[i] = i;
-      if (perm_out) perm_out[i] = i;
-    }
-    return;
-  }
-  __shared__ float kj[256];
-  float ki = -INFINITY;
-  if (i < d) { ki = diag[i]; if (ki != ki) ki = -INFINITY; }
-  int rank = 0;
-  for (int j0 = 0; j0 < d; j0 += 256) {
-    __syncthreads();
-    const int j = j0 + threadIdx.x;
-    float v = -INFINITY;
-    if (j < d) { v = diag[j]; if (v != v) v = -INFINITY; }
-    kj[threadIdx.x] = v;
-    __syncthreads();
-    const int n = min(256, d - j0);
-    for (int k = 0; k < n; ++k) {
-      const float v2 = kj[k];
-      rank += (v2 > ki) || (v2 == ki && j0 + k < i);
-    }
-  }
   if (i < d) {
-    perm[rank] = i;
-    if (perm_out) perm_out[rank] = i;
+    perm[i] = i;
+    if (perm_out) perm_out[i] = i;
   }
+}
+
+__global__ __launch_bounds__(256) void rank_count_kernel(const float* __restrict__ diag, int d,
+                                                         int* __restrict__ cnt) {
+  __shared__ __attribute__((aligned(16))) float kj[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int j0 = blockIdx.y * 256;
+  kj[threadIdx.x] = rank_key(diag, j0 + threadIdx.x, d);   // keys past d: −inf, never counted
+  const float ki = rank_key(diag, i, d);
+  __syncthreads();
+  int rank = 0;
+#pragma unroll 8
+  for (int k = 0; k < 256; k += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(kj + k);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rank += (v[u] > ki) || (v[u] == ki && j0 + k + u < i);
+  }
+  if (i < d && rank > 0) atomicAdd(cnt + i, rank);
+}
+
+__global__ __launch_bounds__(256) void rank_scatter_kernel(const int* __restrict__ cnt, int d,
+                                                           int* __restrict__ perm,
+                                                           int* __restrict__ perm_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < d) {
+    perm[cnt[i]] = i;
+    if (perm_out) perm_out[cnt[i]] = i;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_int_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // G[a][b] = H[π(d−1−a)][π(d−1−b)] + λ·[a == b]: the damped, permuted and
@@ -137,6 +154,80 @@ __global__ __launch_bounds__(256) void build_g_kernel(const float* __restrict__ 
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (b0 + q < d) G[a * d + b0 + q] = v[q];
+      }
+    }
+  }
+}
+
+// The permuted G for rows that fit in LDS (d ≤ kRowLds): one row a per
+// workgroup step.  Row π(d−1−a) of H is staged in LDS with coalesced
+// loads, then every thread gathers its columns from LDS and writes them
+// coalesced (a gather from memory moves one 4-byte word per access).  The
+// source columns π(d−1−b) are re-read for every row (the same 4·d bytes,
+// from cache): held in registers they would cost occupancy.
+constexpr int kRowLds = 16384;          // floats per staged row (64 KB)
+__global__ __launch_bounds__(256) void build_g_rows_kernel(const float* __restrict__ H, int d,
+                                                           const int* __restrict__ perm,
+                                                           const float* __restrict__ lam,
+                                                           float* __restrict__ G) {
+  extern __shared__ __attribute__((aligned(16))) float row[];
+  const float l = lam[0];
+  const int t = threadIdx.x;
+  const bool vec = (d & 3) == 0;
+  for (int a = blockIdx.x; a < d; a += gridDim.x) {
+    const float* src = H + (int64_t)perm[d - 1 - a] * d;
+    __syncthreads();   // the previous row's gathers are done
+    // every load of a pass before its first LDS store
+    if (vec) {
+      for (int e0 = 0; e0 < d; e0 += 8192) {
+        f32x4 buf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + 1024 * u + 4 * t;
+          if (e < d) buf[u] = *reinterpret_cast<const f32x4*>(src + e);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + 1024 * u + 4 * t;
+          if (e < d) *reinterpret_cast<f32x4*>(row + e) = buf[u];
+        }
+      }
+    } else {
+      for (int e0 = 0; e0 < d; e0 += 4096) {
+        float buf[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          buf[u] = e < d ? src[e] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          if (e < d) row[e] = buf[u];
+        }
+      }
+    }
+    __syncthreads();
+    float* dst = G + (int64_t)a * d;
+    for (int b0 = 4 * t; b0 < d; b0 += 1024) {
+      int pb[4];
+      if (vec) {   // π(d−1−b0−q), q = 0..3: one aligned int4, reversed
+        const int4 p4 = *reinterpret_cast<const int4*>(perm + d - 4 - b0);
+        pb[0] = p4.w; pb[1] = p4.z; pb[2] = p4.y; pb[3] = p4.x;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pb[q] = b0 + q < d ? perm[d - 1 - b0 - q] : 0;
+      }
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = row[pb[q]] + ((a == b0 + q) ? l : 0.f);
+      if (vec) {
+        const f32x4 o = {v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(dst + b0) = o;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (b0 + q < d) dst[b0 + q] = v[q];
       }
     }
   }
@@ -650,7 +741,7 @@ FarJob far_base(float* G, int64_t d) {
 }
 
 struct PrepWs {
-  int* status; float* lam; float* diag; int* perm; float* G; float* Linv; float* T;
+  int* status; float* lam; float* diag; int* perm; int* cnt; float* G; float* Linv; float* T;
 };
 
 PrepWs carve(void* ws, int64_t d) {
@@ -660,6 +751,7 @@ PrepWs carve(void* ws, int64_t d) {
   w.lam = reinterpret_cast<float*>(p); p += 256;
   w.diag = reinterpret_cast<float*>(p); p += align_up((size_t)d * 4);
   w.perm = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
+  w.cnt = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
   w.G = reinterpret_cast<float*>(p); p += align_up((size_t)d * d * 4);
   w.Linv = reinterpret_cast<float*>(p); p += align_up((size_t)d * d * 4);
   w.T = reinterpret_cast<float*>(p);
@@ -669,7 +761,7 @@ PrepWs carve(void* ws, int64_t d) {
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t d) {
-  return 512 + 2 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
+  return 512 + 3 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
          align_up((size_t)(d * d / 2 + NB * NB) * 4);
 }
 
@@ -686,12 +778,26 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   } while (0)
   diag_kernel<<<1, 1024, 0, s>>>(H, d, dead_mask, w.diag, percdamp, w.lam, w.status);
   GQ_CHECK();
-  rank_kernel<<<(unsigned)ceil_div(d, 256), 256, 0, s>>>(w.diag, (int)d, act_order, w.perm,
-                                                          perm_out);
+  {
+    const unsigned nb = (unsigned)ceil_div(d, 256);
+    if (!act_order) {
+      rank_identity_kernel<<<nb, 256, 0, s>>>((int)d, w.perm, perm_out);
+    } else {
+      zero_int_kernel<<<nb, 256, 0, s>>>(w.cnt, (int)d);
+      GQ_CHECK();
+      rank_count_kernel<<<dim3(nb, nb), 256, 0, s>>>(w.diag, (int)d, w.cnt);
+      GQ_CHECK();
+      rank_scatter_kernel<<<nb, 256, 0, s>>>(w.cnt, (int)d, w.perm, perm_out);
+    }
+  }
   GQ_CHECK();
   const unsigned gy = (unsigned)std::min<int64_t>(d, 65535);
-  build_g_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(H, d, w.perm, w.lam, w.G,
-                                                                      act_order ? 0 : 1);
+  if (act_order && d <= kRowLds)
+    build_g_rows_kernel<<<(unsigned)std::min<int64_t>(d, 1024), 256, (size_t)d * 4, s>>>(
+        H, (int)d, w.perm, w.lam, w.G);
+  else
+    build_g_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(H, d, w.perm, w.lam, w.G,
+                                                                        act_order ? 0 : 1);
   GQ_CHECK();
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();

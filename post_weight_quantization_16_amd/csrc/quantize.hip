@@ -30,7 +30,7 @@
 namespace gq {
 namespace {
 
-struct QWs { float* Wk; float* Err; uint8_t* codes; int* inv; float* Upad; };
+struct QWs { float* Wk; float* Err; uint8_t* codes; int* inv; int* src; float* Upad; };
 
 // Working copy and codes are padded to whole blocks (dp = ceil(d/128)·128).
 QWs carve(void* ws, int64_t m, int64_t d) {
@@ -41,6 +41,7 @@ QWs carve(void* ws, int64_t m, int64_t d) {
   w.Err = reinterpret_cast<float*>(p); p += align_up((size_t)m * kSuper * kBlock * 4);
   w.codes = reinterpret_cast<uint8_t*>(p); p += align_up((size_t)m * dp);
   w.inv = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
+  w.src = reinterpret_cast<int*>(p); p += align_up((size_t)dp * 4);
   w.Upad = reinterpret_cast<float*>(p);
   return w;
 }
@@ -134,6 +135,122 @@ __global__ __launch_bounds__(256) void init_kernel(const void* __restrict__ W, i
         for (int q = 0; q < 8; ++q)
           if (a0 + q < d) inv[c[q]] = (int)(a0 + q);
       }
+    }
+  }
+}
+
+// Permuted working copy for rows that fit in LDS (dp ≤ kRowLds): src[a] =
+// π(a), or −1 for a dead column or a ≥ d (src_index_kernel, once), then one
+// row of W per workgroup step, staged in LDS with coalesced loads
+// (converted to fp32) and gathered as Wk[r][a] = W[r][src[a]] (0 where src
+// is −1), written coalesced.  The source indices are re-read for every row
+// (the same 4·dp bytes each time, from cache): kept in registers they would
+// cost the occupancy that hides each row's load latency.
+constexpr int kRowLds = 16384;            // staged row length limit (64 KB of fp32)
+__global__ __launch_bounds__(256) void src_index_kernel(const int* __restrict__ perm,
+                                                        const uint8_t* __restrict__ dead, int d,
+                                                        int dp, int* __restrict__ src,
+                                                        int* __restrict__ inv) {
+  const int a = blockIdx.x * 256 + threadIdx.x;
+  if (a >= dp) return;
+  int c = -1;
+  if (a < d) {
+    const int pa = perm[a];
+    inv[pa] = a;
+    c = (dead && dead[pa]) ? -1 : pa;
+  }
+  src[a] = c;
+}
+
+__global__ __launch_bounds__(256) void init_rows_kernel(const void* __restrict__ W, int dt,
+                                                        int64_t ld_w, int64_t m, int d, int dp,
+                                                        const int* __restrict__ src_idx,
+                                                        float* __restrict__ Wk,
+                                                        float* __restrict__ row_loss, int vec_in) {
+  extern __shared__ __attribute__((aligned(16))) float row[];
+  const int t = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+    __syncthreads();
+    // every load of the row before the first LDS store
+    if (dt == GPTQ_F32 && vec_in) {
+      const float* src = static_cast<const float*>(W) + r * ld_w;
+      for (int e0 = 0; e0 < d; e0 += 8192) {
+        f32x4 buf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + 1024 * u + 4 * t;
+          if (e + 3 < d) buf[u] = *reinterpret_cast<const f32x4*>(src + e);
+          else
+#pragma unroll
+            for (int q = 0; q < 4; ++q) buf[u][q] = e + q < d ? src[e + q] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + 1024 * u + 4 * t;
+          if (e < d) *reinterpret_cast<f32x4*>(row + e) = buf[u];
+        }
+      }
+    } else if (dt != GPTQ_F32 && vec_in) {
+      const uint16_t* src = static_cast<const uint16_t*>(W) + r * ld_w;
+      uint4 buf[kRowLds / 2048];
+#pragma unroll
+      for (int u = 0; u < kRowLds / 2048; ++u) {
+        const int e = 2048 * u + 8 * t;
+        if (e + 7 < d) {
+          buf[u] = *reinterpret_cast<const uint4*>(src + e);
+        } else {
+          uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (e + q < d) wd[q >> 1] |= (uint32_t)src[e + q] << (16 * (q & 1));
+          buf[u] = uint4{wd[0], wd[1], wd[2], wd[3]};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kRowLds / 2048; ++u) {
+        const int e = 2048 * u + 8 * t;
+        if (e >= d) break;
+        const uint32_t wd[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+        f32x4 lo, hi;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint16_t h = (uint16_t)(wd[q >> 1] >> (16 * (q & 1)));
+          const float x = dt == GPTQ_BF16 ? __uint_as_float((uint32_t)h << 16)
+                                          : (float)__builtin_bit_cast(_Float16, h);
+          if (q < 4) lo[q] = x; else hi[q - 4] = x;
+        }
+        *reinterpret_cast<f32x4*>(row + e) = lo;       // row has room up to dp >= e + 8
+        *reinterpret_cast<f32x4*>(row + e + 4) = hi;
+      }
+    } else {
+      for (int e0 = 0; e0 < d; e0 += 4096) {
+        float buf[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          buf[u] = e < d ? load_w(W, dt, r * ld_w + e) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          if (e < d) row[e] = buf[u];
+        }
+      }
+    }
+    if (row_loss && t == 0) row_loss[r] = 0.f;
+    __syncthreads();
+    for (int a0 = 8 * t; a0 < dp; a0 += 2048) {   // src_idx is 256-byte aligned, dp % 128 == 0
+      const int4 s0 = *reinterpret_cast<const int4*>(src_idx + a0);
+      const int4 s1 = *reinterpret_cast<const int4*>(src_idx + a0 + 4);
+      const int c[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      f32x4 lo, hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo[q] = c[q] < 0 ? 0.f : row[c[q]];
+        hi[q] = c[4 + q] < 0 ? 0.f : row[c[4 + q]];
+      }
+      *reinterpret_cast<f32x4*>(Wk + r * dp + a0) = lo;
+      *reinterpret_cast<f32x4*>(Wk + r * dp + a0 + 4) = hi;
     }
   }
 }
@@ -270,6 +387,102 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   }
 }
 
+// Outputs in the original column order for rows that fit in LDS (dp ≤
+// kFinLds): one row per workgroup step; the working row and its codes are
+// staged in LDS with coalesced loads, then each thread gathers its 8-column
+// chunks (inv re-read from cache for every row, as in init_rows_kernel),
+// writes Ŵ coalesced and packs the codes.  The workgroup that takes row 0
+// writes g_idx.
+constexpr int kFinLds = 13056;   // floats + code bytes of one row within 64 KB
+__global__ __launch_bounds__(256) void finalize_rows_kernel(const float* __restrict__ Wk,
+                                                            const uint8_t* __restrict__ codes,
+                                                            const int* __restrict__ inv, int64_t m,
+                                                            int d, int dp, int bits, int64_t g,
+                                                            uint32_t* __restrict__ qweight,
+                                                            float* __restrict__ W_hat,
+                                                            int32_t* __restrict__ g_idx, int vec_w) {
+  extern __shared__ __attribute__((aligned(16))) float row[];
+  uint8_t* qrow = reinterpret_cast<uint8_t*>(row + dp);   // dp is a multiple of 128
+  const int t = threadIdx.x;
+  const int cpw = bits <= 4 ? 8 : 4, cwid = 32 / cpw;
+  const int64_t nw = (d + cpw - 1) / cpw;
+  if (g_idx && blockIdx.x == 0)
+    for (int cc = t; cc < d; cc += 256) g_idx[cc] = (int32_t)(inv[cc] / g);
+  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+    __syncthreads();
+    const float* wr = Wk + r * dp;
+    const uint8_t* qr = codes + r * dp;
+    // every load of the row and its codes before the first LDS store
+    for (int e0 = 0; e0 < dp; e0 += 8192) {
+      f32x4 wb[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 1024 * u + 4 * t;
+        if (e < dp) wb[u] = *reinterpret_cast<const f32x4*>(wr + e);
+      }
+      const int eq0 = e0 + 16 * t, eq1 = e0 + 4096 + 16 * t;
+      uint4 qb0 = {0u, 0u, 0u, 0u}, qb1 = {0u, 0u, 0u, 0u};
+      if (eq0 < dp) qb0 = *reinterpret_cast<const uint4*>(qr + eq0);
+      if (eq1 < dp) qb1 = *reinterpret_cast<const uint4*>(qr + eq1);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 1024 * u + 4 * t;
+        if (e < dp) *reinterpret_cast<f32x4*>(row + e) = wb[u];
+      }
+      if (eq0 < dp) *reinterpret_cast<uint4*>(qrow + eq0) = qb0;
+      if (eq1 < dp) *reinterpret_cast<uint4*>(qrow + eq1) = qb1;
+    }
+    __syncthreads();
+    for (int c0 = 8 * t; c0 < d; c0 += 2048) {
+      const bool full = c0 + 7 < d;
+      int a[8];
+      if (full) {   // inv sits 256-byte aligned in the workspace
+        const int4 p0 = *reinterpret_cast<const int4*>(inv + c0);
+        const int4 p1 = *reinterpret_cast<const int4*>(inv + c0 + 4);
+        a[0] = p0.x; a[1] = p0.y; a[2] = p0.z; a[3] = p0.w;
+        a[4] = p1.x; a[5] = p1.y; a[6] = p1.z; a[7] = p1.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = c0 + q < d ? inv[c0 + q] : 0;
+      }
+      float v[8];
+      uint32_t cd[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[q] = c0 + q < d ? row[a[q]] : 0.f;
+        cd[q] = c0 + q < d ? qrow[a[q]] : 0u;
+      }
+      if (W_hat) {
+        float* dst = W_hat + r * d + c0;
+        if (vec_w && full) {
+          const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
+          *reinterpret_cast<f32x4*>(dst) = lo;
+          *reinterpret_cast<f32x4*>(dst + 4) = hi;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (c0 + q < d) dst[q] = v[q];
+        }
+      }
+      if (cpw == 8) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) word |= cd[q] << (cwid * q);
+        qweight[r * nw + c0 / 8] = word;
+      } else {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w0 |= cd[q] << (cwid * q);
+          w1 |= cd[4 + q] << (cwid * q);
+        }
+        qweight[r * nw + c0 / 4] = w0;
+        if (c0 + 4 < d) qweight[r * nw + c0 / 4 + 1] = w1;
+      }
+    }
+  }
+}
+
 template <int G>
 hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_params& p,
                       int64_t g, int ng, float* scales, uint8_t* zeros, float* row_loss,
@@ -336,7 +549,7 @@ size_t quantize_ws_bytes(int64_t m, int64_t d) {
   const int64_t dp = ceil_div(d, kBlock) * kBlock;
   return align_up((size_t)m * dp * 4) + align_up((size_t)m * kSuper * kBlock * 4) +
          align_up((size_t)m * dp) +
-         align_up((size_t)d * 4) + align_up((size_t)kBlock * kBlock * 4);
+         align_up((size_t)d * 4) + align_up((size_t)dp * 4) + align_up((size_t)kBlock * kBlock * 4);
 }
 
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int64_t ld_w,
@@ -352,9 +565,17 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
   const int esz = w_dtype == GPTQ_F32 ? 4 : 2;
   const int vec_in = ((uintptr_t)W % 16 == 0) && ((ld_w * esz) % 16 == 0);
   const unsigned gy4 = (unsigned)std::min<int64_t>(ceil_div(m, 4), 65535);
-  init_kernel<<<dim3((unsigned)ceil_div(dp, 2048), gy4), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp,
-                                                                    perm, dead, w.Wk, w.inv,
-                                                                    row_loss, vec_in);
+  if (perm && dp <= kRowLds) {
+    src_index_kernel<<<(unsigned)ceil_div(dp, 256), 256, 0, s>>>(perm, dead, (int)d, (int)dp, w.src,
+                                                                 w.inv);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    init_rows_kernel<<<(unsigned)std::min<int64_t>(m, 1024), 256, (size_t)dp * 4, s>>>(
+        W, w_dtype, ld_w, m, (int)d, (int)dp, w.src, w.Wk, row_loss, vec_in);
+  } else
+    init_kernel<<<dim3((unsigned)ceil_div(dp, 2048), gy4), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp,
+                                                                      perm, dead, w.Wk, w.inv,
+                                                                      row_loss, vec_in);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g) {
@@ -365,8 +586,12 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
   }
   if (e != hipSuccess) return e;
   const int vec_w = W_hat && ((uintptr_t)W_hat % 16 == 0) && (d % 4 == 0);
-  finalize_kernel<<<dim3((unsigned)ceil_div(d, 2048), gy), 256, 0, s>>>(
-      w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight, W_hat, g_idx, vec_w, perm ? 0 : 1);
+  if (perm && dp <= kFinLds)
+    finalize_rows_kernel<<<(unsigned)std::min<int64_t>(m, 1024), 256, (size_t)dp * 5, s>>>(
+        w.Wk, w.codes, w.inv, m, (int)d, (int)dp, p.bits, g, qweight, W_hat, g_idx, vec_w);
+  else
+    finalize_kernel<<<dim3((unsigned)ceil_div(d, 2048), gy), 256, 0, s>>>(
+        w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight, W_hat, g_idx, vec_w, perm ? 0 : 1);
   return hipGetLastError();
 }
 
