@@ -73,7 +73,9 @@ def test_hessian_of_hadamard_columns_is_exact():
 
 
 # ---------------------------------------------------------------- prepare (fed the oracle's H)
-@pytest.mark.parametrize("d,act", [(256, False), (320, True), (1000, False), (700, True), (64, False), (5, True)])
+@pytest.mark.parametrize("d,act", [(256, False), (320, True), (1000, False), (700, True), (64, False), (5, True),
+                                   # several super-panels of far tasks, ragged end
+                                   (2100, False), (3072, True)])
 def test_prepare_matches_oracle(d, act):
     torch = torch_mod()
     rng = np.random.default_rng(d)
