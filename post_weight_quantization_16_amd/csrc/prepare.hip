@@ -577,6 +577,14 @@ __device__ __forceinline__ void lower_tile(int L, int& by, int& bx) {
   bx = L - y * (y + 1) / 2;
 }
 
+// Without a permutation H_d = H + λI: H already holds the dead fix (its
+// off-diagonal entries never change), so only the diagonal moves.
+__global__ __launch_bounds__(256) void add_diag_kernel(float* __restrict__ H, int64_t d,
+                                                       const float* __restrict__ lam) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < d) H[i * d + i] += lam[0];
+}
+
 // H_out[x][y] = H_d[x][y] rebuilt from G's untouched strict upper triangle
 // (G = J·H_d·J, so H_d[x][y] = G[d-1-x][d-1-y]), one lower 64x64 tile of
 // H_out per workgroup: the tile is read along G's rows, written directly,
@@ -861,10 +869,12 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
 
   write_u_kernel<<<dim3((unsigned)ceil_div(d, 1024), gy), 256, 0, s>>>(w.Linv, d, U);
   GQ_CHECK();
-  {
+  if (act_order) {
     const int64_t nb64 = ceil_div(d, 64);
     write_hd_kernel<<<(unsigned)(nb64 * (nb64 + 1) / 2), 256, 0, s>>>(H, d, w.G, w.diag, w.perm,
                                                                       w.lam);
+  } else {
+    add_diag_kernel<<<(unsigned)ceil_div(d, 256), 256, 0, s>>>(H, d, w.lam);
   }
   GQ_CHECK();
 #undef GQ_CHECK
