@@ -131,11 +131,13 @@ def test_prepare_reports_not_positive_definite():
                                         # (ragged last workgroup and super-block included)
                                         (4096, 640, 4, 128), (4100, 1000, 3, 64),
                                         # several super-blocks, ragged last one included
-                                        (200, 2100, 4, 128), (96, 1536, 3, 64), (130, 1800, 4, 32)])
+                                        (200, 2100, 4, 128), (96, 1536, 3, 64), (130, 1800, 4, 32),
+                                        # degenerate shapes: one row, one column, a 9-column row group
+                                        (1, 300, 4, 128), (7, 1, 4, -1), (2, 9, 3, -1)])
 def test_sweep_matches_oracle_given_oracle_factor(m, d, bits, g):
     rng = np.random.default_rng(m * d + bits)
-    x = rng.standard_normal((4 * d, d))
-    x[:, rng.choice(d, 3, replace=False)] *= 20
+    x = rng.standard_normal((max(4 * d, 16), d))
+    x[:, rng.choice(d, min(3, d), replace=False)] *= 20
     H_ex = oracle.hessian(x, "f64")
     W = (rng.standard_normal((m, d)) * 0.02).astype(np.float32)
     gp, op = params_of(synth.WORKLOADS["llama7b-attn"], bits=bits, group_size=g)
