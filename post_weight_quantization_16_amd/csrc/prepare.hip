@@ -23,6 +23,8 @@
 #include <climits>
 #include <vector>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "chol_sched.hpp"
 #include "gemm_dma.hpp"
@@ -494,30 +496,34 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
         }
     }
   }
-  // own steps
+  // own steps.  The next pivot is computed from two values read before
+  // this step's update, s_a = a[j+1][j] and s_1 = a[j+1][j+1] (every earlier
+  // step applied): l[j+1][j] = s_a·inv and the new pivot is fma(−l, l, s_1),
+  // the same operations on the same values as lane j+1's own update below,
+  // so the value is identical and the serial chain per step is rsq, mul, fma.
+  // The steps are instantiated with and without a pending batch, so the
+  // unrolled steps carry no branch and the scheduler can move each step's
+  // pivot chain ahead of the previous step's remaining updates.
+  auto own_steps = [&](auto pend) {
+    constexpr bool P = decltype(pend)::value;
+    float piv = 0.f;
 #pragma unroll
-  for (int q0 = 0; q0 < 16; ++q0) {
-    const int j = 16 * w + q0;
-    // the pending last batch meets column 0 here and column q0 + 1 below,
-    // so every column sees it exactly once, before its pivot
-    if (w > 0 && q0 == 0) {
+    for (int q0 = 0; q0 < 16; ++q0) {
+      const int j = 16 * w + q0;
+      // the pending last batch meets column 0 here and column q0 + 1 below,
+      // so every column sees it exactly once, before its pivot
+      if (q0 == 0) {
+        if (P) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float c = pc[u][q0 >> 2][q0 & 3];
-        a[q0] = fmaf(-pl[u], c, a[q0]);
-        r[q0] = fmaf(-c, px[u], r[q0]);
+          for (int u = 0; u < 4; ++u) {
+            const float c = pc[u][q0 >> 2][q0 & 3];
+            a[q0] = fmaf(-pl[u], c, a[q0]);
+            r[q0] = fmaf(-c, px[u], r[q0]);
+          }
+        }
+        piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
       }
-    }
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
-    const bool bad = !(piv > 0.f) || !(piv < INFINITY);
-    bad_j = (bad && bad_j < 0) ? j : bad_j;
-    // one hardware reciprocal square root on the serial chain (about 1 ulp)
-    const float inv = bad ? 1.f : __builtin_amdgcn_rsqf(piv);
-    const float l = lane > j ? a[q0] * inv : 0.f;
-    const float x = r[q0] * inv;
-    r[q0] = x;
-    if (q0 + 1 < 16) {   // the next column feeds the next pivot
-      if (w > 0) {
+      if (q0 + 1 < 16 && P) {   // the next column, before its pivot entry is read
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float c = pc[u][(q0 + 1) >> 2][(q0 + 1) & 3];
@@ -525,21 +531,35 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
           r[q0 + 1] = fmaf(-c, px[u], r[q0 + 1]);
         }
       }
-      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), j + 1));
-      a[q0 + 1] = fmaf(-l, c, a[q0 + 1]);
-      r[q0 + 1] = fmaf(-c, x, r[q0 + 1]);
-    }
-    PL[j * NB + lane] = l;
-    PX[j * PXS + lane] = x;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __hip_atomic_store(&flag[j], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const bool bad = !(piv > 0.f) || !(piv < INFINITY);
+      bad_j = (bad && bad_j < 0) ? j : bad_j;
+      // one hardware reciprocal square root on the serial chain (about 1 ulp)
+      const float inv = bad ? 1.f : __builtin_amdgcn_rsqf(piv);
+      const float l = lane > j ? a[q0] * inv : 0.f;
+      const float x = r[q0] * inv;
+      r[q0] = x;
+      if (q0 + 1 < 16) {   // the next column feeds the next pivot
+        const float sa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j + 1));
+        const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0 + 1]), j + 1));
+        const float c = sa * inv;   // = l at lane j + 1
+        piv = fmaf(-c, c, s1);
+        a[q0 + 1] = fmaf(-l, c, a[q0 + 1]);
+        r[q0 + 1] = fmaf(-c, x, r[q0 + 1]);
+      }
+      PL[j * NB + lane] = l;
+      PX[j * PXS + lane] = x;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __hip_atomic_store(&flag[j], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-    for (int q = q0 + 2; q < 16; ++q) {
-      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 16 * w + q));
-      a[q] = fmaf(-l, c, a[q]);
-      r[q] = fmaf(-c, x, r[q]);
+      for (int q = q0 + 2; q < 16; ++q) {
+        const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 16 * w + q));
+        a[q] = fmaf(-l, c, a[q]);
+        r[q] = fmaf(-c, x, r[q]);
+      }
     }
-  }
+  };
+  if (w > 0) own_steps(std::true_type{});
+  else own_steps(std::false_type{});
   const bool rows = R0 < d;
   if (upd && rows) {
     if (w == 0) {
