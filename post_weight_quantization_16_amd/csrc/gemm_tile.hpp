@@ -133,9 +133,11 @@ __device__ __forceinline__ void load_c(const KArgs& g, const float* C, int m0, i
 // ES), honouring the edges and the triangle mask (tri 1: lower, 2: upper).
 // All of a thread's C reads are issued before any of its writes: C is read
 // and written through one pointer, so a read placed after a write would
-// wait for that write's full round trip.  In-range tiles move float4 (a
-// float4 straddling the diagonal is written element by element); their C
-// values come in cv when the caller loaded them already (have_c).
+// wait for that write's full round trip.  In-range tiles move float4; their
+// C values come in cv when the caller loaded them already (have_c).  Where
+// the triangle crosses an in-range tile and C was read, the elements outside
+// it are stored back unchanged; with beta = 0 a float4 straddling the
+// diagonal is written element by element.
 template <int T, int ES>
 __device__ __forceinline__ void store_tile(const KArgs& g, const float* E, float* C, int m0,
                                            int n0, int t, f32x4 (&cv)[T * T / 1024],
@@ -145,6 +147,50 @@ __device__ __forceinline__ void store_tile(const KArgs& g, const float* E, float
   if (c_vec<T>(g, m0, n0)) {
     constexpr int NE = T * T / 1024;
     if (has_beta && !have_c) load_c<T>(g, C, m0, n0, t, cv);
+    // a tile the triangle mask keeps whole: straight-line float4 stores
+    // (the per-element checks below cost more than the stores themselves)
+    const bool whole = g.tri == 0 || (g.tri == 1 && n0 + T - 1 <= m0) ||
+                       (g.tri == 2 && n0 >= m0 + T - 1);
+    if (whole) {
+      const float beta = g.beta;
+      if (has_beta) {
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
+          f32x4 v = *reinterpret_cast<const f32x4*>(E + row * ES + c4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(beta, cv[u][q], v[q]);
+          *reinterpret_cast<f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4) = v;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
+          *reinterpret_cast<f32x4*>(C + (int64_t)(m0 + row) * g.ldc + n0 + c4) =
+              *reinterpret_cast<const f32x4*>(E + row * ES + c4);
+        }
+      }
+      return;
+    }
+    if (has_beta) {
+      // a tile the triangle crosses: elements outside it are written back
+      // unchanged from cv (they belong to this tile alone), so every store
+      // is a whole float4 and needs no branch
+      const float beta = g.beta;
+#pragma unroll
+      for (int u = 0; u < NE; ++u) {
+        const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(E + row * ES + c4);
+        const int gr = m0 + row, gc = n0 + c4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool keep = g.tri == 1 ? gc + q <= gr : gc + q >= gr;
+          v[q] = keep ? fmaf(beta, cv[u][q], v[q]) : cv[u][q];
+        }
+        *reinterpret_cast<f32x4*>(C + (int64_t)gr * g.ldc + gc) = v;
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
       const int idx = t + 256 * u, row = idx / (T / 4), c4 = (idx % (T / 4)) * 4;
