@@ -401,39 +401,50 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   float* G = p.G;
 
   {
-    // all loads first, then the LDS stores (a load-store pair per element
-    // would wait a memory round trip each)
-    float va[16], vb[16];
+    // all loads first, then the masks and the LDS stores (a select right
+    // after its load, or a load-store pair per element, would wait for the
+    // load at once).  Full-width panels of a 4-aligned G load float4: thread
+    // t covers rows (t >> 4) + 16u, columns 4(t & 15) .. +3.
+    if ((d & 3) == 0 && k0 + NB <= d) {
+      const int c4 = 4 * (t & 15);
+      f32x4 va[4], vb[4], vp[4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-      const bool okd = i < kb && k <= i;
-      va[u] = G[(int64_t)(k0 + (okd ? i : 0)) * d + k0 + (okd ? k : 0)];
-      va[u] = okd ? va[u] : (i == k ? 1.f : 0.f);
-      const bool okb = R0 + i < d && k < kb;
-      vb[u] = G[(okb ? R0 + i : 0) * d + (okb ? k0 + k : 0)];
-      vb[u] = okb ? vb[u] : 0.f;
-    }
-    if (upd) {
-      float vp[16];
+      for (int u = 0; u < 4; ++u) {
+        const int i = (t >> 4) + 16 * u;
+        const int64_t ra = k0 + (i < kb ? i : 0), rb = R0 + i < d ? R0 + i : 0;
+        va[u] = *reinterpret_cast<const f32x4*>(G + ra * d + k0 + c4);
+        vb[u] = *reinterpret_cast<const f32x4*>(G + rb * d + k0 + c4);
+        if (upd) vp[u] = *reinterpret_cast<const f32x4*>(G + ra * d + kp + c4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = (t >> 4) + 16 * u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = c4 + e;
+          AS[i * LS + k] = (i < kb && k <= i) ? va[u][e] : (i == k ? 1.f : 0.f);
+          BS[i * LS + k] = R0 + i < d ? vb[u][e] : 0.f;
+          if (upd) XS[i * LS + k] = i < kb ? vp[u][e] : 0.f;
+        }
+      }
+    } else {
+      float va[16], vb[16], vp[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-        const bool okp = i < kb;
-        vp[u] = G[(int64_t)(k0 + (okp ? i : 0)) * d + kp + k];
-        vp[u] = okp ? vp[u] : 0.f;
+        const bool okd = i < kb && k <= i;
+        va[u] = G[(int64_t)(k0 + (okd ? i : 0)) * d + k0 + (okd ? k : 0)];
+        const bool okb = R0 + i < d && k < kb;
+        vb[u] = G[(okb ? R0 + i : 0) * d + (okb ? k0 + k : 0)];
+        if (upd) vp[u] = G[(int64_t)(k0 + (i < kb ? i : 0)) * d + kp + k];
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-        XS[i * LS + k] = vp[u];
+        AS[i * LS + k] = (i < kb && k <= i) ? va[u] : (i == k ? 1.f : 0.f);
+        BS[i * LS + k] = (R0 + i < d && k < kb) ? vb[u] : 0.f;
+        if (upd) XS[i * LS + k] = i < kb ? vp[u] : 0.f;
       }
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-      AS[i * LS + k] = va[u];
-      BS[i * LS + k] = vb[u];
     }
   }
   __syncthreads();
