@@ -246,18 +246,6 @@ constexpr int PXS = NB + 1;      // stride of the published x rows (strip MFMA r
 constexpr int BLK = NB * LS;     // one 64x64 block in LDS (floats)
 static_assert(4 * BLK + 4 * NB <= gemm_detail::GEMM_SMEM_FLOATS, "panel LDS exceeds the shared buffer");
 
-// acc += S1 · S2ᵀ for one 32x32 tile (rows 32mi.., columns 32ni..) of two
-// 64x64 LDS blocks; v_mfma_f32_32x32x2f32 takes A(m = lane%32, k = lane/32),
-// B(k, n = lane%32), so both operands are read along their rows
-__device__ __forceinline__ void mfma_abt(const float* S1, const float* S2, int mi, int ni,
-                                         int lane, f32x16& acc) {
-#pragma unroll
-  for (int kk = 0; kk < NB / 2; ++kk) {
-    const int k = 2 * kk + (lane >> 5);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(S1[(32 * mi + (lane & 31)) * LS + k],
-                                               S2[(32 * ni + (lane & 31)) * LS + k], acc, 0, 0, 0);
-  }
-}
 // row / column of accumulator element e in the 32x32 tile (mi, ni)
 __device__ __forceinline__ int acc_row(int mi, int lane, int e) {
   return 32 * mi + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
@@ -448,27 +436,38 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     }
   }
   __syncthreads();
-  const int mi = w >> 1, ni = w & 1;
-  // the diagonal block's pre-update, lower 32x32 tiles only (wave 1's tile
-  // is above the diagonal); the rows' pre-update (E) waits for wave 0's
-  // idle time after its own steps, as only the L21 strips need it
-  if (upd && !(mi == 0 && ni == 1)) {
-    f32x16 dacc;
+  // The diagonal block's pre-update, AS −= P·Pᵀ (P = XS, the previous
+  // panel's values in this panel's rows), in 16x16 tiles (rb, s): rows
+  // 16rb.., columns 16s.., rb >= s (v_mfma_f32_16x16x4f32, A: (row lane%16,
+  // k lane/16), B: (k lane/16, column lane%16), C: rows 4·(lane/16) + v,
+  // column lane%16).  Column slab 0 is shared out over the four waves so
+  // wave 0 can start its steps after one barrier; every later wave updates
+  // its own slab afterwards, in the time it waits for the earlier waves'
+  // steps.  (What the steps publish overwrites AS and XS from their start,
+  // slab 0's rows; the later slabs lie beyond every row published before
+  // their wave has read them.)  The rows' pre-update (E) waits for wave 0's
+  // idle time after its own steps, as only the L21 strips need it.
+  auto pre_tile = [&](int rb, int sl) {
+    const int m = lane & 15, kq = lane >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dacc[e] = 0.f;
-    mfma_abt(XS, XS, mi, ni, lane, dacc);
+    for (int k4 = 0; k4 < NB; k4 += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(XS[(16 * rb + m) * LS + k4 + kq],
+                                                 XS[(16 * sl + m) * LS + k4 + kq], acc, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) AS[acc_row(mi, lane, e) * LS + 32 * ni + (lane & 31)] -= dacc[e];
-  }
+    for (int v = 0; v < 4; ++v) AS[(16 * rb + 4 * kq + v) * LS + 16 * sl + m] -= acc[v];
+  };
+  if (upd) pre_tile(w, 0);
+  if (t <= NB) flag[t] = 0;   // steps 0..63 and, at NB, "E applied"
   __syncthreads();
+  if (upd && w > 0)
+    for (int rb = w; rb < 4; ++rb) pre_tile(rb, w);
   float a[16], r[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     a[q] = AS[lane * LS + 16 * w + q];
     r[q] = (16 * w + q == lane) ? 1.f : 0.f;
   }
-  if (t <= NB) flag[t] = 0;   // steps 0..63 and, at NB, "E applied"
-  __syncthreads();   // AS is read: PL may overwrite it
 
   // consume the steps of the waves before this one, four at a time: one
   // wait on the fourth step's flag covers all four (one wave publishes them
