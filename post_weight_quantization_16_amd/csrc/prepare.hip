@@ -449,11 +449,19 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   // idle time after its own steps, as only the L21 strips need it.
   auto pre_tile = [&](int rb, int sl) {
     const int m = lane & 15, kq = lane >> 4;
+    // all 32 operands first: left to itself the compiler waits for each
+    // pair of reads before its two MFMAs (eight LDS round trips a tile)
+    float av[NB / 4], bv[NB / 4];
+#pragma unroll
+    for (int k = 0; k < NB / 4; ++k) {
+      av[k] = XS[(16 * rb + m) * LS + 4 * k + kq];
+      bv[k] = XS[(16 * sl + m) * LS + 4 * k + kq];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k4 = 0; k4 < NB; k4 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(XS[(16 * rb + m) * LS + k4 + kq],
-                                                 XS[(16 * sl + m) * LS + k4 + kq], acc, 0, 0, 0);
+    for (int k = 0; k < NB / 4; ++k)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], acc, 0, 0, 0);
 #pragma unroll
     for (int v = 0; v < 4; ++v) AS[(16 * rb + 4 * kq + v) * LS + 16 * sl + m] -= acc[v];
   };
