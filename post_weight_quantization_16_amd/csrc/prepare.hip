@@ -466,10 +466,36 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     for (int v = 0; v < 4; ++v) AS[(16 * rb + 4 * kq + v) * LS + 16 * sl + m] -= acc[v];
   };
   if (upd) pre_tile(w, 0);
-  if (t <= NB) flag[t] = 0;   // steps 0..63 and, at NB, "E applied"
+  // flags: steps 0..63; at NB "E applied"; at NB+1, NB+2 "slab 1's tile in
+  // row block 2 (3) done"
+  if (t <= NB + 2) flag[t] = 0;
   __syncthreads();
-  if (upd && w > 0)
-    for (int rb = w; rb < 4; ++rb) pre_tile(rb, w);
+  int bad_j = -1;
+  bool stalled = false;   // after one expired wait, stop waiting (the result is flagged bad)
+  if (upd && w > 0) {
+    // wave 1 is the first to need its slab and must keep up with wave 0's
+    // steps, so waves 2 and 3 take slab 1's tiles in their row blocks first
+    // and release them with a flag each; then every wave updates its own slab
+    if (w >= 2) {
+      pre_tile(w, 1);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __hip_atomic_store(&flag[NB + w - 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int rb = w; rb < 4; ++rb) pre_tile(rb, w);
+    } else {
+      pre_tile(1, 1);
+      for (int f = NB + 1; f <= NB + 2; ++f) {
+        int spin = 0;
+        while (!stalled &&
+               __hip_atomic_load(&flag[f], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+          if (++spin > kSpinLimit) {
+            stalled = true;
+            bad_j = (bad_j < 0) ? 0 : bad_j;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    }
+  }
   float a[16], r[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -481,8 +507,6 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   // wait on the fourth step's flag covers all four (one wave publishes them
   // in order, each flag a release of the writes before it); the last four
   // stay pending (pl, px, pc) and meet each column just before its pivot
-  int bad_j = -1;
-  bool stalled = false;   // after one expired wait, stop waiting (the result is flagged bad)
   float pl[4], px[4];
   f32x4 pc[4][4];
   for (int j0 = 0; j0 < 16 * w; j0 += 4) {
