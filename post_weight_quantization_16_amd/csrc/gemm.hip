@@ -22,8 +22,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs g, int nx, int ny) 
 }
 
 // Ring depth of the DMA tile: four 16-KB stages for T = 128 (two
-// workgroups per CU), six 8-KB stages for T = 64 (three per CU).
-template <int T> constexpr int kRing = T == 128 ? 4 : 6;
+// workgroups per CU), eight 8-KB stages for T = 64 (two per CU: the deeper
+// ring hides more of the load latency than a third workgroup did).
+template <int T> constexpr int kRing = T == 128 ? 4 : 8;
 
 template <int T, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(KArgs g, int nx, int ny) {
