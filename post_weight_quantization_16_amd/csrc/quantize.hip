@@ -79,9 +79,19 @@ __global__ __launch_bounds__(256) void init_kernel(const void* __restrict__ W, i
       for (int q = 0; q < 8; ++q) c[q] = a0 + q < d ? perm[a0 + q] : 0;
     }
   }
+  // the 8 mask bytes are loaded together (clamped, unconditional), then
+  // tested: a load behind each test waited for the one before it
   bool dz[8];
+  if (dead) {
+    uint8_t dv[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dz[q] = a0 + q >= d || (dead && dead[c[q]]);
+    for (int q = 0; q < 8; ++q) dv[q] = dead[a0 + q < d ? c[q] : 0];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dz[q] = a0 + q >= d || dv[q] != 0;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dz[q] = a0 + q >= d;
+  }
   // rows blockIdx.y·RB .. +RB−1 per step of the grid: every row's loads
   // are issued before the first store
   constexpr int RB = 4;
