@@ -509,16 +509,7 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   // stay pending (pl, px, pc) and meet each column just before its pivot
   float pl[4], px[4];
   f32x4 pc[4][4];
-  for (int j0 = 0; j0 < 16 * w; j0 += 4) {
-    int spin = 0;
-    while (!stalled &&
-           __hip_atomic_load(&flag[j0 + 3], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-      if (++spin > kSpinLimit) {
-        stalled = true;
-        bad_j = (bad_j < 0) ? j0 : bad_j;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
+  auto read_batch = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       pl[u] = PL[(j0 + u) * NB + lane];
@@ -526,6 +517,27 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         pc[u][h] = *reinterpret_cast<const f32x4*>(PL + (j0 + u) * NB + 16 * w + 4 * h);
+    }
+  };
+  for (int j0 = 0; j0 < 16 * w; j0 += 4) {
+    // first look: the flag and the batch are read together, without a wait
+    // between them (this wave's LDS reads complete in order, so a flag
+    // found set vouches for the reads issued after it); only a flag not yet
+    // set is waited for and the batch read again
+    const int f = __hip_atomic_load(&flag[j0 + 3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    read_batch(j0);
+    if (f == 0) {
+      int spin = 0;
+      while (!stalled &&
+             __hip_atomic_load(&flag[j0 + 3], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+        if (++spin > kSpinLimit) {
+          stalled = true;
+          bad_j = (bad_j < 0) ? j0 : bad_j;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      read_batch(j0);
     }
     if (j0 + 4 < 16 * w) {
 #pragma unroll
