@@ -30,6 +30,10 @@ section; "the pages" are the five web pages on GPTQ this path is built from):
   explicit inverse-Hessian downdate ("GPTQ: Mathematical Foundations ...":
   Lagrangian Derivation, Recursive Inverse Hessian Updating), used to pin the
   Cholesky form.
+* ``obq`` -- Optimal Brain Quantization: the same OBS step with the greedy
+  order (smallest saliency first, every row its own order), the comparator
+  for GPTQ's fixed order ("GPTQ: Mathematical Foundations ...": OBS and OBQ,
+  The Computational Bottleneck of OBQ, The GPTQ Algorithmic Innovations 1).
 * ``metrics`` -- layer output error, brute-force optimum on tiny layers, and
   the loss identity that follows from the OBS error penalty.
 
@@ -39,9 +43,11 @@ bf16) and are widened exactly.
 from .quantizer import (  # noqa: F401
     asym_params, asym_quantize, sym_params, sym_quantize, rtn_grouped,
     pack_codes, unpack_codes, bits_per_weight, Params,
+    pack_dense, unpack_dense, fp16_bits, stored_bits_per_weight,
 )
 from .hessian import hessian  # noqa: F401
 from .prepare import prepare, dead_fix, act_order_perm, inverse_cholesky_upper  # noqa: F401
 from .gptq import gptq_sweep, gptq_layer, FollowReport  # noqa: F401
 from .obs import obs_sequential  # noqa: F401
+from .obq import obq_row, obq_layer  # noqa: F401
 from .metrics import layer_error, layer_error_rows, brute_force_row, loss_identity_rhs  # noqa: F401

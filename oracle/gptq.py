@@ -62,12 +62,14 @@ class FollowReport:
     code_hard: int = 0
     zero_allowed: int = 0
     zero_hard: int = 0
+    order_allowed: int = 0      # OBQ only: adopted choices of the next column
+    order_hard: int = 0
     max_tie_dist: float = 0.0   # largest |pre-round − boundary| among adopted decisions
     hard_examples: list = dataclasses.field(default_factory=list)
 
     @property
     def ok(self) -> bool:
-        return self.code_hard == 0 and self.zero_hard == 0
+        return self.code_hard == 0 and self.zero_hard == 0 and self.order_hard == 0
 
     @property
     def frac_codes_identical(self) -> float:

@@ -155,3 +155,55 @@ def unpack_codes(words, d_in: int) -> np.ndarray:
 def bits_per_weight(bits: int, group_size: int) -> float:
     """Storage cost with a 16-bit scale and a 16-bit zero per group."""
     return bits + (16 + 16) / group_size
+
+
+def pack_dense(q, bits: int) -> np.ndarray:
+    """Dense b-bit storage ("GPTQ: Mathematical Foundations ...", Quantization
+    Formats and Group Size: b bits per weight plus the per-group metadata;
+    Inference Execution: codes packed into 32-bit words).
+
+    Each row is one little-endian bit stream: code c occupies bits
+    [c·b, c·b + b) of the row, and bit p of the stream is bit p % 32 of word
+    p // 32.  Rows are padded to whole words with zeros.  For b = 4 this is
+    the eight-per-word layout of ``pack_codes``; for b = 3, 32 codes fill
+    exactly three words (codes 10 and 21 straddle a word boundary).
+    """
+    q = np.asarray(q, dtype=np.int64)
+    if q.size and (q.min() < 0 or q.max() >= (1 << bits)):
+        raise ValueError(f"codes must lie in [0, {(1 << bits) - 1}]")
+    m, d = q.shape
+    words = (d * bits + 31) // 32
+    out = np.zeros((m, words), dtype=np.uint64)
+    for c in range(d):
+        for b in range(bits):
+            p = c * bits + b
+            bit = (q[:, c] >> b) & 1
+            out[:, p // 32] |= bit.astype(np.uint64) << np.uint64(p % 32)
+    return out.astype(np.uint32)
+
+
+def unpack_dense(words, d_in: int, bits: int) -> np.ndarray:
+    """Inverse of ``pack_dense``: uint32 [m, ceil(d·b/32)] -> codes [m, d]."""
+    words = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    m = words.shape[0]
+    out = np.zeros((m, d_in), dtype=np.int64)
+    for c in range(d_in):
+        for b in range(bits):
+            p = c * bits + b
+            out[:, c] |= ((words[:, p // 32] >> (p % 32)) & 1) << b
+    return out.astype(np.uint8)
+
+
+def fp16_bits(x) -> np.ndarray:
+    """IEEE half precision of x, rounded to nearest-even, as uint16 bits
+    (the 16-bit scale and zero of the metadata accounting)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def stored_bits_per_weight(d_in: int, bits: int, group_size: int) -> float:
+    """Bits per weight a row actually occupies in the dense export: its
+    packed words plus a 16-bit scale and a 16-bit zero per group."""
+    g = d_in if group_size in (-1, 0) or group_size >= d_in else group_size
+    n_groups = (d_in + g - 1) // g
+    words = (d_in * bits + 31) // 32
+    return (32 * words + 32 * n_groups) / d_in

@@ -132,3 +132,81 @@ def test_pack_roundtrip(rng):
 def test_bit_rate_matches_page():
     ex = _load("bit_rate.json")
     assert oracle.bits_per_weight(ex["bits"], ex["group_size"]) == ex["bits_per_weight"]
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_one_signed_group_clamps_zero_point_and_codes(bits):
+    """Group Quantization listing: zero = round(−min/scale) clamped to [0, 2ᵇ−1],
+    codes clamped to the same range; the range is the group's own min/max.
+    A group with min > 0 has −min/s < 0, so z = 0 and every value above
+    s·(2ᵇ−1) saturates at the top code; a group with max < 0 has z = 2ᵇ−1 and
+    values below saturate at code 0.  Without the zero-point clamp the codes
+    would spread over the whole grid instead."""
+    maxq = (1 << bits) - 1
+    step = 0.0078125
+    w_pos = np.array([maxq, maxq + 1.25, maxq + 3, 2 * maxq]) * step     # min = maxq·step > 0
+    s, z, zraw = asym_params(w_pos.min(), w_pos.max(), bits)
+    assert s == step and zraw == -maxq and z == 0
+    v, q, what = asym_quantize(w_pos, s, z, bits)
+    assert q.tolist() == [maxq] * 4
+    assert np.all(what == maxq * step)
+    w_neg = -w_pos[::-1]                                                # max = −maxq·step < 0
+    s, z, zraw = asym_params(w_neg.min(), w_neg.max(), bits)
+    assert s == step and zraw == 2 * maxq and z == maxq
+    _, q, what = asym_quantize(w_neg, s, z, bits)
+    assert q.tolist() == [0] * 4
+    assert np.all(what == -maxq * step)
+    # the unclamped zero-point would have placed the codes across the grid
+    _, q_free, _ = asym_quantize(w_pos, step, -maxq, bits)
+    assert q_free.tolist() != [maxq] * 4
+
+
+def test_dense_3bit_words_by_hand():
+    """Dense 3-bit storage: 32 codes in three 32-bit words, code c at bits
+    3c..3c+2 of the row's little-endian bit stream (codes 10 and 21 straddle
+    a word boundary).  Words written out by hand."""
+    def one(c, v, d=32):
+        q = np.zeros((1, d), dtype=np.uint8)
+        q[0, c] = v
+        return [int(x) for x in oracle.pack_dense(q, 3)[0]]
+    assert one(0, 5) == [0x5, 0, 0]
+    assert one(10, 1) == [0x40000000, 0, 0]
+    assert one(10, 2) == [0x80000000, 0, 0]
+    assert one(10, 4) == [0, 0x1, 0]
+    assert one(21, 5) == [0, 0x80000000, 0x2]
+    assert one(31, 7) == [0, 0, 0xE0000000]
+    assert [int(x) for x in oracle.pack_dense(np.full((1, 32), 7), 3)[0]] == [0xFFFFFFFF] * 3
+    # a ragged row is padded to whole words: 33 codes need 99 bits -> 4 words
+    assert oracle.pack_dense(np.full((2, 33), 7), 3).shape == (2, 4)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_dense_pack_roundtrip_and_4bit_layout(bits, rng):
+    for d in (1, 7, 31, 32, 33, 96, 130):
+        q = rng.integers(0, 1 << bits, size=(3, d)).astype(np.uint8)
+        w = oracle.pack_dense(q, bits)
+        assert w.shape == (3, (d * bits + 31) // 32)
+        assert np.array_equal(oracle.unpack_dense(w, d, bits), q)
+        if bits == 4:   # the nibble container is the dense 4-bit layout
+            assert np.array_equal(w, oracle.pack_codes(q))
+
+
+def test_stored_bit_rate_matches_page_accounting():
+    """b + (16 + 16)/g bits per weight ("GPTQ: Mathematical Foundations ...",
+    Quantization Formats and Group Size): 4.25 at b = 4, g = 128 (the page's
+    figure, in the golden fixture) and 3.25 at b = 3 when d fills whole
+    words, counted from the exported buffers' sizes."""
+    ex = _load("bit_rate.json")
+    assert oracle.stored_bits_per_weight(4096, ex["bits"], ex["group_size"]) == ex["bits_per_weight"]
+    assert oracle.stored_bits_per_weight(11008, 3, 128) == 3.25
+    assert oracle.stored_bits_per_weight(4096, 3, 128) == oracle.bits_per_weight(3, 128) == 3.25
+    assert oracle.stored_bits_per_weight(4096, 2, 64) == 2.5
+
+
+def test_fp16_metadata_rounding():
+    """16-bit scale and zero: IEEE half, round to nearest even (bits checked
+    against the half-precision encoding written out by hand)."""
+    assert oracle.fp16_bits([1.0, -2.0, 0.5, 65504.0, 7.0]).tolist() == [0x3C00, 0xC000, 0x3800, 0x7BFF, 0x4700]
+    # 1 + 2^-11 is halfway between 1 and 1 + 2^-10: ties to even (1.0)
+    assert int(oracle.fp16_bits(1.0 + 2.0 ** -11)) == 0x3C00
+    assert int(oracle.fp16_bits(1.0 + 3 * 2.0 ** -11)) == 0x3C02
