@@ -28,19 +28,36 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work_figures(m, d, n_tok, B=128):
+def work_figures(m, d, n_tok, B=128, g=128, w_bytes=2, x_bytes=2):
     """Algorithmic work of each stage (flops / bytes), as defined for the roofline."""
     upd = 0
     for b0 in range(0, d, B):
         b1 = min(b0 + B, d)
         upd += 2 * m * (b1 - b0) * (d - b1)
+    ng = (d + g - 1) // g
     return {
         "hessian_flop": d * (d + 1) * n_tok,               # SYRK: upper triangle only
-        "hessian_bytes": 2 * n_tok * d + 4 * d * d,        # read X (bf16) once, write H
+        "hessian_bytes": x_bytes * n_tok * d + 4 * d * d,  # read X once, write H
         "prepare_flop": 2 * d ** 3 // 3,                   # Cholesky + triangular inverse
         "update_flop": upd,                                # lazy block updates
         "sweep_flop": m * d * (B - 1),                     # in-block rank-1 updates
+        # the whole layer's compulsory traffic: X and W read once; H written
+        # and read, U written and read; codes (4-bit), Ŵ (fp32), scales and
+        # zeros written
+        "layer_bytes": (x_bytes * n_tok * d + w_bytes * m * d + 4 * 4 * d * d
+                        + m * d // 2 + 4 * m * d + 5 * m * ng),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # HBM bytes per gptq_hessian_accumulate call on the 4096x4096, 131072-token
@@ -83,7 +100,9 @@ def copy_calibration(mib):
 
 
 def cpu_baseline(wl, W, X, tok_sample, row_sample):
-    """Time the fp64 oracle as it stands on a bounded sample and scale to one layer."""
+    """Time the fp64 oracle as it stands on the host cores: the whole layer
+    (every token, every row) unless a smaller sample is asked for, in which
+    case the measured stages are scaled to one layer and the line says so."""
     import numpy as np
     import oracle
     try:
@@ -108,16 +127,25 @@ def cpu_baseline(wl, W, X, tok_sample, row_sample):
     oracle.gptq_sweep(Wr, prep["U"], p)
     t_s = time.perf_counter() - t0
     total = t_h * wl.n_tok / tok_sample + t_p + t_s * wl.d_out / row_sample
+    whole = tok_sample == wl.n_tok and row_sample == wl.d_out
+    if whole:
+        sample = (f"fp64 oracle over the whole layer: H over all {wl.n_tok} tokens ({t_h:.2f}s), "
+                  f"prepare ({t_p:.2f}s), sweep of all {wl.d_out} rows ({t_s:.2f}s); "
+                  f"{total:.1f}s per layer")
+    else:
+        sample = (f"fp64 oracle: H over {tok_sample} of {wl.n_tok} tokens ({t_h:.2f}s, scaled x"
+                  f"{wl.n_tok / tok_sample:g}), full prepare ({t_p:.2f}s), sweep of {row_sample} of "
+                  f"{wl.d_out} rows ({t_s:.2f}s, scaled x{wl.d_out / row_sample:g}); "
+                  f"extrapolated {total:.1f}s per layer")
     return {
         "value": wl.d_out * wl.d_in / total,
         "unit": "weights/s",
         "cores": int(cores),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": (f"fp64 oracle: H over {tok_sample} of {wl.n_tok} tokens ({t_h:.2f}s, scaled x"
-                   f"{wl.n_tok / tok_sample:g}), full prepare ({t_p:.2f}s), sweep of {row_sample} of "
-                   f"{wl.d_out} rows ({t_s:.2f}s, scaled x{wl.d_out / row_sample:g}); "
-                   f"extrapolated {total:.1f}s per layer"),
+        "sample": sample,
         "ms_per_layer": total * 1e3,
+        "stage_s": {"hessian": t_h, "prepare": t_p, "sweep": t_s},
     }
 
 
@@ -128,8 +156,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b-attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: all)")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle row sample (0: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -196,10 +224,21 @@ def main():
     st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                    for e in evs])
     h_ms, p_ms, q_ms = (float(x) for x in st.mean(axis=0))
-    wf = work_figures(m, d, N)
+    wf = work_figures(m, d, N, g=wl.group_size if wl.group_size > 0 else d,
+                      w_bytes=2 if wl.w_dtype == "bf16" else 4, x_bytes=2 if wl.x_dtype == "bf16" else 4)
+    # one more step with the library's per-stage event timing (outside the
+    # timed steps): the block-update products, sweeps, Cholesky and inverse
+    gq.timing(True)
+    step()
+    torch.cuda.synchronize()
+    stage = gq.timing_read()
+    gq.timing(False)
+    log("bench: timed stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
     log(f"bench: {ms_step:.3f} ms/step; hessian {h_ms:.3f} ms, prepare {p_ms:.3f} ms, "
         f"quantize {q_ms:.3f} ms")
     h_tflops = wf["hessian_flop"] / (h_ms * 1e-3) / 1e12
+    upd_tflops = wf["update_flop"] / (stage["block_update"] * 1e-3) / 1e12 if stage["block_update"] else None
+    hbm_gbs = wf["layer_bytes"] / (ms_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": m * d / (ms_step * 1e-3),
@@ -215,11 +254,30 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, **{k: v for k, v in wl.describe().items() if k != "workload"}},
         "stages_ms": {"hessian": h_ms, "prepare": p_ms, "quantize": q_ms},
+        "timed_stages_ms": stage,
         "stage_rates": {
             "hessian_tflops": h_tflops,
             "hessian_frac_bf16_peak": h_tflops / PEAK_BF16_TFLOPS,
             "prepare_tflops": wf["prepare_flop"] / (p_ms * 1e-3) / 1e12,
-            "quantize_update_tflops": wf["update_flop"] / (q_ms * 1e-3) / 1e12,
+            "block_update_tflops": upd_tflops,
+            "block_update_frac_fp32_peak": upd_tflops / PEAK_FP32_TFLOPS if upd_tflops else None,
+        },
+        "roofline_block_update": {
+            "kernel": "lazy block-update products inside gptq_quantize_layer (fp32 MFMA)",
+            "bound": "mfma",
+            "achieved": upd_tflops,
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": upd_tflops / PEAK_FP32_TFLOPS if upd_tflops else None,
+            "flop_per_layer": wf["update_flop"],
+            "ms_per_layer": stage["block_update"],
+        },
+        "hbm_end_to_end": {
+            "algorithmic_bytes": wf["layer_bytes"],
+            "achieved": hbm_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": hbm_gbs / PEAK_HBM_GBS,
         },
         "roofline": {
             "kernel": "gptq_hessian_accumulate (syrk256_kernel + reduce_mirror_kernel)",
@@ -233,8 +291,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host ...")
-        result["cpu_baseline"] = cpu_baseline(wl, W_host, X_host, min(args.cpu_tokens, N),
-                                              min(args.cpu_rows, m))
+        result["cpu_baseline"] = cpu_baseline(wl, W_host, X_host,
+                                              min(args.cpu_tokens, N) if args.cpu_tokens else N,
+                                              min(args.cpu_rows, m) if args.cpu_rows else m)
     print(json.dumps(result), flush=True)
 
 

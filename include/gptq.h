@@ -54,7 +54,9 @@ typedef enum {
   GPTQ_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. g/B mismatch)  */
   GPTQ_ERR_NOT_SPD = -3,      /* damped Hessian not positive definite           */
   GPTQ_ERR_WORKSPACE = -4,    /* workspace null or smaller than required        */
-  GPTQ_ERR_HIP = -5           /* a HIP runtime call failed                      */
+  GPTQ_ERR_HIP = -5,          /* a HIP runtime call failed                      */
+  GPTQ_ERR_INTERNAL = -6      /* a kernel's bounded internal wait ran out: the
+                                 outputs are undefined (a library fault)        */
 } gptq_status;
 
 typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
@@ -84,7 +86,7 @@ typedef struct {
 
 typedef void* gptq_stream;
 
-enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2 };
+enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2, GPTQ_WS_OBQ = 3 };
 
 /* Workspace size in bytes that call `which` (GPTQ_WS_*) needs for the given
  * shape.  n_tok is used by the Hessian call only; p may be NULL for it.
@@ -125,7 +127,10 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
  *  ws         workspace of gptq_workspace_bytes(GPTQ_WS_PREPARE, 0, d_in, 0, p).
  * SYNCHRONIZES `stream` before returning (it reads back the factorization
  * status).  On GPTQ_ERR_NOT_SPD, U is undefined; a larger percdamp is the
- * usual remedy ("GPTQ" card, Implementation pitfalls). */
+ * usual remedy ("GPTQ" card, Implementation pitfalls).  GPTQ_ERR_INTERNAL
+ * means a wave of the factorization gave up waiting for another wave (every
+ * such wait is bounded, so the call never hangs); U and H are then
+ * undefined. */
 int gptq_prepare_hinv(float* H, int64_t d_in, const gptq_params* p, float* U,
                       int32_t* perm, uint8_t* dead_mask, void* ws, size_t ws_bytes,
                       int64_t* info, gptq_stream stream);
@@ -158,6 +163,99 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
                         const gptq_params* p, uint32_t* qweight, float* scales,
                         uint8_t* zeros, float* W_hat, int32_t* g_idx, float* row_loss,
                         void* ws, size_t ws_bytes, gptq_stream stream);
+
+/* One layer of gptq_quantize_layers: its weights and its outputs, with the
+ * meaning, layout and NULL rules of the gptq_quantize_layer arguments of the
+ * same names. */
+typedef struct {
+  const void* W;       /* [d_out x d_in] of w_dtype, row stride ld_w          */
+  int32_t w_dtype;     /* GPTQ_F32 / GPTQ_BF16 / GPTQ_F16                     */
+  int32_t reserved;    /* 0                                                   */
+  int64_t d_out;
+  int64_t ld_w;
+  uint32_t* qweight;   /* out, packed codes                                   */
+  float* scales;       /* out [d_out x n_groups]                              */
+  uint8_t* zeros;      /* out [d_out x n_groups]                              */
+  float* W_hat;        /* out [d_out x d_in] or NULL                          */
+  float* row_loss;     /* out [d_out] or NULL                                 */
+} gptq_layer;
+
+/* Several layers quantized against one prepared factor ("Foundations",
+ * Second-Order Taylor Expansion and the Hessian: H depends only on the
+ * layer's inputs, so layers fed the same X -- e.g. the query, key and value
+ * projections -- share H, U and the column order; The Layer-Wise
+ * Reconstruction Problem: rows are independent problems).  The layers' rows
+ * are stacked and swept together, which fills the GPU better than one small
+ * layer at a time; every output equals, bit for bit, what gptq_quantize_layer
+ * gives for that layer alone.
+ *  layers     host array of n_layers (1..1024) descriptors; all share d_in.
+ *  U, perm, dead_mask, p   as for gptq_quantize_layer.
+ *  g_idx      out [d_in] (the same for every layer); may be NULL.
+ *  ws         workspace of gptq_workspace_bytes(GPTQ_WS_QUANTIZE, Σ d_out, d_in, 0, p).
+ * Asynchronous; argument errors only. */
+int gptq_quantize_layers(int n_layers, const gptq_layer* layers, int64_t d_in, const float* U,
+                         const int32_t* perm, const uint8_t* dead_mask, const gptq_params* p,
+                         int32_t* g_idx, void* ws, size_t ws_bytes, gptq_stream stream);
+
+/* Optimal Brain Quantization, the greedy-order comparator for GPTQ's fixed
+ * order on tiny layers ("Foundations": Optimal Brain Surgeon (OBS) and
+ * Optimal Brain Quantization (OBQ), Lagrangian Derivation, Minimal Error
+ * Penalty, Recursive Inverse Hessian Updating, The Computational Bottleneck
+ * of OBQ; The GPTQ Algorithmic Innovations §1).  Every row runs its own
+ * greedy sequence: quantize the free column with the smallest saliency
+ * ΔE_c = (w_c − quant(w_c))²/(2·[H_F⁻¹]_cc) (the lower index on ties),
+ * compensate the free columns with the OBS update, downdate H_F⁻¹.  quant()
+ * is one grid per row from the row's dead-fixed weights (asymmetric min/max,
+ * or symmetric).  fp64 throughout; O(d_in³) per row.
+ *  W          [d_out x d_in] of w_dtype, row stride ld_w; d_in <= 128
+ *             (larger returns GPTQ_ERR_UNSUPPORTED).
+ *  H          [d_in x d_in] fp32 accumulated Hessian (not modified); the
+ *             call applies the dead fix and p->percdamp damping itself.
+ *  p          bits, percdamp, sym; group_size must be -1 (one grid per row)
+ *             and act_order 0.
+ *  qweight, scales [d_out x 1], zeros [d_out x 1], W_hat, row_loss: as for
+ *             gptq_quantize_layer (row_loss = Σ ΔE along the row's steps).
+ *  order      out [d_out x d_in] int32: the column quantized at each step;
+ *             may be NULL.
+ *  ws         workspace of gptq_workspace_bytes(GPTQ_WS_OBQ, d_out, d_in, 0, p).
+ * SYNCHRONIZES `stream` (it reads back whether H_d was positive definite:
+ * GPTQ_ERR_NOT_SPD otherwise, with the outputs undefined). */
+int gptq_obq_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
+                   const float* H, const gptq_params* p, uint32_t* qweight, float* scales,
+                   uint8_t* zeros, float* W_hat, int32_t* order, float* row_loss, void* ws,
+                   size_t ws_bytes, gptq_stream stream);
+
+/* Storage export of a quantized layer ("Foundations", Quantization Formats
+ * and Group Size: b bits per weight plus a 16-bit scale and a 16-bit zero per
+ * group, b + 32/g bits in all; Inference Execution: codes packed into 32-bit
+ * words).  Reads the outputs of gptq_quantize_layer and writes
+ *  qweight_dense  [d_out x ceil(d_in·bits/32)] uint32: each row one
+ *                 little-endian bit stream, the code of original column c in
+ *                 bits [c·bits, c·bits + bits) (bit p in bit p%32 of word
+ *                 p/32; the row padded with zero bits).  For bits 4 and 8
+ *                 this is the layout qweight already has; for bits 3, 32
+ *                 codes fill three words; for bits 2, sixteen fill one.
+ *  scales_f16     [d_out x n_groups] IEEE half of the fp32 scales, rounded to
+ *                 nearest even (scales above 65504 become infinity).
+ *  zeros_f16      [d_out x n_groups] IEEE half of the zero-points (exact).
+ * Any output may be NULL; its input may then be NULL too.  n_groups is the
+ * group count of the quantize call (1 for one group per row).  The inputs
+ * stay as they are.  Asynchronous; argument errors only. */
+int gptq_export(int bits, int64_t d_out, int64_t d_in, int64_t n_groups, const uint32_t* qweight,
+                const float* scales, const uint8_t* zeros, uint32_t* qweight_dense,
+                uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream);
+
+/* Per-stage timing, for measurement only.  gptq_timing(1) clears what was
+ * recorded and starts bracketing, on the caller's stream, the launches of
+ * each timed stage with a pair of HIP events; gptq_timing(0) stops.
+ * gptq_timing_read() waits for the recorded events, writes the summed
+ * milliseconds per stage to ms[0..n-1] (host) and clears the record:
+ *   0 lazy block updates (the products W[:, later] −= Err·U[block, later]),
+ *   1 in-block sweeps, 2 blocked Cholesky (panels and trailing updates),
+ *   3 triangular inverse, 4 Hessian accumulation.
+ * Timing is process-wide; enable it only while one thread issues calls. */
+int gptq_timing(int enable);
+int gptq_timing_read(float* ms, int n);
 
 /* Message for the last non-zero status on the calling thread (never NULL). */
 const char* gptq_last_error(void);

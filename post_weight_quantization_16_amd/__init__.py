@@ -21,6 +21,7 @@ from . import _native
 __all__ = [
     "GPTQParams", "GPTQError", "NotPositiveDefinite", "hessian_accumulate", "prepare_hinv",
     "quantize_layer", "quantize", "workspace_bytes", "version", "Prepared", "Quantized",
+    "Exported", "export", "quantize_layers", "obq_layer", "timing", "timing_read",
 ]
 
 
@@ -86,8 +87,29 @@ def _dtype_code(t) -> int:
     torch = _torch()
     m = {torch.float32: _native.F32, torch.bfloat16: _native.BF16, torch.float16: _native.F16}
     if t.dtype not in m:
-        raise TypeError(f"unsupported dtype {t.dtype}")
+        raise ValueError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
     return m[t.dtype]
+
+
+def _require(t, name, dtype, shape, device=None):
+    """Dense tensor of the given dtype and shape (on `device` when given):
+    the library reads and writes it as a plain row-major buffer."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _matrix_rows(t, name):
+    """2-D with unit column stride (rows may be padded: the row stride is passed)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1) or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
 
 
 def _dev(t, name):
@@ -96,6 +118,14 @@ def _dev(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws_check(ws, device):
+    torch = _torch()
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("a workspace must be a contiguous uint8 tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
 
 
 def _stream(device):
@@ -120,13 +150,16 @@ def workspace_bytes(which: int, d_out: int, d_in: int, n_tok: int = 0,
 
 def hessian_accumulate(H, X, ws=None):
     """H += 2·XᵀX (X token-major [n_tok, d_in]; row stride X.stride(0))."""
-    L = _native.lib()
-    if X.dim() != 2 or X.stride(1) != 1:
-        raise ValueError("X must be 2-D with unit column stride")
+    torch = _torch()
+    _matrix_rows(X, "X")
     n_tok, d = X.shape
+    xdt = _dtype_code(X)
+    _require(H, "H", torch.float32, (d, d), X.device)
+    L = _native.lib()
     if ws is None:
         ws = _workspace(L.gptq_workspace_bytes(_native.WS_HESSIAN, 0, d, n_tok, None), X.device)
-    _check(L.gptq_hessian_accumulate(_dev(H, "H"), d, _dev(X, "X"), _dtype_code(X), n_tok,
+    _ws_check(ws, X.device)
+    _check(L.gptq_hessian_accumulate(_dev(H, "H"), d, _dev(X, "X"), xdt, n_tok,
                                      X.stride(0), _dev(ws, "ws"), ws.numel(), _stream(X.device)))
     return H
 
@@ -134,8 +167,11 @@ def hessian_accumulate(H, X, ws=None):
 def prepare_hinv(H, params: GPTQParams, ws=None) -> Prepared:
     """Dead fix, damping, act-order and U (H is overwritten with H_d)."""
     torch = _torch()
-    L = _native.lib()
+    if H.dim() != 2:
+        raise ValueError("H must be a square matrix")
     d = H.shape[0]
+    _require(H, "H", torch.float32, (d, d))
+    L = _native.lib()
     p = params.c()
     dev = H.device
     U = torch.empty(d, d, dtype=torch.float32, device=dev)
@@ -143,6 +179,7 @@ def prepare_hinv(H, params: GPTQParams, ws=None) -> Prepared:
     dead = torch.empty(d, dtype=torch.uint8, device=dev)
     if ws is None:
         ws = _workspace(L.gptq_workspace_bytes(_native.WS_PREPARE, 0, d, 0, ctypes.byref(p)), dev)
+    _ws_check(ws, dev)
     info = ctypes.c_int64(-1)
     rc = L.gptq_prepare_hinv(_dev(H, "H"), d, ctypes.byref(p), _dev(U, "U"), _dev(perm, "perm"),
                              _dev(dead, "dead"), _dev(ws, "ws"), ws.numel(), ctypes.byref(info),
@@ -157,11 +194,18 @@ def quantize_layer(W, prep: Prepared, params: GPTQParams, want_what: bool = True
                    ws=None) -> Quantized:
     """Run the sweep on W [d_out, d_in] with the factor from prepare_hinv."""
     torch = _torch()
-    L = _native.lib()
-    if W.dim() != 2 or W.stride(1) != 1:
-        raise ValueError("W must be 2-D with unit column stride")
+    _matrix_rows(W, "W")
     m, d = W.shape
+    wdt = _dtype_code(W)
     dev = W.device
+    _require(prep.U, "U", torch.float32, (d, d), dev)
+    if params.act_order and prep.natural:
+        raise ValueError("act_order needs a Prepared from prepare_hinv with act_order")
+    if not prep.natural:
+        _require(prep.perm, "perm", torch.int32, (d,), dev)
+    if prep.dead is not None:
+        _require(prep.dead, "dead", torch.uint8, (d,), dev)
+    L = _native.lib()
     p = params.c()
     cpw = 8 if params.bits <= 4 else 4
     ng = params.n_groups(d)
@@ -173,13 +217,140 @@ def quantize_layer(W, prep: Prepared, params: GPTQParams, want_what: bool = True
     row_loss = torch.empty(m, dtype=torch.float32, device=dev)
     if ws is None:
         ws = _workspace(L.gptq_workspace_bytes(_native.WS_QUANTIZE, m, d, 0, ctypes.byref(p)), dev)
+    _ws_check(ws, dev)
     _check(L.gptq_quantize_layer(
-        _dev(W, "W"), _dtype_code(W), m, d, W.stride(0), _dev(prep.U, "U"),
+        _dev(W, "W"), wdt, m, d, W.stride(0), _dev(prep.U, "U"),
         None if prep.natural else _dev(prep.perm, "perm"),
         _dev(prep.dead, "dead"), ctypes.byref(p), _dev(qweight, "qweight"), _dev(scales, "scales"),
         _dev(zeros, "zeros"), _dev(W_hat, "W_hat"), _dev(g_idx, "g_idx"), _dev(row_loss, "row_loss"),
         _dev(ws, "ws"), ws.numel(), _stream(dev)))
     return Quantized(qweight, scales, zeros, W_hat, g_idx, row_loss)
+
+
+def quantize_layers(Ws, prep: Prepared, params: GPTQParams, want_what: bool = True,
+                    ws=None) -> list:
+    """Several layers with the same inputs (one H, one factor): one Quantized
+    per W, bitwise what quantize_layer gives for each alone."""
+    torch = _torch()
+    if not Ws:
+        raise ValueError("no layers")
+    d = Ws[0].shape[1]
+    dev = Ws[0].device
+    _require(prep.U, "U", torch.float32, (d, d), dev)
+    if params.act_order and prep.natural:
+        raise ValueError("act_order needs a Prepared from prepare_hinv with act_order")
+    if not prep.natural:
+        _require(prep.perm, "perm", torch.int32, (d,), dev)
+    if prep.dead is not None:
+        _require(prep.dead, "dead", torch.uint8, (d,), dev)
+    p = params.c()
+    cpw = 8 if params.bits <= 4 else 4
+    ng = params.n_groups(d)
+    outs, descs = [], (_native.Layer * len(Ws))()
+    for i, W in enumerate(Ws):
+        _matrix_rows(W, f"W[{i}]")
+        if W.shape[1] != d or W.device != dev:
+            raise ValueError(f"W[{i}] must have {d} columns and live on {dev}")
+        m = W.shape[0]
+        o = Quantized(torch.empty(m, (d + cpw - 1) // cpw, dtype=torch.int32, device=dev),
+                      torch.empty(m, ng, dtype=torch.float32, device=dev),
+                      torch.empty(m, ng, dtype=torch.uint8, device=dev),
+                      torch.empty(m, d, dtype=torch.float32, device=dev) if want_what else None,
+                      None, torch.empty(m, dtype=torch.float32, device=dev))
+        outs.append(o)
+        descs[i] = _native.Layer(_dev(W, "W"), _dtype_code(W), 0, m, W.stride(0),
+                                 _dev(o.qweight, "qweight"), _dev(o.scales, "scales"),
+                                 _dev(o.zeros, "zeros"), _dev(o.W_hat, "W_hat"),
+                                 _dev(o.row_loss, "row_loss"))
+    g_idx = torch.empty(d, dtype=torch.int32, device=dev)
+    L = _native.lib()
+    total = sum(W.shape[0] for W in Ws)
+    if ws is None:
+        ws = _workspace(L.gptq_workspace_bytes(_native.WS_QUANTIZE, total, d, 0, ctypes.byref(p)), dev)
+    _ws_check(ws, dev)
+    _check(L.gptq_quantize_layers(len(Ws), descs, d, _dev(prep.U, "U"),
+                                  None if prep.natural else _dev(prep.perm, "perm"),
+                                  _dev(prep.dead, "dead"), ctypes.byref(p), _dev(g_idx, "g_idx"),
+                                  _dev(ws, "ws"), ws.numel(), _stream(dev)))
+    for o in outs:
+        o.g_idx = g_idx
+    return outs
+
+
+def obq_layer(W, H, params: GPTQParams, ws=None):
+    """OBQ (greedy order per row) of a tiny layer against the fp32 Hessian H.
+
+    Returns (Quantized, order [d_out, d_in] int32).  params.group_size must
+    be -1 (one grid per row) and act_order False; d_in <= 128.
+    """
+    torch = _torch()
+    _matrix_rows(W, "W")
+    m, d = W.shape
+    wdt = _dtype_code(W)
+    dev = W.device
+    _require(H, "H", torch.float32, (d, d), dev)
+    p = params.c()
+    cpw = 8 if params.bits <= 4 else 4
+    qweight = torch.empty(m, (d + cpw - 1) // cpw, dtype=torch.int32, device=dev)
+    scales = torch.empty(m, 1, dtype=torch.float32, device=dev)
+    zeros = torch.empty(m, 1, dtype=torch.uint8, device=dev)
+    W_hat = torch.empty(m, d, dtype=torch.float32, device=dev)
+    order = torch.empty(m, d, dtype=torch.int32, device=dev)
+    row_loss = torch.empty(m, dtype=torch.float32, device=dev)
+    L = _native.lib()
+    if ws is None:
+        ws = _workspace(L.gptq_workspace_bytes(_native.WS_OBQ, m, d, 0, ctypes.byref(p)), dev)
+    _ws_check(ws, dev)
+    rc = L.gptq_obq_layer(_dev(W, "W"), wdt, m, d, W.stride(0), _dev(H, "H"), ctypes.byref(p),
+                          _dev(qweight, "qweight"), _dev(scales, "scales"), _dev(zeros, "zeros"),
+                          _dev(W_hat, "W_hat"), _dev(order, "order"), _dev(row_loss, "row_loss"),
+                          _dev(ws, "ws"), ws.numel(), _stream(dev))
+    if rc == _native.ERR_NOT_SPD:
+        raise NotPositiveDefinite(rc, _native.last_error(), -1)
+    _check(rc)
+    return Quantized(qweight, scales, zeros, W_hat, None, row_loss), order
+
+
+TIMED_STAGES = ("block_update", "sweep", "cholesky", "inverse", "hessian")
+
+
+def timing(enable: bool) -> None:
+    """Start (clearing earlier records) or stop per-stage event timing."""
+    _native.lib().gptq_timing(1 if enable else 0)
+
+
+def timing_read() -> dict:
+    """Milliseconds per timed stage since timing was enabled (or last read)."""
+    buf = (ctypes.c_float * len(TIMED_STAGES))()
+    _check(_native.lib().gptq_timing_read(buf, len(TIMED_STAGES)))
+    return {k: float(v) for k, v in zip(TIMED_STAGES, buf)}
+
+
+@dataclasses.dataclass
+class Exported:
+    qweight: "object"     # [d_out, ceil(d_in·bits/32)] int32, dense little-endian bit stream per row
+    scales_f16: "object"  # [d_out, n_groups] float16
+    zeros_f16: "object"   # [d_out, n_groups] float16
+
+
+def export(q: Quantized, params: GPTQParams, d_in: int) -> Exported:
+    """Dense b-bit codes and 16-bit scales/zeros from a quantize_layer result."""
+    torch = _torch()
+    m = q.scales.shape[0]
+    ng = q.scales.shape[1]
+    dev = q.scales.device
+    cpw = 8 if params.bits <= 4 else 4
+    _require(q.qweight, "qweight", torch.int32, (m, (d_in + cpw - 1) // cpw), dev)
+    _require(q.scales, "scales", torch.float32, (m, ng), dev)
+    _require(q.zeros, "zeros", torch.uint8, (m, ng), dev)
+    qd = torch.empty(m, (d_in * params.bits + 31) // 32, dtype=torch.int32, device=dev)
+    s16 = torch.empty(m, ng, dtype=torch.float16, device=dev)
+    z16 = torch.empty(m, ng, dtype=torch.float16, device=dev)
+    _check(_native.lib().gptq_export(params.bits, m, d_in, ng, _dev(q.qweight, "qweight"),
+                                     _dev(q.scales, "scales"), _dev(q.zeros, "zeros"),
+                                     _dev(qd, "qweight_dense"), _dev(s16, "scales_f16"),
+                                     _dev(z16, "zeros_f16"), _stream(dev)))
+    return Exported(qd, s16, z16)
 
 
 def quantize(W, X, params: GPTQParams = GPTQParams()):

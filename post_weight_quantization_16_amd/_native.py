@@ -11,17 +11,22 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi355x.so")
 
 # gptq_status
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NOT_SPD, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NOT_SPD, ERR_WORKSPACE, ERR_HIP, ERR_INTERNAL = 0, -1, -2, -3, -4, -5, -6
 # gptq_dtype
 F32, BF16, F16 = 0, 1, 2
 # workspace kinds
-WS_HESSIAN, WS_PREPARE, WS_QUANTIZE = 0, 1, 2
+WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ = 0, 1, 2, 3
 
 EXPORTS = (
     "gptq_workspace_bytes",
     "gptq_hessian_accumulate",
     "gptq_prepare_hinv",
     "gptq_quantize_layer",
+    "gptq_quantize_layers",
+    "gptq_obq_layer",
+    "gptq_export",
+    "gptq_timing",
+    "gptq_timing_read",
     "gptq_last_error",
     "gptq_version",
 )
@@ -37,6 +42,23 @@ class Params(ctypes.Structure):
         ("percdamp", ctypes.c_float),
         ("act_order", ctypes.c_int32),
         ("sym", ctypes.c_int32),
+    ]
+
+
+class Layer(ctypes.Structure):
+    """Mirror of ``gptq_layer``."""
+
+    _fields_ = [
+        ("W", ctypes.c_void_p),
+        ("w_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("d_out", ctypes.c_int64),
+        ("ld_w", ctypes.c_int64),
+        ("qweight", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("zeros", ctypes.c_void_p),
+        ("W_hat", ctypes.c_void_p),
+        ("row_loss", ctypes.c_void_p),
     ]
 
 
@@ -66,6 +88,18 @@ def lib() -> ctypes.CDLL:
     L.gptq_quantize_layer.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _pp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     L.gptq_quantize_layer.restype = _int
+    L.gptq_quantize_layers.argtypes = [_int, ctypes.POINTER(Layer), _i64, _vp, _vp, _vp, _pp, _vp,
+                                       _vp, _sz, _vp]
+    L.gptq_quantize_layers.restype = _int
+    L.gptq_obq_layer.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _pp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _sz, _vp]
+    L.gptq_obq_layer.restype = _int
+    L.gptq_export.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.gptq_export.restype = _int
+    L.gptq_timing.argtypes = [_int]
+    L.gptq_timing.restype = _int
+    L.gptq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), _int]
+    L.gptq_timing_read.restype = _int
     L.gptq_last_error.argtypes = []
     L.gptq_last_error.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []

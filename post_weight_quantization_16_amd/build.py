@@ -27,6 +27,9 @@ SOURCES = [
     ("hessian.hip", "hessian.o", []),
     ("prepare.hip", "prepare.o", []),
     ("quantize.hip", "quantize.o", []),
+    ("export.hip", "export.o", []),
+    ("obq.hip", "obq.o", []),
+    ("timing.hip", "timing.o", []),
 ] + [("sweep.hip", f"sweep_g{g}.o", [f"-DGQ_SWEEP_G={g}"]) for g in (0, 32, 64, 128)]
 
 FLAGS = [

@@ -6,8 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "common.hpp"
+#include "status_map.hpp"
 
 namespace {
 
@@ -91,6 +93,9 @@ size_t gptq_workspace_bytes(int which, int64_t d_out, int64_t d_in, int64_t n_to
       if (d_out <= 0 || d_out > kMaxDout) return 0;
       (void)p;
       return gq::quantize_ws_bytes(d_out, d_in);
+    case GPTQ_WS_OBQ:
+      if (d_in > gq::obq_max_din()) return 0;
+      return gq::obq_ws_bytes(d_in);
     default:
       return 0;
   }
@@ -110,7 +115,11 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, 
                                (long long)d_in);
   int rc = check_ws(ws, ws_bytes, gq::hessian_ws_bytes(d_in, n_tok), "hessian_accumulate");
   if (rc) return rc;
-  hipError_t e = gq::hessian_launch(H, d_in, X, x_dtype, n_tok, ld_x, ws, (hipStream_t)stream);
+  hipError_t e;
+  {
+    gq::TimerScope ts(gq::kTimerHessian, (hipStream_t)stream);
+    e = gq::hessian_launch(H, d_in, X, x_dtype, n_tok, ld_x, ws, ws_bytes, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return hip_fail("hessian_accumulate", e);
   return GPTQ_OK;
 }
@@ -132,18 +141,22 @@ int gptq_prepare_hinv(float* H, int64_t d_in, const gptq_params* p, float* U, in
   hipError_t e = gq::prepare_launch(H, d_in, p->percdamp, p->act_order, U, perm, dead_mask, ws,
                                     &status_dev, s);
   if (e != hipSuccess) return hip_fail("prepare_hinv", e);
-  int32_t st = 0;
-  e = hipMemcpyAsync(&st, status_dev, sizeof st, hipMemcpyDeviceToHost, s);
+  int32_t st[2] = {0, 0};   // failing pivot (or INT_MAX), stall flag
+  e = hipMemcpyAsync(st, status_dev, sizeof st, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail("prepare_hinv (status read-back)", e);
-  if (st != INT_MAX) {
-    const int64_t piv = d_in - 1 - (int64_t)st;
-    if (info) *info = piv;
+  int64_t piv = -1;
+  rc = gq::prepare_status(st[0], st[1], d_in, &piv);
+  if (info) *info = piv;
+  if (rc == GPTQ_ERR_NOT_SPD)
     return fail(GPTQ_ERR_NOT_SPD,
                 "damped Hessian is not positive definite (pivot %lld of the quantization order); "
                 "raise percdamp",
                 (long long)piv);
-  }
+  if (rc != GPTQ_OK)
+    return fail(rc, "prepare_hinv: a factorization wave ran out of its bounded wait for "
+                    "another wave (status words %d, %d); the outputs are undefined",
+                (int)st[0], (int)st[1]);
   return GPTQ_OK;
 }
 
@@ -162,12 +175,121 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
   if (ld_w < d_in) return fail(GPTQ_ERR_INVALID_ARG, "ld_w < d_in");
   int rc = check_params(p, d_in);
   if (rc) return rc;
+  if (p->act_order && !perm)
+    return fail(GPTQ_ERR_INVALID_ARG,
+                "act_order needs the perm from gptq_prepare_hinv (U is in that order)");
   rc = check_ws(ws, ws_bytes, gq::quantize_ws_bytes(d_out, d_in), "quantize_layer");
   if (rc) return rc;
   hipError_t e = gq::quantize_launch(W, w_dtype, d_out, d_in, ld_w, U, perm, dead_mask, *p,
                                      qweight, scales, zeros, W_hat, g_idx, row_loss, ws,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("quantize_layer", e);
+  return GPTQ_OK;
+}
+
+int gptq_quantize_layers(int n_layers, const gptq_layer* layers, int64_t d_in, const float* U,
+                         const int32_t* perm, const uint8_t* dead_mask, const gptq_params* p,
+                         int32_t* g_idx, void* ws, size_t ws_bytes, gptq_stream stream) {
+  if (n_layers < 1 || n_layers > 1024)
+    return fail(GPTQ_ERR_INVALID_ARG, "n_layers must be in [1, 1024] (got %d)", n_layers);
+  if (!layers || !U) return fail(GPTQ_ERR_INVALID_ARG, "layers and U must not be NULL");
+  if (d_in <= 0 || d_in > kMaxDin)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld]", (long long)kMaxDin);
+  int64_t total = 0;
+  std::vector<gq::LayerIO> io((size_t)n_layers);
+  for (int i = 0; i < n_layers; ++i) {
+    const gptq_layer& L = layers[i];
+    if (!L.W || !L.qweight || !L.scales || !L.zeros)
+      return fail(GPTQ_ERR_INVALID_ARG, "layer %d: W, qweight, scales and zeros must not be NULL", i);
+    if (!valid_dtype(L.w_dtype)) return fail(GPTQ_ERR_INVALID_ARG, "layer %d: unknown w_dtype", i);
+    if (L.d_out <= 0 || L.d_out > kMaxDout)
+      return fail(GPTQ_ERR_INVALID_ARG, "layer %d: d_out must be in [1, %lld]", i, (long long)kMaxDout);
+    if (L.ld_w < d_in) return fail(GPTQ_ERR_INVALID_ARG, "layer %d: ld_w < d_in", i);
+    total += L.d_out;
+    io[(size_t)i] = gq::LayerIO{L.W, L.w_dtype, L.d_out, L.ld_w, L.qweight, L.scales, L.zeros,
+                                L.W_hat, L.row_loss};
+  }
+  if (total > kMaxDout)
+    return fail(GPTQ_ERR_INVALID_ARG, "the layers' rows add up to more than %lld", (long long)kMaxDout);
+  int rc = check_params(p, d_in);
+  if (rc) return rc;
+  if (p->act_order && !perm)
+    return fail(GPTQ_ERR_INVALID_ARG,
+                "act_order needs the perm from gptq_prepare_hinv (U is in that order)");
+  rc = check_ws(ws, ws_bytes, gq::quantize_ws_bytes(total, d_in), "quantize_layers");
+  if (rc) return rc;
+  hipError_t e = gq::quantize_layers_launch(io.data(), n_layers, d_in, U, perm, dead_mask, *p, g_idx,
+                                            ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("quantize_layers", e);
+  return GPTQ_OK;
+}
+
+int gptq_obq_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
+                   const float* H, const gptq_params* p, uint32_t* qweight, float* scales,
+                   uint8_t* zeros, float* W_hat, int32_t* order, float* row_loss, void* ws,
+                   size_t ws_bytes, gptq_stream stream) {
+  if (!W || !H || !qweight || !scales || !zeros)
+    return fail(GPTQ_ERR_INVALID_ARG, "W, H, qweight, scales and zeros must not be NULL");
+  if (!valid_dtype(w_dtype)) return fail(GPTQ_ERR_INVALID_ARG, "unknown w_dtype %d", w_dtype);
+  if (d_in <= 0 || d_out <= 0 || d_out > kMaxDout)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in and d_out must be positive");
+  if (ld_w < d_in) return fail(GPTQ_ERR_INVALID_ARG, "ld_w < d_in");
+  if (!p) return fail(GPTQ_ERR_INVALID_ARG, "params is NULL");
+  if (p->bits != 2 && p->bits != 3 && p->bits != 4 && p->bits != 8)
+    return fail(GPTQ_ERR_INVALID_ARG, "bits must be 2, 3, 4 or 8 (got %d)", p->bits);
+  if (!(p->percdamp >= 0.f) || !std::isfinite(p->percdamp))
+    return fail(GPTQ_ERR_INVALID_ARG, "percdamp must be finite and >= 0");
+  if (p->sym != 0 && p->sym != 1) return fail(GPTQ_ERR_INVALID_ARG, "sym must be 0 or 1");
+  if (p->group_size != -1 && p->group_size < d_in)
+    return fail(GPTQ_ERR_UNSUPPORTED, "OBQ runs with one grid per row (group_size -1)");
+  if (p->act_order) return fail(GPTQ_ERR_UNSUPPORTED, "OBQ chooses its own order (act_order 0)");
+  if (d_in > gq::obq_max_din())
+    return fail(GPTQ_ERR_UNSUPPORTED, "OBQ is the tiny-layer comparator: d_in <= %d (got %lld)",
+                gq::obq_max_din(), (long long)d_in);
+  int rc = check_ws(ws, ws_bytes, gq::obq_ws_bytes(d_in), "obq_layer");
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* status_dev = nullptr;
+  hipError_t e = gq::obq_launch(W, w_dtype, d_out, d_in, ld_w, H, *p, qweight, scales, zeros,
+                                W_hat, order, row_loss, ws, &status_dev, s);
+  if (e != hipSuccess) return hip_fail("obq_layer", e);
+  int32_t st = 0;
+  e = hipMemcpyAsync(&st, status_dev, sizeof st, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail("obq_layer (status read-back)", e);
+  if (st != INT_MAX)
+    return fail(GPTQ_ERR_NOT_SPD, "damped Hessian is not positive definite (pivot %d); raise percdamp",
+                (int)st);
+  return GPTQ_OK;
+}
+
+int gptq_timing(int enable) { return gq::timing_enable(enable); }
+
+int gptq_timing_read(float* ms, int n) {
+  if (!ms || n <= 0) return fail(GPTQ_ERR_INVALID_ARG, "ms must hold n > 0 floats");
+  hipError_t e = gq::timing_read(ms, n);
+  if (e != hipSuccess) return hip_fail("timing_read", e);
+  return GPTQ_OK;
+}
+
+int gptq_export(int bits, int64_t d_out, int64_t d_in, int64_t n_groups, const uint32_t* qweight,
+                const float* scales, const uint8_t* zeros, uint32_t* qweight_dense,
+                uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_INVALID_ARG, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+  if (d_in <= 0 || d_in > kMaxDin)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld]", (long long)kMaxDin);
+  if (d_out <= 0 || d_out > kMaxDout)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_out must be in [1, %lld]", (long long)kMaxDout);
+  if (n_groups <= 0 || n_groups > d_in)
+    return fail(GPTQ_ERR_INVALID_ARG, "n_groups must be in [1, d_in]");
+  if (qweight_dense && !qweight)
+    return fail(GPTQ_ERR_INVALID_ARG, "qweight_dense needs qweight");
+  if (scales_f16 && !scales) return fail(GPTQ_ERR_INVALID_ARG, "scales_f16 needs scales");
+  if (zeros_f16 && !zeros) return fail(GPTQ_ERR_INVALID_ARG, "zeros_f16 needs zeros");
+  hipError_t e = gq::export_launch(bits, d_out, d_in, n_groups, qweight, scales, zeros,
+                                   qweight_dense, scales_f16, zeros_f16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("export", e);
   return GPTQ_OK;
 }
 

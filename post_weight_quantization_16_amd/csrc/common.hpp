@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -66,8 +67,10 @@ hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
 // ---------------------------------------------------------------- Hessian
 int hessian_splits(int64_t d, int64_t n_tok);
 size_t hessian_ws_bytes(int64_t d, int64_t n_tok);
+// smallest workspace the Hessian runs with (one partial Hessian)
+size_t hessian_min_ws_bytes(int64_t d);
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
-                          int64_t ld_x, void* ws, hipStream_t s);
+                          int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------- prepare
 size_t prepare_ws_bytes(int64_t d);
@@ -96,10 +99,50 @@ template <> hipError_t launch_sweep<64>(const SweepArgs& a, hipStream_t s);
 template <> hipError_t launch_sweep<128>(const SweepArgs& a, hipStream_t s);
 
 size_t quantize_ws_bytes(int64_t m, int64_t d);
+// one layer of a multi-layer call (all layers share d_in, U, perm and dead)
+struct LayerIO {
+  const void* W; int dt; int64_t m, ld_w;
+  uint32_t* qweight; float* scales; uint8_t* zeros; float* W_hat; float* row_loss;
+};
+hipError_t quantize_layers_launch(const LayerIO* L, int n, int64_t d, const float* U,
+                                  const int32_t* perm, const uint8_t* dead, const gptq_params& p,
+                                  int32_t* g_idx, void* ws, hipStream_t s);
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int64_t ld_w,
                            const float* U, const int32_t* perm, const uint8_t* dead,
                            const gptq_params& p, uint32_t* qweight, float* scales,
                            uint8_t* zeros, float* W_hat, int32_t* g_idx, float* row_loss,
                            void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- stage timing
+// (diagnostics, timing.hip): a scope records a HIP event pair around the
+// launches it encloses while timing is enabled.
+enum { kTimerUpdate = 0, kTimerSweep = 1, kTimerChol = 2, kTimerInverse = 3, kTimerHessian = 4,
+       kTimerCount = 5 };
+class TimerScope {
+ public:
+  TimerScope(int which, hipStream_t s);
+  ~TimerScope();
+  TimerScope(const TimerScope&) = delete;
+  TimerScope& operator=(const TimerScope&) = delete;
+ private:
+  int which_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr;
+};
+int timing_enable(int on);
+hipError_t timing_read(float* ms, int n);
+
+// ---------------------------------------------------------------- OBQ comparator
+int obq_max_din();
+size_t obq_ws_bytes(int64_t d);
+hipError_t obq_launch(const void* W, int w_dtype, int64_t m, int64_t d, int64_t ld_w,
+                      const float* H, const gptq_params& p, uint32_t* qweight, float* scales,
+                      uint8_t* zeros, float* W_hat, int32_t* order, float* row_loss, void* ws,
+                      int32_t** status_dev, hipStream_t s);
+
+// ---------------------------------------------------------------- export
+hipError_t export_launch(int bits, int64_t m, int64_t d, int64_t ng, const uint32_t* qweight,
+                         const float* scales, const uint8_t* zeros, uint32_t* qdense,
+                         uint16_t* s16, uint16_t* z16, hipStream_t s);
 
 }  // namespace gq

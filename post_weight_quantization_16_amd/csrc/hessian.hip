@@ -10,7 +10,23 @@
 // exactly symmetric and the result is deterministic.
 //
 // bf16/fp16 inputs: v_mfma_f32_32x32x16_{bf16,f16}; the products are exact in
-// fp32 and accumulate in fp32.  The MFMA operand wants 8 consecutive tokens of
+// fp32 and accumulate in fp32.
+//
+// Shifted accumulation.  An fp32 sum of n terms that share a sign loses
+// about u·sqrt(n) of its value, and activations with a non-zero channel mean
+// make every entry of XᵀX such a sum (the entries grow like N·μ_iμ_j).  Each
+// workgroup therefore keeps its accumulators near zero: every 512 tokens it
+// adds, with one more MFMA per accumulator tile, the product of the constant
+// operands 32·μ_i and −μ_j over its 16 k-slots, i.e. −512·μ_iμ_j, where μ is
+// the per-channel mean of the call's first tokens rounded to the input's
+// 16-bit format (0 where that mean is not significant).  These products are
+// exact in fp32, and the reduction adds the exact total 512·c·μ_iμ_j back in
+// fp64 (c = number of such MFMAs over all splits).  The result is the same
+// sum with its rounding errors taken relative to the centred partial sums;
+// for zero-mean channels μ = 0 and nothing changes.  The split partials are
+// summed in fp64 as well, so H leaves the reduction rounded once to fp32.
+//
+// The MFMA operand wants 8 consecutive tokens of
 // one column per lane while X is contiguous along columns:
 //   fast path (d, ld multiples of 8, X 16-byte aligned): 256x256 tiles, X kept
 //     in natural layout in LDS and read with LDS transpose loads;
@@ -28,6 +44,100 @@ namespace {
 constexpr int HT = 128;        // output tile
 constexpr int HK = 64;         // tokens per LDS stage
 constexpr int HLD = HK + 8;    // LDS row stride in 16-bit elements
+constexpr int kShiftTok = 512;        // tokens between two shift MFMAs
+constexpr int kShiftSample = 1024;    // tokens the shift μ is estimated from
+
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
+// The shift operands of one lane: 8 k-slots holding the same 16-bit value.
+__device__ __forceinline__ s16x8 splat16(uint16_t v) {
+  const short x = (short)v;
+  return s16x8{x, x, x, x, x, x, x, x};
+}
+// 32·μ and −μ as 16-bit patterns (exact: a power-of-two scale and a sign
+// flip of a value whose magnitude the shift kernel keeps in range)
+template <bool BF16>
+__device__ __forceinline__ uint16_t times32(uint16_t m) {
+  if (m == 0) return 0;
+  return (uint16_t)(m + (BF16 ? (5u << 7) : (5u << 10)));   // exponent + 5
+}
+__device__ __forceinline__ uint16_t negate16(uint16_t m) { return m ? (uint16_t)(m ^ 0x8000u) : 0; }
+
+template <bool BF16>
+__device__ __forceinline__ float half_to_f32(uint16_t b) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)b << 16);
+  else return (float)__builtin_bit_cast(_Float16, b);
+}
+template <bool BF16>
+__device__ __forceinline__ uint16_t f32_to_half_rne(float f) {
+  if constexpr (BF16) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+}
+
+// μ_c for c < dp: the mean of column c over the first n0 tokens, rounded to
+// the 16-bit input format, or 0 when it is not significant (|mean| at most
+// 4·std/√n0: a zero-mean channel keeps the plain accumulation) or when
+// c >= d.  Workgroup: 64 columns (8 groups of 8 adjacent columns, 16-byte
+// loads) x 32 token lanes; the lanes' sums are combined in a fixed order, so
+// μ is deterministic.  The magnitude is kept below 2^10 so that 32·μ and
+// the shift products stay finite in either 16-bit format.
+template <bool BF16>
+__global__ __launch_bounds__(256) void shift_mean_kernel(const uint16_t* __restrict__ X, int64_t ld,
+                                                         int d, int dp, int n0, int vec,
+                                                         uint16_t* __restrict__ mu) {
+  __shared__ float S1[32][65], S2[32][65];
+  const int t = threadIdx.x, cg = t & 7, tl = t >> 3;
+  const int c0 = blockIdx.x * 64 + cg * 8;
+  float s1[8], s2[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { s1[q] = 0.f; s2[q] = 0.f; }
+  for (int r0 = tl; r0 < n0; r0 += 32 * 4) {
+    uint16_t e[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + 32 * u;
+      const uint16_t* p = X + (int64_t)r * ld + c0;
+      if (r < n0 && vec && c0 + 7 < d) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[u][q] = (uint16_t)(w4[q >> 1] >> (16 * (q & 1)));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[u][q] = (r < n0 && c0 + q < d) ? p[q] : (uint16_t)0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float x = half_to_f32<BF16>(e[u][q]);
+        s1[q] += x;
+        s2[q] = fmaf(x, x, s2[q]);
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { S1[tl][cg * 8 + q] = s1[q]; S2[tl][cg * 8 + q] = s2[q]; }
+  __syncthreads();
+  if (t < 64) {
+    const int c = blockIdx.x * 64 + t;
+    double a = 0.0, b = 0.0;
+    for (int l = 0; l < 32; ++l) { a += S1[l][t]; b += S2[l][t]; }
+    uint16_t m = 0;
+    if (c < d && n0 > 1) {
+      const double mean = a / n0;
+      const double var = fmax(b / n0 - mean * mean, 0.0);
+      // normal numbers only (32·μ is formed by the exponent), below 2^10
+      if (fabs(mean) > 4.0 * sqrt(var / n0) && fabs(mean) < 1024.0 && fabs(mean) >= 1.0 / 8192)
+        m = f32_to_half_rne<BF16>((float)mean);
+    }
+    if (c < dp) mu[c] = m;
+  }
+}
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
@@ -55,7 +165,8 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 template <bool BF16>
 __global__ __launch_bounds__(256) void syrk16_generic_kernel(const uint16_t* __restrict__ X, int64_t ld,
                                                      int d, int64_t n_tok, int64_t chunk, int nt,
-                                                     float* __restrict__ P, int64_t dp, int vec) {
+                                                     float* __restrict__ P, int64_t dp, int vec,
+                                                     const uint16_t* __restrict__ mu) {
   int ti, tj;
   tile_of(blockIdx.x, nt, ti, tj);
   const int split = blockIdx.y;
@@ -79,6 +190,13 @@ __global__ __launch_bounds__(256) void syrk16_generic_kernel(const uint16_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // shift operands: 32·μ of this lane's A rows, −μ of its B columns
+  uint16_t sa[2], sb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    sa[i] = times32<BF16>(mu[ti * HT + wm * 64 + i * 32 + (lane & 31)]);
+    sb[i] = negate16(mu[tj * HT + wn * 64 + i * 32 + (lane & 31)]);
+  }
   u32x4 rin[8];
   auto gload = [&](int64_t t0) {
 #pragma unroll
@@ -144,6 +262,21 @@ __global__ __launch_bounds__(256) void syrk16_generic_kernel(const uint16_t* __r
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
     }
+    if (((t0 - t_begin) / HK) % (kShiftTok / HK) == kShiftTok / HK - 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (BF16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, splat16(sa[i])), __builtin_bit_cast(bf16x8, splat16(sb[j])),
+                acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, splat16(sa[i])), __builtin_bit_cast(f16x8, splat16(sb[j])),
+                acc[i][j], 0, 0, 0);
+        }
+    }
     __syncthreads();
     if (more) {
       lstore();
@@ -202,7 +335,6 @@ constexpr int kWaitFirstCount = 8 * (NBUF - 3);   // before the loop: stages 0 a
 constexpr int kWaitFirst = ((kWaitFirstCount >> 4) << 14) | (kWaitFirstCount & 15) | 0x70 | 0xF00;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int fswz(int row) { return (row & 3) << 2; }
@@ -249,13 +381,17 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict__ X, int64_t ld,
                                                        int d, int64_t n_tok, int64_t chunk, int nt,
                                                        float* __restrict__ P, int64_t dp,
-                                                       const uint16_t* __restrict__ zero16) {
+                                                       const uint16_t* __restrict__ zero16,
+                                                       const uint16_t* __restrict__ mu) {
   const int tiles = nt * (nt + 1) / 2;
   int ti, tj, split;
   fast_tile(blockIdx.x, nt, tiles, ti, tj, split);
   const int64_t t_begin = (int64_t)split * chunk;
   const int64_t t_end = min(n_tok, t_begin + chunk);
-  const int nstage = (int)((t_end - t_begin + FK - 1) / FK);
+  // stages of FK tokens, rounded up to whole shift groups of kShiftTok
+  // tokens (stages past the data copy the zero chunk and add nothing)
+  constexpr int kGroup = kShiftTok / FK;
+  const int nstage = (int)((t_end - t_begin + kShiftTok - 1) / kShiftTok) * kGroup;
   __shared__ __attribute__((aligned(1024))) char S[NBUF * FSTAGE];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -336,6 +472,28 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
   };
   static_assert(FK == 32, "a stage is two 16-token MFMA steps");
   auto stage_ptr = [&](int st) { return (const char*)S + (st % NBUF) * FSTAGE; };
+  // shift operands (see the top of this file): 32·μ of this lane's A rows
+  // and −μ of its B columns, packed two per register
+  uint32_t sh[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    sh[f] = (uint32_t)times32<BF16>(mu[ti * FT + wm * 128 + f * 32 + (lane & 31)]) |
+            ((uint32_t)negate16(mu[tj * FT + wn * 128 + f * 32 + (lane & 31)]) << 16);
+  auto shift = [&]() {
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj) {
+        const s16x8 a = splat16((uint16_t)(sh[fi] & 0xFFFFu));
+        const s16x8 b = splat16((uint16_t)(sh[fj] >> 16));
+        if constexpr (BF16)
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[fi][fj], 0, 0, 0);
+        else
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc[fi][fj], 0, 0, 0);
+      }
+  };
   for (int s0 = 0; s0 < NBUF - 1; ++s0) dma(s0);
   // Each stage is two batches of 16 MFMAs.  Batch A multiplies the pieces of
   // the stage's first step (p0) while reading those of its second step (p1)
@@ -362,7 +520,13 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
     s16x4 p0[16], p1[16];
 #pragma unroll
     for (int n = 0; n < 16; ++n) p0[n] = rd(stage_ptr(0), 0, n);
-    for (int st = 0; st < nstage; ++st) {
+    // one shift per group of 16 stages (512 tokens); the group is unrolled
+    // so the shift MFMAs share the stages' basic block (a shift behind a
+    // branch made the compiler move the accumulators out of their registers)
+    for (int g0 = 0; g0 < nstage; g0 += kGroup) {
+#pragma unroll
+    for (int st16 = 0; st16 < kGroup; ++st16) {
+      const int st = g0 + st16;
       const char* cur = stage_ptr(st);
       const char* nxt = stage_ptr(st + 1);
 #pragma unroll
@@ -389,6 +553,9 @@ __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    shift();
+    __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA may outlive the workgroup
   if (idle) return;
@@ -411,28 +578,39 @@ __global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z
   z[threadIdx.x] = 0u;
 }
 
-// H[i][j] += 2·Σ_s P_s[i][j] over the upper triangle, and the mirrored
-// H[j][i] = H[i][j], one 128x128 upper tile (ti <= tj) per workgroup.  The
-// split partials are summed in a fixed order (deterministic).  Each thread
+// H[i][j] += 2·(Σ_s P_s[i][j] + c·μ_iμ_j) over the upper triangle, and the
+// mirrored H[j][i] = H[i][j], one 128x128 upper tile (ti <= tj) per
+// workgroup.  c·μ_iμ_j restores what the shift MFMAs took out (c tokens'
+// worth, mu = null when no shift was applied).  The sum is formed in fp64 in
+// a fixed order (deterministic) and rounded once.  Each thread
 // owns 16 float4 runs of the tile and issues all of a split's loads before
 // adding them, and all of its H reads before any H write (reads after a
 // write through the same pointer would each wait a memory round trip); the
 // finished tile goes through LDS to be written transposed, so both writes
 // are coalesced.
+template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
                                                             const float* __restrict__ P,
                                                             int64_t dp, int splits, int nt,
-                                                            int vec_h) {
+                                                            int vec_h,
+                                                            const uint16_t* __restrict__ mu,
+                                                            double shift_tok) {
   int ti, tj;
   tile_of(blockIdx.x, nt, ti, tj);
   __shared__ float T[HT][HT + 1];
+  __shared__ double mr[HT], mc[HT];
   const int t = threadIdx.x;
   constexpr int NR = HT * HT / (256 * 4);   // float4 runs per thread (16)
   const int64_t pstride = dp * dp;
   const float* src = P + (int64_t)(ti * HT) * dp + tj * HT;   // always inside the partials
-  f32x4 acc[NR];
+  if (mu && t < HT) {
+    mr[t] = shift_tok * (double)half_to_f32<BF16>(mu[ti * HT + t]);
+    mc[t] = (double)half_to_f32<BF16>(mu[tj * HT + t]);
+  }
+  typedef __attribute__((ext_vector_type(4))) double f64x4;
+  f64x4 acc[NR];
 #pragma unroll
-  for (int it = 0; it < NR; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < NR; ++it) acc[it] = f64x4{0.0, 0.0, 0.0, 0.0};
   for (int sp = 0; sp < splits; ++sp) {
     f32x4 v[NR];
 #pragma unroll
@@ -441,7 +619,18 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
       v[it] = *reinterpret_cast<const f32x4*>(src + sp * pstride + (int64_t)a * dp + b4);
     }
 #pragma unroll
-    for (int it = 0; it < NR; ++it) acc[it] += v[it];
+    for (int it = 0; it < NR; ++it)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[it][q] += (double)v[it][q];
+  }
+  if (mu) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < NR; ++it) {
+      const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[it][q] = fma(mr[a], mc[b4 + q], acc[it][q]);
+    }
   }
   const bool full = vec_h && ti < tj && (tj + 1) * HT <= d;
   if (full) {
@@ -455,7 +644,7 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
     for (int it = 0; it < NR; ++it) {
       const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[it][q] = fmaf(2.f, acc[it][q], h[it][q]);
+      for (int q = 0; q < 4; ++q) h[it][q] = (float)fma(2.0, acc[it][q], (double)h[it][q]);
       *reinterpret_cast<f32x4*>(H + (int64_t)(ti * HT + a) * d + tj * HT + b4) = h[it];
 #pragma unroll
       for (int q = 0; q < 4; ++q) T[a][b4 + q] = h[it][q];
@@ -469,7 +658,7 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
         const int jq = tj * HT + b4 + q;
         float v = 0.f;
         if (i < d && jq < d && jq >= i) {
-          v = fmaf(2.f, acc[it][q], H[(int64_t)i * d + jq]);
+          v = (float)fma(2.0, acc[it][q], (double)H[(int64_t)i * d + jq]);
           H[(int64_t)i * d + jq] = v;
         }
         T[a][b4 + q] = v;
@@ -532,40 +721,67 @@ size_t hessian_ws_bytes(int64_t d, int64_t n_tok) {
   const int64_t dpg = ceil_div(d, FT) * FT;
   const size_t fast = (size_t)fast_splits(d, n_tok) * dpg * dpg * sizeof(float);
   const size_t gen = (size_t)generic_splits(d, n_tok) * dpg * dpg * sizeof(float);
-  // + a 256-byte zero chunk after the partials (source of out-of-range copies)
-  return align_up(std::max<size_t>(std::max(fast, gen), 256)) + 256;
+  // partials, then the shift μ (dp 16-bit values), then a 256-byte zero
+  // chunk (source of out-of-range copies)
+  return align_up(std::max<size_t>(std::max(fast, gen), 256)) + align_up((size_t)dpg * 2) + 256;
 }
 
+size_t hessian_min_ws_bytes(int64_t d) {
+  const int64_t dp = ceil_div(d, FT) * FT;
+  return (size_t)dp * dp * 4 + align_up((size_t)dp * 2) + 256;
+}
+
+// Workspace layout: S partial Hessians (S as the path wants, at most what
+// ws_bytes holds), then μ (dp 16-bit values), then the 256-byte zero chunk.
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
-                          int64_t ld_x, void* ws, hipStream_t s) {
+                          int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s) {
   if (n_tok <= 0) return hipSuccess;
   const int64_t dp = ceil_div(d, FT) * FT;   // partial Hessians are dp x dp
   float* P = static_cast<float*>(ws);
+  const size_t part = (size_t)dp * dp * 4;
+  const int fit = (int)std::min<size_t>(64, (ws_bytes - align_up((size_t)dp * 2) - 256) / part);
   hipError_t e;
   const bool fast = x_dtype != GPTQ_F32 && d % 8 == 0 && ld_x % 8 == 0 && (uintptr_t)X % 16 == 0;
-  int splits;
+  // splits: the path's choice, capped by the workspace; the token chunk of
+  // each split is a whole number of stages
+  const int want = fast ? fast_splits(d, n_tok) : generic_splits(d, n_tok);
+  const int step = fast ? FK : HK;
+  const int64_t chunk = ceil_div(ceil_div(n_tok, std::min(want, fit)), step) * step;
+  const int splits = (int)ceil_div(n_tok, chunk);
+  uint16_t* mu = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(part * splits));
+  uint16_t* zero16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(mu) + align_up((size_t)dp * 2));
+  const bool bf = x_dtype == GPTQ_BF16;
+  double shift_tok = 0.0;   // tokens' worth of μμᵀ the shift MFMAs took out
+  if (x_dtype != GPTQ_F32) {
+    const int n0 = (int)std::min<int64_t>(n_tok, kShiftSample);
+    const int vec = ((uintptr_t)X % 16 == 0) && (ld_x % 8 == 0);
+    const unsigned gm = (unsigned)ceil_div(dp, 64);
+    if (bf) shift_mean_kernel<true><<<gm, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
+                                                        (int)dp, n0, vec, mu);
+    else shift_mean_kernel<false><<<gm, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
+                                                      (int)dp, n0, vec, mu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (fast) {
     const int nt = (int)ceil_div(d, FT);
     const int tiles = nt * (nt + 1) / 2;
-    splits = fast_splits(d, n_tok);
-    const int64_t chunk = ceil_div(ceil_div(n_tok, splits), FK) * FK;
     const unsigned grid = (unsigned)(tiles * splits);
-    uint16_t* zero16 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
-                                                   hessian_ws_bytes(d, n_tok) - 256);
+    for (int sp = 0; sp < splits; ++sp) {   // shift MFMAs per split: one per started 16 stages
+      const int64_t rows = std::min<int64_t>(n_tok, (sp + 1) * chunk) - sp * chunk;
+      shift_tok += (double)ceil_div(ceil_div(rows, FK), kShiftTok / FK) * kShiftTok;
+    }
     zero_chunk_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(zero16));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (x_dtype == GPTQ_BF16)
       syrk256_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
-                                                chunk, nt, P, dp, zero16);
+                                                chunk, nt, P, dp, zero16, mu);
     else
       syrk256_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
-                                                 n_tok, chunk, nt, P, dp, zero16);
+                                                 n_tok, chunk, nt, P, dp, zero16, mu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
     const int nt = (int)ceil_div(d, HT);
     const int tiles = nt * (nt + 1) / 2;
-    splits = generic_splits(d, n_tok);
-    const int64_t chunk = ceil_div(ceil_div(n_tok, splits), HK) * HK;
     if (x_dtype == GPTQ_F32) {
       GemmArgs g{};
       g.M = (int)d; g.N = (int)d;
@@ -578,19 +794,29 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
     } else {
       const int vec = ((uintptr_t)X % 16 == 0) && (ld_x % 8 == 0);
       dim3 grid(tiles, splits);
+      for (int sp = 0; sp < splits; ++sp) {   // shift MFMAs per split: one per 8 stages
+        const int64_t rows = std::min<int64_t>(n_tok, (sp + 1) * chunk) - sp * chunk;
+        shift_tok += (double)(ceil_div(rows, HK) / (kShiftTok / HK)) * kShiftTok;
+      }
       if (x_dtype == GPTQ_BF16)
         syrk16_generic_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
-                                                         n_tok, chunk, nt, P, dp, vec);
+                                                         n_tok, chunk, nt, P, dp, vec, mu);
       else
         syrk16_generic_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
-                                                          n_tok, chunk, nt, P, dp, vec);
+                                                          n_tok, chunk, nt, P, dp, vec, mu);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
   const int nt128 = (int)(dp / HT);
   const int vec_h = ((uintptr_t)H % 16 == 0) && (d % 4 == 0);
-  reduce_mirror_kernel<<<nt128 * (nt128 + 1) / 2, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128,
-                                                               vec_h);
+  const unsigned gr = (unsigned)(nt128 * (nt128 + 1) / 2);
+  const uint16_t* mu_r = x_dtype == GPTQ_F32 ? nullptr : mu;
+  if (bf || x_dtype == GPTQ_F32)
+    reduce_mirror_kernel<true><<<gr, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128, vec_h, mu_r,
+                                                  shift_tok);
+  else
+    reduce_mirror_kernel<false><<<gr, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128, vec_h, mu_r,
+                                                   shift_tok);
   return hipGetLastError();
 }
 

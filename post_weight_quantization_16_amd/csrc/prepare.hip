@@ -21,6 +21,8 @@
 // skipping the zero triangles).
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
+#include <memory>
 #include <vector>
 
 #include <type_traits>
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(1024) void diag_kernel(float* __restrict__ H, int64
   }
   if (threadIdx.x == 0) {
     lam[0] = (float)((double)percdamp * part[0] / (double)d);
-    status[0] = INT_MAX;
+    status[0] = INT_MAX;   // smallest failing pivot
+    status[1] = 0;         // a wave's bounded wait ran out
   }
 }
 
@@ -236,9 +239,12 @@ __global__ __launch_bounds__(256) void build_g_rows_kernel(const float* __restri
 }
 
 struct PanelArgs {
-  float* G; int64_t d; int k0, kb;
+  float* G; int64_t d; int k0, kb;   // G: the n x n matrix being factored (n = d here)
   float* Linv; int* status;
-  int np;   // panel workgroups in the launch
+  int np;          // panel workgroups in the launch
+  int spin_limit;  // bound on every flag wait (polls)
+  int64_t ld;      // row stride of G and Linv
+  int piv_base;    // index of G's first column in the whole factorization
 };
 
 constexpr int LS = NB + 2;       // LDS row stride: the half-waves' MFMA reads hit disjoint banks
@@ -296,8 +302,8 @@ __device__ __forceinline__ int acc_row(int mi, int lane, int e) {
 // (row lane%16, k lane/16), B: (k lane/16, column lane%16), C: rows
 // 4·(lane/16) + v, column lane%16), stored to G.
 __device__ __forceinline__ void strip(const float* BS, const float* PX, float* G, int64_t d,
-                                      int64_t R0, int k0, int kb, int c, int rb0, int rb1,
-                                      int lane) {
+                                      int64_t ld, int64_t R0, int k0, int kb, int c, int rb0,
+                                      int rb1, int lane) {
   const int m = lane & 15, kq = lane >> 4;
   for (int rb = rb0; rb < rb1; ++rb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -311,7 +317,7 @@ __device__ __forceinline__ void strip(const float* BS, const float* PX, float* G
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t row = R0 + 16 * rb + 4 * kq + v;
-      if (row < d && col < kb) G[row * d + k0 + col] = acc[v];
+      if (row < d && col < kb) G[row * ld + k0 + col] = acc[v];
     }
   }
 }
@@ -321,18 +327,18 @@ __device__ __forceinline__ void strip(const float* BS, const float* PX, float* G
 // panel's rows, by one wave from registers (v_mfma_f32_32x32x2f32; lanes
 // 0-31 take k in [0, 32), lanes 32-63 k in [32, 64), so each lane's 32
 // values of a row are contiguous).  Rows past d or kb count as zero.
-__device__ __forceinline__ void rows_preupdate(const float* G, int64_t d, int64_t R0, int k0,
-                                               int kb, int kp, float* BS, int lane) {
+__device__ __forceinline__ void rows_preupdate(const float* G, int64_t d, int64_t ld, int64_t R0,
+                                               int k0, int kb, int kp, float* BS, int lane) {
   const int h = lane >> 5, l32 = lane & 31;
-  const bool vec = (d & 3) == 0;
+  const bool vec = (ld & 3) == 0;
   float qv[2][32], pv[2][32];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int64_t qr = R0 + 32 * x + l32;
     const int pr = 32 * x + l32;
     const bool qok = qr < d, pok = pr < kb;
-    const float* qs = G + (qok ? qr : 0) * d + kp + 32 * h;
-    const float* ps = G + (int64_t)(k0 + (pok ? pr : 0)) * d + kp + 32 * h;
+    const float* qs = G + (qok ? qr : 0) * ld + kp + 32 * h;
+    const float* ps = G + (int64_t)(k0 + (pok ? pr : 0)) * ld + kp + 32 * h;
     if (vec) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -367,7 +373,7 @@ __device__ __forceinline__ void rows_preupdate(const float* G, int64_t d, int64_
     }
 }
 
-constexpr int kSpinLimit = 1 << 20;   // safety bound on a flag wait (never reached)
+constexpr int kSpinLimit = 1 << 20;   // default bound on a flag wait (never reached)
 
 __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __restrict__ smem) {
   float* AS = smem;              // G11 (lower, identity-padded)
@@ -381,7 +387,7 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   static_assert(NB * NB <= BLK && NB * PXS <= BLK, "published steps exceed their LDS region");
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t d = p.d;
+  const int64_t d = p.d, ld = p.ld;
   const int k0 = p.k0, kb = p.kb;
   const int64_t R0 = (int64_t)k0 + kb + (int64_t)b * NB;
   const bool upd = k0 > 0;       // previous panels are full width
@@ -393,16 +399,16 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
     // after its load, or a load-store pair per element, would wait for the
     // load at once).  Full-width panels of a 4-aligned G load float4: thread
     // t covers rows (t >> 4) + 16u, columns 4(t & 15) .. +3.
-    if ((d & 3) == 0 && k0 + NB <= d) {
+    if ((ld & 3) == 0 && k0 + NB <= d) {
       const int c4 = 4 * (t & 15);
       f32x4 va[4], vb[4], vp[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = (t >> 4) + 16 * u;
         const int64_t ra = k0 + (i < kb ? i : 0), rb = R0 + i < d ? R0 + i : 0;
-        va[u] = *reinterpret_cast<const f32x4*>(G + ra * d + k0 + c4);
-        vb[u] = *reinterpret_cast<const f32x4*>(G + rb * d + k0 + c4);
-        if (upd) vp[u] = *reinterpret_cast<const f32x4*>(G + ra * d + kp + c4);
+        va[u] = *reinterpret_cast<const f32x4*>(G + ra * ld + k0 + c4);
+        vb[u] = *reinterpret_cast<const f32x4*>(G + rb * ld + k0 + c4);
+        if (upd) vp[u] = *reinterpret_cast<const f32x4*>(G + ra * ld + kp + c4);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -421,10 +427,10 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
       for (int u = 0; u < 16; ++u) {
         const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
         const bool okd = i < kb && k <= i;
-        va[u] = G[(int64_t)(k0 + (okd ? i : 0)) * d + k0 + (okd ? k : 0)];
+        va[u] = G[(int64_t)(k0 + (okd ? i : 0)) * ld + k0 + (okd ? k : 0)];
         const bool okb = R0 + i < d && k < kb;
-        vb[u] = G[(okb ? R0 + i : 0) * d + (okb ? k0 + k : 0)];
-        if (upd) vp[u] = G[(int64_t)(k0 + (i < kb ? i : 0)) * d + kp + k];
+        vb[u] = G[(okb ? R0 + i : 0) * ld + (okb ? k0 + k : 0)];
+        if (upd) vp[u] = G[(int64_t)(k0 + (i < kb ? i : 0)) * ld + kp + k];
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -471,7 +477,9 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   if (t <= NB + 2) flag[t] = 0;
   __syncthreads();
   int bad_j = -1;
-  bool stalled = false;   // after one expired wait, stop waiting (the result is flagged bad)
+  // after one expired wait a wave stops waiting; status[1] then flags the
+  // whole call, whose outputs are undefined
+  bool stalled = false;
   if (upd && w > 0) {
     // wave 1 is the first to need its slab and must keep up with wave 0's
     // steps, so waves 2 and 3 take slab 1's tiles in their row blocks first
@@ -487,10 +495,7 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
         int spin = 0;
         while (!stalled &&
                __hip_atomic_load(&flag[f], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-          if (++spin > kSpinLimit) {
-            stalled = true;
-            bad_j = (bad_j < 0) ? 0 : bad_j;
-          }
+          if (++spin > p.spin_limit) stalled = true;
           __builtin_amdgcn_s_sleep(1);
         }
       }
@@ -531,10 +536,7 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
       int spin = 0;
       while (!stalled &&
              __hip_atomic_load(&flag[j0 + 3], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-        if (++spin > kSpinLimit) {
-          stalled = true;
-          bad_j = (bad_j < 0) ? j0 : bad_j;
-        }
+        if (++spin > p.spin_limit) stalled = true;
         __builtin_amdgcn_s_sleep(1);
       }
       read_batch(j0);
@@ -617,29 +619,27 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   const bool rows = R0 < d;
   if (upd && rows) {
     if (w == 0) {
-      rows_preupdate(G, d, R0, k0, kb, kp, BS, lane);
+      rows_preupdate(G, d, ld, R0, k0, kb, kp, BS, lane);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __hip_atomic_store(&flag[NB], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else if (w < 3) {
       int spin = 0;
       while (!stalled &&
              __hip_atomic_load(&flag[NB], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-        if (++spin > kSpinLimit) {
-          stalled = true;
-          bad_j = (bad_j < 0) ? 0 : bad_j;
-        }
+        if (++spin > p.spin_limit) stalled = true;
         __builtin_amdgcn_s_sleep(1);
       }
     }
   }
-  if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, k0 + bad_j);
-  if (rows && w < 3) strip(BS, PX, G, d, R0, k0, kb, w, 0, 4, lane);
+  if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, p.piv_base + k0 + bad_j);
+  if (lane == 0 && stalled) atomicOr(p.status + 1, 1);
+  if (rows && w < 3) strip(BS, PX, G, d, ld, R0, k0, kb, w, 0, 4, lane);
   __syncthreads();   // the last strip's X rows (published by wave 3) are visible
-  if (rows) strip(BS, PX, G, d, R0, k0, kb, 3, w, w + 1, lane);
+  if (rows) strip(BS, PX, G, d, ld, R0, k0, kb, 3, w, w + 1, lane);
   // X = L11⁻¹ to Linv's diagonal block, its rows spread over the panel's
   // workgroups and waves (row j by workgroup j % np)
   for (int jr = b + p.np * w; jr < kb; jr += 4 * p.np)
-    if (lane < kb) p.Linv[(int64_t)(k0 + jr) * d + k0 + lane] = PX[jr * PXS + lane];
+    if (lane < kb) p.Linv[(int64_t)(k0 + jr) * ld + k0 + lane] = PX[jr * PXS + lane];
 }
 
 // Lower-triangular tile enumeration: L -> (row by, column bx <= by).
@@ -788,16 +788,16 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_
     p[i] = 0.f;
 }
 
-TileJob near_job(float* G, int64_t d, int64_t k) {
+TileJob near_job(float* G, int64_t d, int64_t ld, int64_t k) {
   const chol_sched::NearRegion n = chol_sched::near_region(d, k);
   TileJob j{};
   if (n.c1 <= n.c0) return j;
   GemmArgs h{};  // G[c0:, c0:c1] −= G[c0:, a0:a0+K] · G[c0:c1, a0:a0+K]ᵀ  (lower part)
   h.M = (int)(d - n.c0); h.N = (int)(n.c1 - n.c0); h.K = n.K; h.k_last = n.K; h.batch = 1;
   h.alpha = -1.f; h.beta = 1.f;
-  h.A = G + n.c0 * d + n.a0; h.lda = d; h.trans_a = false;
-  h.B = G + n.c0 * d + n.a0; h.ldb = d; h.trans_b = true;
-  h.C = G + n.c0 * d + n.c0; h.ldc = d; h.tri = 1;
+  h.A = G + n.c0 * ld + n.a0; h.lda = ld; h.trans_a = false;
+  h.B = G + n.c0 * ld + n.a0; h.ldb = ld; h.trans_b = true;
+  h.C = G + n.c0 * ld + n.c0; h.ldc = ld; h.tri = 1;
   j.g = gemm_detail::make_kargs(h);
   j.dma = gemm_detail::dma_ok(j.g, false, true) ? 1 : 0;
   j.tile = n.tile;
@@ -807,19 +807,155 @@ TileJob near_job(float* G, int64_t d, int64_t k) {
   return j;
 }
 
-FarJob far_base(float* G, int64_t d) {
+FarJob far_base(float* G, int64_t d, int64_t ld) {
   FarJob f;
   GemmArgs h{};  // tile (r, t): G[128r:, 128t:] −= G[128r:, 128s:+128] · G[128t:, 128s:+128]ᵀ
   h.M = (int)d; h.N = (int)d; h.K = chol_sched::kSW; h.k_last = chol_sched::kSW; h.batch = 1;
   h.alpha = -1.f; h.beta = 1.f;
-  h.A = G; h.lda = d; h.trans_a = false;
-  h.B = G; h.ldb = d; h.trans_b = true;
-  h.C = G; h.ldc = d; h.tri = 1;
+  h.A = G; h.lda = ld; h.trans_a = false;
+  h.B = G; h.ldb = ld; h.trans_b = true;
+  h.C = G; h.ldc = ld; h.tri = 1;
   f.g = gemm_detail::make_kargs(h);
   // the per-task offsets of A and B (128 floats) keep the alignment
   f.dma = gemm_detail::dma_ok(f.g, false, true) ? 1 : 0;
   f.count = 0;
   return f;
+}
+
+// ---------------------------------------------------------------- leading panel in fp64
+// The first 64 columns of G are eliminated in fp64.  When the activations
+// share a non-zero mean, H (and G) is dominated by one large rank-1 part
+// and the Schur complement left after the first columns is orders of
+// magnitude smaller than the entries it comes from: an fp32 update there
+// cancels to a few correct bits.  The first panel takes that part out, so
+// its factor, its inverse and its update of the rest are formed in fp64
+// (the L values stored back and used in the update are the fp32 ones the
+// rest of the factorization reads); everything after it is well scaled and
+// runs in fp32.
+
+// L11 = chol(G11) and X = L11⁻¹ for the leading kb <= 64 columns (identity-
+// padded to 64), one wave: lane i owns row i of the right-looking sweep and
+// column i of the forward substitution.  X goes to Xd (fp64, row-major
+// 64x64) and, rounded, to Linv's leading block; a failed pivot (not
+// positive, or not finite) is recorded in *status and replaced by 1.
+__global__ __launch_bounds__(64) void lead_factor_kernel(const float* __restrict__ G, int64_t ld,
+                                                         int kb, double* __restrict__ Xd,
+                                                         float* __restrict__ Linv,
+                                                         int* __restrict__ status) {
+  __shared__ double A[NB][NB + 1];
+  __shared__ double Xs[NB][NB + 1];
+  const int i = threadIdx.x;
+  for (int k = 0; k < NB; ++k)
+    A[i][k] = (i < kb && k <= i) ? (double)G[(int64_t)i * ld + k] : (i == k ? 1.0 : 0.0);
+  __syncthreads();
+  int bad = -1;
+  for (int j = 0; j < NB; ++j) {
+    double piv = A[j][j];
+    if (!(piv > 0.0) || !(piv < INFINITY)) {
+      bad = bad < 0 ? j : bad;
+      piv = 1.0;
+    }
+    const double ljj = sqrt(piv), inv = 1.0 / ljj;
+    __syncthreads();                       // A[j][j] read by every lane
+    if (i == j) A[j][j] = ljj;
+    if (i > j) A[i][j] *= inv;
+    __syncthreads();                       // column j of L published
+    if (i > j) {
+      const double lij = A[i][j];
+      for (int k = j + 1; k <= i; ++k) A[i][k] = fma(-lij, A[k][j], A[i][k]);
+    }
+    __syncthreads();
+  }
+  // column c of X: X[r][c] = (δ_rc − Σ_{c<=k<r} L[r][k]·X[k][c]) / L[r][r]
+  const int c = i;
+  for (int r = 0; r < NB; ++r) {
+    double v = 0.0;
+    if (r >= c) {
+      v = (r == c) ? 1.0 : 0.0;
+      for (int k = c; k < r; ++k) v = fma(-A[r][k], Xs[k][c], v);
+      v /= A[r][r];
+    }
+    Xs[r][c] = v;
+  }
+  for (int r = 0; r < NB; ++r) Xd[r * NB + i] = Xs[r][i];
+  if (i < kb)
+    for (int r = 0; r < kb; ++r) Linv[(int64_t)r * ld + i] = (float)Xs[r][i];
+  if (i == 0 && bad >= 0 && bad < kb) atomicMin(status, bad);
+}
+
+// L21 = G21·Xᵀ in fp64 for rows 64 + 64·blockIdx.x .. +63 (below the
+// leading block), rounded to fp32 in place: thread t takes row t % 64 and
+// columns 16·(t / 64) .. +15.
+__global__ __launch_bounds__(256) void lead_solve_kernel(float* __restrict__ G, int64_t d, int64_t ld,
+                                                         const double* __restrict__ Xd) {
+  __shared__ double Xs[NB][NB + 1];
+  __shared__ double Rs[NB][NB + 1];
+  const int t = threadIdx.x;
+  const int64_t r0 = NB + (int64_t)blockIdx.x * NB;
+  for (int e = t; e < NB * NB; e += 256) {
+    const int a = e >> 6, b = e & 63;
+    Xs[a][b] = Xd[e];
+    Rs[a][b] = r0 + a < d ? (double)G[(r0 + a) * ld + b] : 0.0;
+  }
+  __syncthreads();
+  const int rr = t & 63, j0 = 16 * (t >> 6);
+  if (r0 + rr >= d) return;
+  double out[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int j = j0 + q;
+    double v = 0.0;
+    for (int k = 0; k <= j; ++k) v = fma(Rs[rr][k], Xs[j][k], v);
+    out[q] = v;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) G[(r0 + rr) * ld + j0 + q] = (float)out[q];
+}
+
+// G22 −= L21·L21ᵀ over the lower triangle of the trailing (d−64)² block, in
+// fp64 from the stored fp32 L21 (exact products), rounded once.  One 64x64
+// lower tile (by >= bx) per workgroup; thread t takes rows 4·(t / 16) .. +3
+// and columns 4·(t % 16) .. +3 of the tile.
+__global__ __launch_bounds__(256) void lead_update_kernel(float* __restrict__ G, int64_t d, int64_t ld) {
+  int by = (int)((sqrtf(8.f * (float)blockIdx.x + 1.f) - 1.f) * 0.5f);
+  while ((by + 1) * (by + 2) / 2 <= (int)blockIdx.x) ++by;
+  while (by * (by + 1) / 2 > (int)blockIdx.x) --by;
+  const int bx = (int)blockIdx.x - by * (by + 1) / 2;
+  __shared__ double Ra[NB][NB + 1];
+  __shared__ double Rb[NB][NB + 1];
+  const int t = threadIdx.x;
+  const int64_t ra0 = NB + (int64_t)by * NB, rb0 = NB + (int64_t)bx * NB;
+  for (int e = t; e < NB * NB; e += 256) {
+    const int a = e >> 6, k = e & 63;
+    Ra[a][k] = ra0 + a < d ? (double)G[(ra0 + a) * ld + k] : 0.0;
+    Rb[a][k] = rb0 + a < d ? (double)G[(rb0 + a) * ld + k] : 0.0;
+  }
+  __syncthreads();
+  const int i0 = 4 * (t >> 4), j0 = 4 * (t & 15);
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int k = 0; k < NB; ++k) {
+    double x[4], y[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) { x[a] = Ra[i0 + a][k]; y[a] = Rb[j0 + a][k]; }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = fma(x[a], y[b], acc[a][b]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t r = ra0 + i0 + a;
+    if (r >= d) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t c = rb0 + j0 + b;
+      if (c <= r) G[r * ld + c] = (float)((double)G[r * ld + c] - acc[a][b]);
+    }
+  }
 }
 
 struct PrepWs {
@@ -843,8 +979,10 @@ PrepWs carve(void* ws, int64_t d) {
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t d) {
+  // T: the doubling's products (d²/2 + 64² floats); the leading panel's fp64
+  // inverse (64² doubles) uses it first
   return 512 + 3 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
-         align_up((size_t)(d * d / 2 + NB * NB) * 4);
+         align_up((size_t)(d * d / 2 + 2 * NB * NB) * 4);
 }
 
 hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, float* U,
@@ -884,17 +1022,38 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();
 
-  // blocked right-looking Cholesky of G (lower), 64-wide panels, one launch
-  // per panel, with the trailing updates in two levels
-  const std::vector<std::vector<uint32_t>> far = chol_sched::far_schedule(d);
-  FarJob fj = far_base(w.G, d);
-  for (int64_t k = 0; k * NB < d; ++k) {
+  std::unique_ptr<TimerScope> chol_ts(new TimerScope(kTimerChol, s));
+  // the leading 64 columns in fp64 (lead_factor_kernel), then the blocked
+  // right-looking Cholesky (lower) of the trailing n x n block in fp32,
+  // 64-wide panels, one launch per panel, trailing updates in two levels
+  {
+    double* Xd = reinterpret_cast<double*>(w.T);
+    lead_factor_kernel<<<1, 64, 0, s>>>(w.G, d, (int)std::min<int64_t>(NB, d), Xd, w.Linv, w.status);
+    GQ_CHECK();
+    if (d > NB) {
+      const int64_t nb = ceil_div(d - NB, NB);
+      lead_solve_kernel<<<(unsigned)nb, 256, 0, s>>>(w.G, d, d, Xd);
+      GQ_CHECK();
+      lead_update_kernel<<<(unsigned)(nb * (nb + 1) / 2), 256, 0, s>>>(w.G, d, d);
+      GQ_CHECK();
+    }
+  }
+  const int64_t n = std::max<int64_t>(d - NB, 0);
+  float* G1 = w.G + NB * d + NB;
+  float* L1 = w.Linv + NB * d + NB;
+  const std::vector<std::vector<uint32_t>> far = chol_sched::far_schedule(n);
+  // GPTQ_PANEL_SPIN_LIMIT (diagnostics only) shortens the panels' bounded
+  // flag waits so that the stall report can be exercised
+  int spin_limit = kSpinLimit;
+  if (const char* sl = std::getenv("GPTQ_PANEL_SPIN_LIMIT")) spin_limit = std::max(0, std::atoi(sl));
+  FarJob fj = far_base(G1, n, d);
+  for (int64_t k = 0; k * NB < n; ++k) {
     const int64_t k0 = k * NB;
-    const int kb = (int)std::min<int64_t>(NB, d - k0);
-    const int64_t nr = d - (k0 + kb);
+    const int kb = (int)std::min<int64_t>(NB, n - k0);
+    const int64_t nr = n - (k0 + kb);
     const int nP = (int)std::max<int64_t>(1, ceil_div(nr, NB));
-    PanelArgs pa{w.G, d, (int)k0, kb, w.Linv, w.status, nP};
-    const TileJob nj = near_job(w.G, d, k);
+    PanelArgs pa{G1, n, (int)k0, kb, L1, w.status, nP, spin_limit, d, NB};
+    const TileJob nj = near_job(G1, n, d, k);
     const std::vector<uint32_t>& ft = far[(size_t)k];
     // far tasks beyond one launch's list run first, in launches of their own
     size_t done = 0;
@@ -911,7 +1070,9 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     GQ_CHECK();
   }
 
+  chol_ts.reset();
   // triangular inverse by recursive doubling on 64-aligned blocks
+  TimerScope inv_ts(kTimerInverse, s);
   for (int64_t sz = NB; sz < d; sz *= 2) {
     const int64_t full = d / (2 * sz);                 // pairs with a full C block
     const int64_t rag0 = full * 2 * sz;                // start of a ragged pair, if any

@@ -30,7 +30,12 @@
 namespace gq {
 namespace {
 
-struct QWs { float* Wk; float* Err; uint8_t* codes; int* inv; int* src; float* Upad; };
+struct QWs {
+  float* Wk; float* Err; uint8_t* codes; int* inv; int* src; float* Upad;
+  float* S; uint8_t* Z; float* RL;   // stacked rows' scales/zeros/losses (several layers)
+};
+// group-count bound used for sizing (the smallest group the sweep runs is 32)
+inline int64_t max_groups(int64_t d) { return ceil_div(d, 32); }
 
 // Working copy and codes are padded to whole blocks (dp = ceil(d/128)·128).
 QWs carve(void* ws, int64_t m, int64_t d) {
@@ -42,7 +47,10 @@ QWs carve(void* ws, int64_t m, int64_t d) {
   w.codes = reinterpret_cast<uint8_t*>(p); p += align_up((size_t)m * dp);
   w.inv = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
   w.src = reinterpret_cast<int*>(p); p += align_up((size_t)dp * 4);
-  w.Upad = reinterpret_cast<float*>(p);
+  w.Upad = reinterpret_cast<float*>(p); p += align_up((size_t)kBlock * kBlock * 4);
+  w.S = reinterpret_cast<float*>(p); p += align_up((size_t)m * max_groups(d) * 4);
+  w.Z = reinterpret_cast<uint8_t*>(p); p += align_up((size_t)m * max_groups(d));
+  w.RL = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -528,7 +536,10 @@ hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_p
       a.maxq = maxq; a.sym = p.sym; a.scales = scales; a.zeros = zeros; a.ng = ng; a.g = g;
       a.Err = w.Err + (b0 - sb0); a.lde = lde;
       a.codes = w.codes; a.row_loss = row_loss;
-      if ((e = launch_sweep<G>(a, s)) != hipSuccess) return e;
+      {
+        TimerScope ts(kTimerSweep, s);
+        if ((e = launch_sweep<G>(a, s)) != hipSuccess) return e;
+      }
       const int64_t b1 = b0 + bw;
       if (b1 < se) {  // the rest of the super-block: W[:, b1:se] −= Err_b · U[b, b1:se]
         GemmArgs u{};
@@ -537,6 +548,7 @@ hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_p
         u.A = w.Err + (b0 - sb0); u.lda = lde; u.trans_a = false;
         u.B = U + b0 * d + b1; u.ldb = d; u.trans_b = false;
         u.C = w.Wk + b1; u.ldc = dp; u.tri = 0;
+        TimerScope ts(kTimerUpdate, s);
         if ((e = gemm_f32(u, s)) != hipSuccess) return e;
       }
     }
@@ -547,6 +559,7 @@ hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_p
       u.A = w.Err; u.lda = lde; u.trans_a = false;
       u.B = U + sb0 * d + se; u.ldb = d; u.trans_b = false;
       u.C = w.Wk + se; u.ldc = dp; u.tri = 0;
+      TimerScope ts(kTimerUpdate, s);
       if ((e = gemm_f32(u, s)) != hipSuccess) return e;
     }
   }
@@ -559,7 +572,87 @@ size_t quantize_ws_bytes(int64_t m, int64_t d) {
   const int64_t dp = ceil_div(d, kBlock) * kBlock;
   return align_up((size_t)m * dp * 4) + align_up((size_t)m * kSuper * kBlock * 4) +
          align_up((size_t)m * dp) +
-         align_up((size_t)d * 4) + align_up((size_t)dp * 4) + align_up((size_t)kBlock * kBlock * 4);
+         align_up((size_t)d * 4) + align_up((size_t)dp * 4) + align_up((size_t)kBlock * kBlock * 4) +
+         align_up((size_t)m * max_groups(d) * 4) + align_up((size_t)m * max_groups(d)) +
+         align_up((size_t)m * 4);
+}
+
+// Several layers against one factor: their rows are stacked into one working
+// matrix (rows are independent problems sharing H and U), swept together,
+// and written back per layer.  Every row's arithmetic is the one a separate
+// call would do (the block products' k order does not depend on the row
+// count), so the results are bitwise those of separate calls.  With one
+// layer the scales, zeros and losses go straight to its outputs.
+hipError_t quantize_layers_launch(const LayerIO* L, int n, int64_t d, const float* U,
+                                  const int32_t* perm, const uint8_t* dead, const gptq_params& p,
+                                  int32_t* g_idx, void* ws, hipStream_t s) {
+  int64_t M = 0;
+  for (int i = 0; i < n; ++i) M += L[i].m;
+  QWs w = carve(ws, M, d);
+  const int64_t g = (p.group_size <= 0 || p.group_size >= d) ? d : p.group_size;
+  const int ng = (int)ceil_div(d, g);
+  const int64_t dp = ceil_div(d, kBlock) * kBlock;
+  const bool single = n == 1;
+  float* S = single ? L[0].scales : w.S;
+  uint8_t* Z = single ? L[0].zeros : w.Z;
+  float* RL = single ? L[0].row_loss : w.RL;
+  hipError_t e;
+  const bool rows_path = perm && dp <= kRowLds;
+  if (rows_path) {
+    src_index_kernel<<<(unsigned)ceil_div(dp, 256), 256, 0, s>>>(perm, dead, (int)d, (int)dp, w.src,
+                                                                 w.inv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  int64_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t m = L[i].m;
+    const int esz = L[i].dt == GPTQ_F32 ? 4 : 2;
+    const int vec_in = ((uintptr_t)L[i].W % 16 == 0) && ((L[i].ld_w * esz) % 16 == 0);
+    const unsigned gy4 = (unsigned)std::min<int64_t>(ceil_div(m, 4), 65535);
+    float* rl = RL ? RL + off : nullptr;
+    if (rows_path)
+      init_rows_kernel<<<(unsigned)std::min<int64_t>(m, 1024), 256, (size_t)dp * 4, s>>>(
+          L[i].W, L[i].dt, L[i].ld_w, m, (int)d, (int)dp, w.src, w.Wk + off * dp, rl, vec_in);
+    else
+      init_kernel<<<dim3((unsigned)ceil_div(dp, 2048), gy4), 256, 0, s>>>(
+          L[i].W, L[i].dt, L[i].ld_w, m, d, dp, perm, dead, w.Wk + off * dp, w.inv, rl, vec_in);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    off += m;
+  }
+  switch (g) {
+    case 32: e = run_blocks<32>(w, M, d, U, p, g, ng, S, Z, RL, s); break;
+    case 64: e = run_blocks<64>(w, M, d, U, p, g, ng, S, Z, RL, s); break;
+    case 128: e = run_blocks<128>(w, M, d, U, p, g, ng, S, Z, RL, s); break;
+    default: e = run_blocks<0>(w, M, d, U, p, g, ng, S, Z, RL, s); break;
+  }
+  if (e != hipSuccess) return e;
+  off = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t m = L[i].m;
+    const unsigned gy = (unsigned)std::min<int64_t>(m, 65535);
+    float* W_hat = L[i].W_hat;
+    int32_t* gi = i == 0 ? g_idx : nullptr;
+    const int vec_w = W_hat && ((uintptr_t)W_hat % 16 == 0) && (d % 4 == 0);
+    if (perm && dp <= kFinLds)
+      finalize_rows_kernel<<<(unsigned)std::min<int64_t>(m, 1024), 256, (size_t)dp * 5, s>>>(
+          w.Wk + off * dp, w.codes + off * dp, w.inv, m, (int)d, (int)dp, p.bits, g, L[i].qweight,
+          W_hat, gi, vec_w);
+    else
+      finalize_kernel<<<dim3((unsigned)ceil_div(d, 2048), gy), 256, 0, s>>>(
+          w.Wk + off * dp, w.codes + off * dp, w.inv, m, d, dp, p.bits, g, L[i].qweight, W_hat, gi,
+          vec_w, perm ? 0 : 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!single) {
+      e = hipMemcpyAsync(L[i].scales, w.S + off * ng, (size_t)m * ng * 4, hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(L[i].zeros, w.Z + off * ng, (size_t)m * ng, hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess && L[i].row_loss)
+        e = hipMemcpyAsync(L[i].row_loss, w.RL + off, (size_t)m * 4, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+    }
+    off += m;
+  }
+  return hipSuccess;
 }
 
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int64_t ld_w,
@@ -567,42 +660,8 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
                            const gptq_params& p, uint32_t* qweight, float* scales,
                            uint8_t* zeros, float* W_hat, int32_t* g_idx, float* row_loss,
                            void* ws, hipStream_t s) {
-  QWs w = carve(ws, m, d);
-  const int64_t g = (p.group_size <= 0 || p.group_size >= d) ? d : p.group_size;
-  const int ng = (int)ceil_div(d, g);
-  const unsigned gy = (unsigned)std::min<int64_t>(m, 65535);
-  const int64_t dp = ceil_div(d, kBlock) * kBlock;
-  const int esz = w_dtype == GPTQ_F32 ? 4 : 2;
-  const int vec_in = ((uintptr_t)W % 16 == 0) && ((ld_w * esz) % 16 == 0);
-  const unsigned gy4 = (unsigned)std::min<int64_t>(ceil_div(m, 4), 65535);
-  if (perm && dp <= kRowLds) {
-    src_index_kernel<<<(unsigned)ceil_div(dp, 256), 256, 0, s>>>(perm, dead, (int)d, (int)dp, w.src,
-                                                                 w.inv);
-    hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
-    init_rows_kernel<<<(unsigned)std::min<int64_t>(m, 1024), 256, (size_t)dp * 4, s>>>(
-        W, w_dtype, ld_w, m, (int)d, (int)dp, w.src, w.Wk, row_loss, vec_in);
-  } else
-    init_kernel<<<dim3((unsigned)ceil_div(dp, 2048), gy4), 256, 0, s>>>(W, w_dtype, ld_w, m, d, dp,
-                                                                      perm, dead, w.Wk, w.inv,
-                                                                      row_loss, vec_in);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  switch (g) {
-    case 32: e = run_blocks<32>(w, m, d, U, p, g, ng, scales, zeros, row_loss, s); break;
-    case 64: e = run_blocks<64>(w, m, d, U, p, g, ng, scales, zeros, row_loss, s); break;
-    case 128: e = run_blocks<128>(w, m, d, U, p, g, ng, scales, zeros, row_loss, s); break;
-    default: e = run_blocks<0>(w, m, d, U, p, g, ng, scales, zeros, row_loss, s); break;
-  }
-  if (e != hipSuccess) return e;
-  const int vec_w = W_hat && ((uintptr_t)W_hat % 16 == 0) && (d % 4 == 0);
-  if (perm && dp <= kFinLds)
-    finalize_rows_kernel<<<(unsigned)std::min<int64_t>(m, 1024), 256, (size_t)dp * 5, s>>>(
-        w.Wk, w.codes, w.inv, m, (int)d, (int)dp, p.bits, g, qweight, W_hat, g_idx, vec_w);
-  else
-    finalize_kernel<<<dim3((unsigned)ceil_div(d, 2048), gy), 256, 0, s>>>(
-        w.Wk, w.codes, w.inv, m, d, dp, p.bits, g, qweight, W_hat, g_idx, vec_w, perm ? 0 : 1);
-  return hipGetLastError();
+  const LayerIO one{W, w_dtype, m, ld_w, qweight, scales, zeros, W_hat, row_loss};
+  return quantize_layers_launch(&one, 1, d, U, perm, dead, p, g_idx, ws, s);
 }
 
 }  // namespace gq

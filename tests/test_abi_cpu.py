@@ -150,3 +150,115 @@ def test_workspace_sizes():
     q = ws(2, 4096, 4096, 0, ctypes.byref(p))
     assert q >= 4096 * 4096 * 5  # fp32 working copy + codes
     assert ws(1, 0, 4096, 0, ctypes.byref(p)) >= 2 * 4096 * 4096 * 4
+
+
+def test_quantize_rejects_act_order_without_perm():
+    """U is factored in the act-order permutation: quantizing without it would
+    pair columns with the wrong rows of U."""
+    assert _quant(_params(act_order=1)) == n.ERR_INVALID_ARG
+    assert "perm" in n.last_error()
+
+
+def test_prepare_status_mapping():
+    """Device status words of the factorization -> the call's status: a stall
+    of any wave wins over a failed pivot, and a failed pivot is reported in
+    the quantization order (the factorization runs reversed)."""
+    prog = r"""
+#include <cstdio>
+#include <climits>
+#include "status_map.hpp"
+int main() {
+  const int cases[][2] = {{INT_MAX, 0}, {5, 0}, {0, 0}, {99, 0}, {INT_MAX, 1}, {5, 1}, {100, 0}, {-3, 0}};
+  for (auto& c : cases) {
+    long long piv = 7;
+    int64_t p = 7;
+    int rc = gq::prepare_status(c[0], c[1], 100, &p);
+    piv = p;
+    std::printf("%d %lld\n", rc, piv);
+  }
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "t.cpp")
+        exe = os.path.join(td, "t")
+        open(c, "w").write(prog)
+        subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                        "-I", os.path.join(ROOT, "post_weight_quantization_16_amd", "csrc"), c,
+                        "-o", exe], check=True)
+        got = [tuple(int(v) for v in line.split())
+               for line in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines()]
+    assert got == [(n.OK, -1), (n.ERR_NOT_SPD, 94), (n.ERR_NOT_SPD, 99), (n.ERR_NOT_SPD, 0),
+                   (n.ERR_INTERNAL, -1), (n.ERR_INTERNAL, -1), (n.ERR_INTERNAL, -1),
+                   (n.ERR_INTERNAL, -1)]
+
+
+def test_binding_checks_tensor_arguments():
+    """The binding hands raw pointers to the library, so it refuses tensors the
+    library would misread (wrong dtype, shape, strides) before any call."""
+    import torch
+
+    import post_weight_quantization_16_amd as g
+    d = 16
+    X = torch.zeros(32, d, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="float32"):
+        g.hessian_accumulate(torch.zeros(d, d, dtype=torch.float64), X)
+    with pytest.raises(ValueError, match="shape"):
+        g.hessian_accumulate(torch.zeros(d, d + 1), X)
+    with pytest.raises(ValueError, match="contiguous"):
+        g.hessian_accumulate(torch.zeros(2 * d, d)[::2], X)
+    with pytest.raises(ValueError, match="dtype"):
+        g.hessian_accumulate(torch.zeros(d, d), X.to(torch.int32))
+    with pytest.raises(ValueError, match="unit column stride"):
+        g.hessian_accumulate(torch.zeros(d, d), torch.zeros(d, 32, dtype=torch.bfloat16).t())
+    with pytest.raises(ValueError, match="float32"):
+        g.prepare_hinv(torch.zeros(d, d, dtype=torch.float64), g.GPTQParams())
+    with pytest.raises(ValueError, match="shape"):
+        g.prepare_hinv(torch.zeros(d, d + 1), g.GPTQParams())
+    W = torch.zeros(8, d, dtype=torch.bfloat16)
+    ok = dict(U=torch.zeros(d, d), perm=torch.zeros(d, dtype=torch.int32),
+              dead=torch.zeros(d, dtype=torch.uint8))
+    for k, bad, msg in [("U", torch.zeros(d, d, dtype=torch.float64), "float32"),
+                        ("U", torch.zeros(d + 1, d + 1), "shape"),
+                        ("U", torch.zeros(d, 2 * d)[:, ::2], "contiguous"),
+                        ("perm", torch.zeros(d, dtype=torch.int64), "int32"),
+                        ("dead", torch.zeros(d, dtype=torch.bool), "uint8")]:
+        kw = dict(ok)
+        kw[k] = bad
+        with pytest.raises(ValueError, match=msg):
+            g.quantize_layer(W, g.Prepared(**kw), g.GPTQParams())
+    with pytest.raises(ValueError, match="act_order"):
+        g.quantize_layer(W, g.Prepared(**ok, natural=True), g.GPTQParams(act_order=True))
+
+
+def test_export_validation():
+    L = n.lib()
+    ex = L.gptq_export
+    assert ex(5, 4, 64, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == n.ERR_INVALID_ARG
+    assert ex(3, 0, 64, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == n.ERR_INVALID_ARG
+    assert ex(3, 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == n.ERR_INVALID_ARG
+    assert ex(3, 4, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == n.ERR_INVALID_ARG
+    assert ex(3, 4, 64, 65, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == n.ERR_INVALID_ARG
+    assert ex(3, 4, 64, 1, None, FAKE, FAKE, FAKE, None, None, None) == n.ERR_INVALID_ARG
+    assert ex(3, 4, 64, 1, FAKE, None, FAKE, None, FAKE, None, None) == n.ERR_INVALID_ARG
+    assert ex(3, 4, 64, 1, FAKE, FAKE, None, None, None, FAKE, None) == n.ERR_INVALID_ARG
+    # nothing requested: a no-op that touches nothing
+    assert ex(3, 4, 64, 1, None, None, None, None, None, None, None) == n.OK
+
+
+def test_obq_validation():
+    L = n.lib()
+    f = L.gptq_obq_layer
+    p = _params(group_size=-1)
+    args = lambda **kw: [kw.get("W", FAKE), n.BF16, kw.get("m", 8), kw.get("d", 64), kw.get("ld", 64),
+                         kw.get("H", FAKE), ctypes.byref(kw.get("p", p)), FAKE, FAKE, FAKE, None, None,
+                         None, FAKE, kw.get("ws_bytes", 1 << 30), None]
+    assert f(*args(W=None)) == n.ERR_INVALID_ARG
+    assert f(*args(H=None)) == n.ERR_INVALID_ARG
+    assert f(*args(ld=10)) == n.ERR_INVALID_ARG
+    assert f(*args(p=_params(group_size=32))) == n.ERR_UNSUPPORTED
+    assert f(*args(p=_params(group_size=-1, act_order=1))) == n.ERR_UNSUPPORTED
+    assert f(*args(d=129, ld=129)) == n.ERR_UNSUPPORTED
+    assert f(*args(ws_bytes=16)) == n.ERR_WORKSPACE
+    assert L.gptq_workspace_bytes(3, 8, 129, 0, ctypes.byref(p)) == 0
+    assert L.gptq_workspace_bytes(3, 8, 128, 0, ctypes.byref(p)) >= 128 * 128 * 8
