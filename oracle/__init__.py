@@ -34,6 +34,9 @@ section; "the pages" are the five web pages on GPTQ this path is built from):
   order (smallest saliency first, every row its own order), the comparator
   for GPTQ's fixed order ("GPTQ: Mathematical Foundations ...": OBS and OBQ,
   The Computational Bottleneck of OBQ, The GPTQ Algorithmic Innovations 1).
+* ``w4a16`` -- inference with the exported weights: dequantize to the
+  activations' 16-bit format and multiply ("GPTQ: Mathematical Foundations
+  ...", Inference Execution and Modern Kernel Architectures).
 * ``metrics`` -- layer output error, brute-force optimum on tiny layers, and
   the loss identity that follows from the OBS error penalty.
 
@@ -50,4 +53,5 @@ from .prepare import prepare, dead_fix, act_order_perm, inverse_cholesky_upper  
 from .gptq import gptq_sweep, gptq_layer, FollowReport  # noqa: F401
 from .obs import obs_sequential  # noqa: F401
 from .obq import obq_row, obq_layer  # noqa: F401
+from . import w4a16  # noqa: F401
 from .metrics import layer_error, layer_error_rows, brute_force_row, loss_identity_rhs  # noqa: F401
