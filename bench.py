@@ -22,6 +22,7 @@ METRIC = "ms per layer quantize (4096×4096, 4-bit g128) & weights/s; % MFMA pea
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_TFLOPS = 78.6     # MI355X fp64 (vector and matrix)
 
 
 def log(*a):
@@ -149,6 +150,84 @@ def cpu_baseline(wl, W, X, tok_sample, row_sample):
     }
 
 
+def time_events(fn, reps, stream):
+    """Average milliseconds of fn() over reps calls, HIP events on `stream`."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def extras(gq, torch, wl, W, X, params, H, ws_h, ws_p, stream):
+    """Throughput of the rows beyond the single layer, on the same inputs:
+    several layers against one factor, the exported layer's W4A16 product, and
+    the OBQ comparator on a tiny layer."""
+    import numpy as np
+    import synth
+    out = {}
+    m, d = W.shape
+    # three layers fed the same X (query/key/value): one H, one factor, one call
+    Ws = [W] + [torch.from_numpy(synth.make_weights(wl.scaled(seed=wl.seed + 100 + i)).view(np.int16))
+                .view(torch.bfloat16).to(W.device) for i in range(2)]
+    ws_q3 = torch.empty(gq.workspace_bytes(2, 3 * m, d, 0, params), dtype=torch.uint8, device=W.device)
+
+    def batched():
+        H.zero_()
+        gq.hessian_accumulate(H, X, ws=ws_h)
+        prep = gq.prepare_hinv(H, params, ws=ws_p)
+        gq.quantize_layers(Ws, prep, params, ws=ws_q3)
+
+    def separate():
+        H.zero_()
+        gq.hessian_accumulate(H, X, ws=ws_h)
+        prep = gq.prepare_hinv(H, params, ws=ws_p)
+        for Wi in Ws:
+            gq.quantize_layer(Wi, prep, params, ws=ws_q3)
+
+    tb, ts = time_events(batched, 5, stream), time_events(separate, 5, stream)
+    out["three_layers_one_factor"] = {
+        "shape": f"3 x {m}x{d}, one H over {X.shape[0]} tokens", "ms": tb,
+        "weights_per_s": 3 * m * d / (tb * 1e-3), "ms_separate_calls": ts,
+        "weights_per_s_separate_calls": 3 * m * d / (ts * 1e-3)}
+    # W4A16 product with the exported headline layer (4-bit, g128)
+    H.zero_()
+    gq.hessian_accumulate(H, X, ws=ws_h)
+    prep = gq.prepare_hinv(H, params, ws=ws_p)
+    q = gq.quantize_layer(W, prep, params)
+    ex = gq.export(q, params, d)
+    ng = ex.scales_f16.shape[1]
+    for M in (1, 64):
+        A = torch.randn(M, d, device=W.device).to(torch.float16)
+        C = torch.empty(M, m, device=W.device)
+        t = time_events(lambda: gq.w4a16_gemm(A, ex, params.bits, params.group_size, out=C), 50, stream)
+        wbytes = m * ((d * params.bits + 31) // 32) * 4 + 2 * 2 * m * ng
+        byts = wbytes + M * d * 2 + M * m * 4
+        flop = 2 * M * m * d
+        out[f"w4a16_M{M}"] = {
+            "ms": t, "GB_per_s": byts / (t * 1e-3) / 1e9, "frac_hbm": byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "TFLOP_per_s": flop / (t * 1e-3) / 1e12,
+            "frac_f16_mfma": flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bytes": byts}
+    # OBQ comparator on a tiny layer: 2048 rows x 128 columns
+    Wt = torch.randn(2048, 128, device=W.device) * 0.02
+    Xt = torch.randn(4096, 128, device=W.device).to(torch.bfloat16)
+    Ht = torch.zeros(128, 128, device=W.device)
+    gq.hessian_accumulate(Ht, Xt)
+    po = gq.GPTQParams(bits=4, group_size=-1)
+    t = time_events(lambda: gq.obq_layer(Wt, Ht, po), 3, stream)
+    dd = 128
+    flop = 2048 * sum(2 * (dd - k) ** 2 for k in range(dd))   # per-step downdate, fp64
+    out["obq_2048x128"] = {"ms": t, "weights_per_s": 2048 * 128 / (t * 1e-3),
+                           "fp64_TFLOP_per_s": flop / (t * 1e-3) / 1e12,
+                           "frac_fp64_peak": flop / (t * 1e-3) / 1e12 / PEAK_FP64_TFLOPS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b-attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the multi-layer, W4A16 and OBQ throughput figures")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: all)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle row sample (0: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -289,6 +370,9 @@ def main():
             "traffic": hessian_traffic(),
         },
     }
+    if not args.no_extras:
+        log("bench: multi-layer, W4A16 and OBQ figures ...")
+        result["extras"] = extras(gq, torch, wl, W, X, params, H, ws_h, ws_p, stream)
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(wl, W_host, X_host,

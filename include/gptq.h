@@ -245,6 +245,27 @@ int gptq_export(int bits, int64_t d_out, int64_t d_in, int64_t n_groups, const u
                 const float* scales, const uint8_t* zeros, uint32_t* qweight_dense,
                 uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream);
 
+/* Inference with an exported layer: C = A·Ŵᵀ ("Foundations", Inference
+ * Execution and Modern Kernel Architectures: the FP16xINT4 pipeline --
+ * dequantize the packed codes in registers as (q − zero)·scale, multiply with
+ * the 16-bit activations, accumulate in fp32).  Each Ŵ value is the exact
+ * product (q − z)·s of the 16-bit zero and scale, rounded once to the
+ * activations' format; products are exact and accumulate in fp32.
+ *  A          [M x K] 16-bit activations of a_dtype (GPTQ_F16 or GPTQ_BF16),
+ *             row stride lda >= K.
+ *  qweight    [N x ceil(K·bits/32)] uint32, the dense layout of gptq_export;
+ *             bits 2, 3, 4 or 8.
+ *  scales_f16, zeros_f16   [N x n_groups] IEEE half (gptq_export).
+ *  g_idx      [K] group of each column (act-order layers) or NULL: column k
+ *             is then in group k / group_size (group_size -1: one group).
+ *  C          out [M x N] fp32, row stride ldc >= N.
+ * M <= 4 runs a GEMV bound by the weights' HBM traffic; larger M an MFMA
+ * product.  Asynchronous; argument errors only. */
+int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
+                    const uint32_t* qweight, int bits, const uint16_t* scales_f16,
+                    const uint16_t* zeros_f16, const int32_t* g_idx, int group_size,
+                    int64_t n_groups, int64_t N, float* C, int64_t ldc, gptq_stream stream);
+
 /* Per-stage timing, for measurement only.  gptq_timing(1) clears what was
  * recorded and starts bracketing, on the caller's stream, the launches of
  * each timed stage with a pair of HIP events; gptq_timing(0) stops.
@@ -252,7 +273,8 @@ int gptq_export(int bits, int64_t d_out, int64_t d_in, int64_t n_groups, const u
  * milliseconds per stage to ms[0..n-1] (host) and clears the record:
  *   0 lazy block updates (the products W[:, later] −= Err·U[block, later]),
  *   1 in-block sweeps, 2 blocked Cholesky (panels and trailing updates),
- *   3 triangular inverse, 4 Hessian accumulation.
+ *   3 triangular inverse, 4 Hessian accumulation, 5 the factorization's
+ *   leading panel (fp64). 
  * Timing is process-wide; enable it only while one thread issues calls. */
 int gptq_timing(int enable);
 int gptq_timing_read(float* ms, int n);

@@ -21,7 +21,7 @@ from . import _native
 __all__ = [
     "GPTQParams", "GPTQError", "NotPositiveDefinite", "hessian_accumulate", "prepare_hinv",
     "quantize_layer", "quantize", "workspace_bytes", "version", "Prepared", "Quantized",
-    "Exported", "export", "quantize_layers", "obq_layer", "timing", "timing_read",
+    "Exported", "export", "quantize_layers", "obq_layer", "timing", "timing_read", "w4a16_gemm",
 ]
 
 
@@ -311,7 +311,7 @@ def obq_layer(W, H, params: GPTQParams, ws=None):
     return Quantized(qweight, scales, zeros, W_hat, None, row_loss), order
 
 
-TIMED_STAGES = ("block_update", "sweep", "cholesky", "inverse", "hessian")
+TIMED_STAGES = ("block_update", "sweep", "cholesky", "inverse", "hessian", "lead_panel")
 
 
 def timing(enable: bool) -> None:
@@ -351,6 +351,29 @@ def export(q: Quantized, params: GPTQParams, d_in: int) -> Exported:
                                      _dev(qd, "qweight_dense"), _dev(s16, "scales_f16"),
                                      _dev(z16, "zeros_f16"), _stream(dev)))
     return Exported(qd, s16, z16)
+
+
+def w4a16_gemm(A, ex: Exported, bits: int, group_size: int, g_idx=None, out=None):
+    """C = A·Ŵᵀ from an export: A [M, K] float16/bfloat16, C [M, N] float32."""
+    torch = _torch()
+    _matrix_rows(A, "A")
+    M, K = A.shape
+    dev = A.device
+    if A.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("A must be float16 or bfloat16")
+    N, ng = ex.scales_f16.shape
+    _require(ex.qweight, "qweight", torch.int32, (N, (K * bits + 31) // 32), dev)
+    _require(ex.scales_f16, "scales_f16", torch.float16, (N, ng), dev)
+    _require(ex.zeros_f16, "zeros_f16", torch.float16, (N, ng), dev)
+    if g_idx is not None:
+        _require(g_idx, "g_idx", torch.int32, (K,), dev)
+    C = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=dev)
+    _require(C, "C", torch.float32, (M, N), dev)
+    _check(_native.lib().gptq_w4a16_gemm(
+        _dev(A, "A"), _dtype_code(A), M, K, A.stride(0), _dev(ex.qweight, "qweight"), bits,
+        _dev(ex.scales_f16, "scales_f16"), _dev(ex.zeros_f16, "zeros_f16"),
+        _dev(g_idx, "g_idx"), group_size, ng, N, _dev(C, "C"), N, _stream(dev)))
+    return C
 
 
 def quantize(W, X, params: GPTQParams = GPTQParams()):

@@ -25,6 +25,7 @@ EXPORTS = (
     "gptq_quantize_layers",
     "gptq_obq_layer",
     "gptq_export",
+    "gptq_w4a16_gemm",
     "gptq_timing",
     "gptq_timing_read",
     "gptq_last_error",
@@ -96,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.gptq_obq_layer.restype = _int
     L.gptq_export.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.gptq_export.restype = _int
+    L.gptq_w4a16_gemm.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _int, _vp, _vp, _vp, _int,
+                                  _i64, _i64, _vp, _i64, _vp]
+    L.gptq_w4a16_gemm.restype = _int
     L.gptq_timing.argtypes = [_int]
     L.gptq_timing.restype = _int
     L.gptq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), _int]

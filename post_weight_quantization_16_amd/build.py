@@ -30,6 +30,7 @@ SOURCES = [
     ("export.hip", "export.o", []),
     ("obq.hip", "obq.o", []),
     ("timing.hip", "timing.o", []),
+    ("w4a16.hip", "w4a16.o", []),
 ] + [("sweep.hip", f"sweep_g{g}.o", [f"-DGQ_SWEEP_G={g}"]) for g in (0, 32, 64, 128)]
 
 FLAGS = [

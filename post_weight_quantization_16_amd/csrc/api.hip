@@ -32,6 +32,8 @@ int hip_fail(const char* where, hipError_t e) {
 constexpr int64_t kMaxDin = 65536;
 constexpr int64_t kMaxDout = int64_t(1) << 24;
 
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 bool valid_dtype(int dt) { return dt == GPTQ_F32 || dt == GPTQ_BF16 || dt == GPTQ_F16; }
 
 // Checks the quantizer parameters for a layer with d_in columns.
@@ -260,6 +262,30 @@ int gptq_obq_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int6
   if (st != INT_MAX)
     return fail(GPTQ_ERR_NOT_SPD, "damped Hessian is not positive definite (pivot %d); raise percdamp",
                 (int)st);
+  return GPTQ_OK;
+}
+
+int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
+                    const uint32_t* qweight, int bits, const uint16_t* scales_f16,
+                    const uint16_t* zeros_f16, const int32_t* g_idx, int group_size,
+                    int64_t n_groups, int64_t N, float* C, int64_t ldc, gptq_stream stream) {
+  if (!A || !qweight || !scales_f16 || !zeros_f16 || !C)
+    return fail(GPTQ_ERR_INVALID_ARG, "A, qweight, scales, zeros and C must not be NULL");
+  if (a_dtype != GPTQ_F16 && a_dtype != GPTQ_BF16)
+    return fail(GPTQ_ERR_INVALID_ARG, "a_dtype must be GPTQ_F16 or GPTQ_BF16");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_INVALID_ARG, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+  if (M <= 0 || K <= 0 || N <= 0 || K > kMaxDin || N > kMaxDout || M > kMaxDout)
+    return fail(GPTQ_ERR_INVALID_ARG, "M, K and N must be positive (K <= %lld)", (long long)kMaxDin);
+  if (lda < K || ldc < N) return fail(GPTQ_ERR_INVALID_ARG, "lda < K or ldc < N");
+  const int64_t g = (group_size <= 0 || group_size >= K) ? K : group_size;
+  if (!g_idx && g % 32 != 0 && g != K)
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size must be a multiple of 32 (or -1)");
+  if (n_groups < ceil_div64(K, g) || n_groups > K)
+    return fail(GPTQ_ERR_INVALID_ARG, "n_groups must cover the groups of K columns");
+  hipError_t e = gq::w4a16_launch(A, a_dtype, M, K, lda, qweight, bits, scales_f16, zeros_f16,
+                                  g_idx, g, n_groups, N, C, ldc, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("w4a16_gemm", e);
   return GPTQ_OK;
 }
 

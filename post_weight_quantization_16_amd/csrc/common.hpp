@@ -117,7 +117,7 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t m, int64_t d, int
 // (diagnostics, timing.hip): a scope records a HIP event pair around the
 // launches it encloses while timing is enabled.
 enum { kTimerUpdate = 0, kTimerSweep = 1, kTimerChol = 2, kTimerInverse = 3, kTimerHessian = 4,
-       kTimerCount = 5 };
+       kTimerLead = 5, kTimerCount = 6 };
 class TimerScope {
  public:
   TimerScope(int which, hipStream_t s);
@@ -139,6 +139,12 @@ hipError_t obq_launch(const void* W, int w_dtype, int64_t m, int64_t d, int64_t 
                       const float* H, const gptq_params& p, uint32_t* qweight, float* scales,
                       uint8_t* zeros, float* W_hat, int32_t* order, float* row_loss, void* ws,
                       int32_t** status_dev, hipStream_t s);
+
+// ---------------------------------------------------------------- W4A16 inference
+hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
+                        const uint32_t* qweight, int bits, const uint16_t* s16, const uint16_t* z16,
+                        const int32_t* g_idx, int64_t g, int64_t ng, int64_t N, float* C,
+                        int64_t ldc, hipStream_t s);
 
 // ---------------------------------------------------------------- export
 hipError_t export_launch(int bits, int64_t m, int64_t d, int64_t ng, const uint32_t* qweight,

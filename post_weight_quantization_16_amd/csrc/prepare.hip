@@ -833,128 +833,209 @@ FarJob far_base(float* G, int64_t d, int64_t ld) {
 // rest of the factorization reads); everything after it is well scaled and
 // runs in fp32.
 
-// L11 = chol(G11) and X = L11⁻¹ for the leading kb <= 64 columns (identity-
-// padded to 64), one wave: lane i owns row i of the right-looking sweep and
-// column i of the forward substitution.  X goes to Xd (fp64, row-major
-// 64x64) and, rounded, to Linv's leading block; a failed pivot (not
-// positive, or not finite) is recorded in *status and replaced by 1.
-__global__ __launch_bounds__(64) void lead_factor_kernel(const float* __restrict__ G, int64_t ld,
-                                                         int kb, double* __restrict__ Xd,
-                                                         float* __restrict__ Linv,
+// The leading panel in fp64, one launch: every workgroup factors and inverts
+// the 64x64 leading block itself (no workgroup waits for another), then
+// workgroup b solves rows 64 + 64b .. +63 below it, L21 = G21·Xᵀ, and stores
+// them rounded to fp32 in L21b [(d−64) x 64]; workgroup 0 stores X = L11⁻¹
+// (rounded) in X0b [64 x 64] and reports a failed pivot (not positive or not
+// finite; replaced by 1) in *status.  Blocks narrower than 64 (kb < 64) are
+// padded with the identity.
+//
+// Lane i of every wave holds row i; wave w holds columns 16w .. 16w+15 in
+// registers.  Step j of the factorization: the owner of column j scales it by
+// 1/l_jj and publishes it in LDS (one barrier), and every wave updates its
+// later columns, a_ik −= l_ij·l_kj.  X then comes column block by column
+// block, each wave on its own 16 columns with no barrier: for k = 0..63, row
+// k of the block is final once scaled by 1/l_kk, and every later row
+// subtracts l_ik times it (row k reaches the other lanes through LDS: a
+// wave's LDS operations complete in order).
+__global__ __launch_bounds__(256) void lead_panel_kernel(const float* __restrict__ G, int64_t d,
+                                                         int64_t ld, int kb, float* __restrict__ L21b,
+                                                         float* __restrict__ X0b,
                                                          int* __restrict__ status) {
-  __shared__ double A[NB][NB + 1];
+  __shared__ double Lc[NB][NB + 1];   // L by columns as they are published
   __shared__ double Xs[NB][NB + 1];
-  const int i = threadIdx.x;
-  for (int k = 0; k < NB; ++k)
-    A[i][k] = (i < kb && k <= i) ? (double)G[(int64_t)i * ld + k] : (i == k ? 1.0 : 0.0);
-  __syncthreads();
-  int bad = -1;
-  for (int j = 0; j < NB; ++j) {
-    double piv = A[j][j];
-    if (!(piv > 0.0) || !(piv < INFINITY)) {
-      bad = bad < 0 ? j : bad;
-      piv = 1.0;
-    }
-    const double ljj = sqrt(piv), inv = 1.0 / ljj;
-    __syncthreads();                       // A[j][j] read by every lane
-    if (i == j) A[j][j] = ljj;
-    if (i > j) A[i][j] *= inv;
-    __syncthreads();                       // column j of L published
-    if (i > j) {
-      const double lij = A[i][j];
-      for (int k = j + 1; k <= i; ++k) A[i][k] = fma(-lij, A[k][j], A[i][k]);
-    }
-    __syncthreads();
-  }
-  // column c of X: X[r][c] = (δ_rc − Σ_{c<=k<r} L[r][k]·X[k][c]) / L[r][r]
-  const int c = i;
-  for (int r = 0; r < NB; ++r) {
-    double v = 0.0;
-    if (r >= c) {
-      v = (r == c) ? 1.0 : 0.0;
-      for (int k = c; k < r; ++k) v = fma(-A[r][k], Xs[k][c], v);
-      v /= A[r][r];
-    }
-    Xs[r][c] = v;
-  }
-  for (int r = 0; r < NB; ++r) Xd[r * NB + i] = Xs[r][i];
-  if (i < kb)
-    for (int r = 0; r < kb; ++r) Linv[(int64_t)r * ld + i] = (float)Xs[r][i];
-  if (i == 0 && bad >= 0 && bad < kb) atomicMin(status, bad);
-}
-
-// L21 = G21·Xᵀ in fp64 for rows 64 + 64·blockIdx.x .. +63 (below the
-// leading block), rounded to fp32 in place: thread t takes row t % 64 and
-// columns 16·(t / 64) .. +15.
-__global__ __launch_bounds__(256) void lead_solve_kernel(float* __restrict__ G, int64_t d, int64_t ld,
-                                                         const double* __restrict__ Xd) {
-  __shared__ double Xs[NB][NB + 1];
-  __shared__ double Rs[NB][NB + 1];
-  const int t = threadIdx.x;
+  __shared__ double Rs[NB][NB + 1];   // this workgroup's rows of G21
+  __shared__ double dinv[NB];
+  __shared__ int bad;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t r0 = NB + (int64_t)blockIdx.x * NB;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int a = e >> 6, b = e & 63;
-    Xs[a][b] = Xd[e];
-    Rs[a][b] = r0 + a < d ? (double)G[(r0 + a) * ld + b] : 0.0;
+  if (t == 0) bad = INT_MAX;
+  // G21 rows (every load before the stores)
+  {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = t + 256 * u, rr = e >> 6, k = e & 63;
+      v[u] = (r0 + rr < d && k < kb) ? G[(r0 + rr) * ld + k] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = t + 256 * u;
+      Rs[e >> 6][e & 63] = (double)v[u];
+    }
   }
-  __syncthreads();
-  const int rr = t & 63, j0 = 16 * (t >> 6);
-  if (r0 + rr >= d) return;
-  double out[16];
+  double a[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const int j = j0 + q;
-    double v = 0.0;
-    for (int k = 0; k <= j; ++k) v = fma(Rs[rr][k], Xs[j][k], v);
-    out[q] = v;
+    const int k = 16 * w + q;
+    a[q] = (lane < kb && k <= lane) ? (double)G[(int64_t)lane * ld + k] : (lane == k ? 1.0 : 0.0);
   }
+  __syncthreads();
+  for (int j = 0; j < NB; ++j) {
+    if ((j >> 4) == w) {   // owner: column j = register j & 15
+      double cj = 0.0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) G[(r0 + rr) * ld + j0 + q] = (float)out[q];
+      for (int q = 0; q < 16; ++q) cj = (q == (j & 15)) ? a[q] : cj;
+      double piv = __shfl(cj, j);
+      if (!(piv > 0.0) || !(piv < INFINITY)) {
+        if (lane == 0) atomicMin(&bad, j);
+        piv = 1.0;
+      }
+      const double ljj = sqrt(piv), inv = 1.0 / ljj;
+      const double l = lane > j ? cj * inv : (lane == j ? ljj : 0.0);
+      Lc[lane][j] = l;
+      if (lane == 0) dinv[j] = inv;
+    }
+    __syncthreads();
+    const double li = Lc[lane][j];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int k = 16 * w + q;
+      if (k > j) a[q] = fma(-li, Lc[k][j], a[q]);
+    }
+  }
+  // X, column block of wave w: x[q] = X[lane][16w + q]
+  double x[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) x[q] = (lane == 16 * w + q) ? 1.0 : 0.0;
+  for (int k = 0; k < NB; ++k) {
+    const double dk = dinv[k], lik = Lc[lane][k];
+    if (lane == k) {   // row k is final: publish it
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        x[q] *= dk;
+        Xs[k][16 * w + q] = x[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const double xk = Xs[k][16 * w + q];
+      if (lane > k) x[q] = fma(-lik, xk, x[q]);
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) X0b[lane * NB + 16 * w + q] = (float)x[q];
+    if (t == 0 && bad < kb) atomicMin(status, bad);
+  }
+  // L21 rows r0 + lane, columns 16w + q: Σ_{k <= j} G21[lane][k]·X[j][k]
+  if (r0 + lane < d && r0 < d) {
+    double acc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0;
+    for (int k = 0; k < NB; ++k) {
+      const double g = Rs[lane][k];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = fma(g, Xs[16 * w + q][k], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) L21b[(r0 - NB + lane) * NB + 16 * w + q] = (float)acc[q];
+  }
 }
 
 // G22 −= L21·L21ᵀ over the lower triangle of the trailing (d−64)² block, in
-// fp64 from the stored fp32 L21 (exact products), rounded once.  One 64x64
-// lower tile (by >= bx) per workgroup; thread t takes rows 4·(t / 16) .. +3
-// and columns 4·(t % 16) .. +3 of the tile.
-__global__ __launch_bounds__(256) void lead_update_kernel(float* __restrict__ G, int64_t d, int64_t ld) {
+// fp64 from the stored fp32 L21 (exact products), rounded once.  One 128x128
+// lower tile (by >= bx) per workgroup, the two 128x64 strips of L21 staged
+// in LDS as fp32 (rows padded to 65: the row groups a wave reads fall in
+// distinct banks); thread t takes rows (t / 16) + 16a and columns
+// (t % 16) + 16b, a, b = 0..7, and keeps its 64 sums in fp64 registers.
+constexpr int LT = 128;
+__global__ __launch_bounds__(256) void lead_update_kernel(float* __restrict__ G, int64_t d, int64_t ld,
+                                                          const float* __restrict__ L21b) {
   int by = (int)((sqrtf(8.f * (float)blockIdx.x + 1.f) - 1.f) * 0.5f);
   while ((by + 1) * (by + 2) / 2 <= (int)blockIdx.x) ++by;
   while (by * (by + 1) / 2 > (int)blockIdx.x) --by;
   const int bx = (int)blockIdx.x - by * (by + 1) / 2;
-  __shared__ double Ra[NB][NB + 1];
-  __shared__ double Rb[NB][NB + 1];
+  __shared__ float Ra[LT][NB + 1];
+  __shared__ float Rb[LT][NB + 1];
   const int t = threadIdx.x;
-  const int64_t ra0 = NB + (int64_t)by * NB, rb0 = NB + (int64_t)bx * NB;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int a = e >> 6, k = e & 63;
-    Ra[a][k] = ra0 + a < d ? (double)G[(ra0 + a) * ld + k] : 0.0;
-    Rb[a][k] = rb0 + a < d ? (double)G[(rb0 + a) * ld + k] : 0.0;
+  const int64_t ra0 = NB + (int64_t)by * LT, rb0 = NB + (int64_t)bx * LT;
+  {
+    // every load before the LDS stores: 32 floats of each strip a thread
+    float va[32], vb[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = t + 256 * u, rr = e >> 6, k = e & 63;
+      va[u] = ra0 + rr < d ? L21b[(ra0 - NB + rr) * NB + k] : 0.f;
+      vb[u] = rb0 + rr < d ? L21b[(rb0 - NB + rr) * NB + k] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = t + 256 * u, rr = e >> 6, k = e & 63;
+      Ra[rr][k] = va[u];
+      Rb[rr][k] = vb[u];
+    }
   }
   __syncthreads();
-  const int i0 = 4 * (t >> 4), j0 = 4 * (t & 15);
-  double acc[4][4];
+  const int ti = t >> 4, tj = t & 15;
+  double acc[8][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
   for (int k = 0; k < NB; ++k) {
-    double x[4], y[4];
+    double x[8], y[8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) { x[a] = Ra[i0 + a][k]; y[a] = Rb[j0 + a][k]; }
+    for (int a = 0; a < 8; ++a) {
+      x[a] = (double)Ra[ti + 16 * a][k];
+      y[a] = (double)Rb[tj + 16 * a][k];
+    }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = fma(x[a], y[b], acc[a][b]);
+      for (int b = 0; b < 8; ++b) acc[a][b] = fma(x[a], y[b], acc[a][b]);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t r = ra0 + i0 + a;
+  for (int a = 0; a < 8; ++a) {
+    const int64_t r = ra0 + ti + 16 * a;
     if (r >= d) continue;
+    float* row = G + r * ld;
+    float old[8];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t c = rb0 + j0 + b;
-      if (c <= r) G[r * ld + c] = (float)((double)G[r * ld + c] - acc[a][b]);
+    for (int b = 0; b < 8; ++b) {
+      const int64_t c = rb0 + tj + 16 * b;
+      old[b] = (c <= r) ? row[c] : 0.f;
     }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int64_t c = rb0 + tj + 16 * b;
+      if (c <= r) row[c] = (float)((double)old[b] - acc[a][b]);
+    }
+  }
+}
+
+// Before the fp32 factorization: the leading 64 columns of G become those of
+// the identity (lower part only; G's strict upper triangle is kept for the
+// act-order H_d write-back), so its first panel factors to I and applies a
+// zero update.  After it: the leading panel's own L21 and X = L11⁻¹ go back
+// into G and Linv for the triangular inverse.
+__global__ __launch_bounds__(256) void lead_identity_kernel(float* __restrict__ G, int64_t d) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < d * NB; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / NB, c = e % NB;
+    if (c <= r) G[r * d + c] = (r == c) ? 1.f : 0.f;
+  }
+}
+__global__ __launch_bounds__(256) void lead_restore_kernel(float* __restrict__ G, float* __restrict__ Linv,
+                                                           int64_t d, int kb,
+                                                           const float* __restrict__ L21b,
+                                                           const float* __restrict__ X0b) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < d * NB; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / NB, c = e % NB;
+    if (r >= NB) G[r * d + c] = L21b[(r - NB) * NB + c];
+    else if (r < kb && c < kb) Linv[r * d + c] = X0b[r * NB + c];
   }
 }
 
@@ -1022,38 +1103,42 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 256), 8192), 256, 0, s>>>(w.Linv, d * d);
   GQ_CHECK();
 
-  std::unique_ptr<TimerScope> chol_ts(new TimerScope(kTimerChol, s));
-  // the leading 64 columns in fp64 (lead_factor_kernel), then the blocked
-  // right-looking Cholesky (lower) of the trailing n x n block in fp32,
-  // 64-wide panels, one launch per panel, trailing updates in two levels
+  // The leading 64 columns in fp64 (lead_panel_kernel, lead_update_kernel:
+  // L21 and X of the first panel kept aside in T), then the blocked
+  // right-looking Cholesky (lower) of G in fp32 with the first panel's
+  // columns set to the identity (a zero update), 64-wide panels, one launch
+  // per panel, trailing updates in two levels; then the first panel's L21
+  // and X go back.
+  const int kb0 = (int)std::min<int64_t>(NB, d);
+  float* L21b = w.T;
+  float* X0b = w.T + (size_t)std::max<int64_t>(d - NB, 0) * NB;
   {
-    double* Xd = reinterpret_cast<double*>(w.T);
-    lead_factor_kernel<<<1, 64, 0, s>>>(w.G, d, (int)std::min<int64_t>(NB, d), Xd, w.Linv, w.status);
+    TimerScope lead_ts(kTimerLead, s);
+    const int64_t nb = std::max<int64_t>(1, ceil_div(d - NB, NB));
+    lead_panel_kernel<<<(unsigned)nb, 256, 0, s>>>(w.G, d, d, kb0, L21b, X0b, w.status);
     GQ_CHECK();
     if (d > NB) {
-      const int64_t nb = ceil_div(d - NB, NB);
-      lead_solve_kernel<<<(unsigned)nb, 256, 0, s>>>(w.G, d, d, Xd);
-      GQ_CHECK();
-      lead_update_kernel<<<(unsigned)(nb * (nb + 1) / 2), 256, 0, s>>>(w.G, d, d);
+      const int64_t nt = ceil_div(d - NB, LT);
+      lead_update_kernel<<<(unsigned)(nt * (nt + 1) / 2), 256, 0, s>>>(w.G, d, d, L21b);
       GQ_CHECK();
     }
+    lead_identity_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * NB, 256), 1024), 256, 0, s>>>(w.G, d);
+    GQ_CHECK();
   }
-  const int64_t n = std::max<int64_t>(d - NB, 0);
-  float* G1 = w.G + NB * d + NB;
-  float* L1 = w.Linv + NB * d + NB;
-  const std::vector<std::vector<uint32_t>> far = chol_sched::far_schedule(n);
+  std::unique_ptr<TimerScope> chol_ts(new TimerScope(kTimerChol, s));
+  const std::vector<std::vector<uint32_t>> far = chol_sched::far_schedule(d);
   // GPTQ_PANEL_SPIN_LIMIT (diagnostics only) shortens the panels' bounded
   // flag waits so that the stall report can be exercised
   int spin_limit = kSpinLimit;
   if (const char* sl = std::getenv("GPTQ_PANEL_SPIN_LIMIT")) spin_limit = std::max(0, std::atoi(sl));
-  FarJob fj = far_base(G1, n, d);
-  for (int64_t k = 0; k * NB < n; ++k) {
+  FarJob fj = far_base(w.G, d, d);
+  for (int64_t k = 0; k * NB < d; ++k) {
     const int64_t k0 = k * NB;
-    const int kb = (int)std::min<int64_t>(NB, n - k0);
-    const int64_t nr = n - (k0 + kb);
+    const int kb = (int)std::min<int64_t>(NB, d - k0);
+    const int64_t nr = d - (k0 + kb);
     const int nP = (int)std::max<int64_t>(1, ceil_div(nr, NB));
-    PanelArgs pa{G1, n, (int)k0, kb, L1, w.status, nP, spin_limit, d, NB};
-    const TileJob nj = near_job(G1, n, d, k);
+    PanelArgs pa{w.G, d, (int)k0, kb, w.Linv, w.status, nP, spin_limit, d, 0};
+    const TileJob nj = near_job(w.G, d, d, k);
     const std::vector<uint32_t>& ft = far[(size_t)k];
     // far tasks beyond one launch's list run first, in launches of their own
     size_t done = 0;
@@ -1069,7 +1154,9 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     chol_step_kernel<<<(unsigned)(nP + nj.count + fj.count), 256, 0, s>>>(pa, nP, nj, fj);
     GQ_CHECK();
   }
-
+  lead_restore_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * NB, 256), 1024), 256, 0, s>>>(
+      w.G, w.Linv, d, kb0, L21b, X0b);
+  GQ_CHECK();
   chol_ts.reset();
   // triangular inverse by recursive doubling on 64-aligned blocks
   TimerScope inv_ts(kTimerInverse, s);

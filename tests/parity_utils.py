@@ -162,7 +162,7 @@ def check_what_rebuild(gpu, d):
 
 
 def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, check_u=True,
-                  perm_follow=True, free_run=True, tie_tol=TIE_TOL, scale_tol=None):
+                  perm_follow=True, free_run=True, tie_tol=TIE_TOL):
     """Full comparison; returns a dict of measured figures and asserts the bar.
 
     free_run=False skips the informational second oracle run without
@@ -198,7 +198,7 @@ def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, che
     assert r.frac_codes_identical >= MIN_IDENTICAL, rep
     s_rel = np.abs(gpu["scales"] - ora["s"]) / np.abs(ora["s"])
     rep["scale_rel_max"] = float(s_rel.max())
-    assert rep["scale_rel_max"] <= (SCALE_TOL if scale_tol is None else scale_tol), rep
+    assert rep["scale_rel_max"] <= SCALE_TOL, rep
     assert np.array_equal(gpu["zeros"], ora["z"].astype(np.uint8))
     e_gpu = oracle.layer_error(ora["W"], gpu["what"], H_exact)
     e_ora = oracle.layer_error(ora["W"], ora["what"], H_exact)
@@ -217,7 +217,7 @@ def compare_layer(gpu, W, w_dtype, H_exact, oparams, label="", check_h=True, che
     qz = np.abs(gpu["codes"][:, :d].astype(np.float64) - ora["z"][:, gi])
     dw = np.abs(gpu["what"] - ora["what"])
     rep["what_max_abs_diff"] = float(dw.max())
-    bound = (SCALE_TOL if scale_tol is None else scale_tol) * s_o * qz + 2.0 ** -23 * np.abs(ora["what"])
+    bound = SCALE_TOL * s_o * qz + 2.0 ** -23 * np.abs(ora["what"])
     bad = dw > bound
     assert not np.any(bad), (rep, np.argwhere(bad)[:5].tolist())
     rl_o = ora["row_loss"]

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "gptq.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gptq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gptq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_loads_and_exports_every_declared_call():
@@ -262,3 +262,17 @@ def test_obq_validation():
     assert f(*args(ws_bytes=16)) == n.ERR_WORKSPACE
     assert L.gptq_workspace_bytes(3, 8, 129, 0, ctypes.byref(p)) == 0
     assert L.gptq_workspace_bytes(3, 8, 128, 0, ctypes.byref(p)) >= 128 * 128 * 8
+
+
+def test_w4a16_validation():
+    L = n.lib()
+    f = L.gptq_w4a16_gemm
+    ok = lambda **kw: [kw.get("A", FAKE), kw.get("adt", n.F16), kw.get("M", 1), kw.get("K", 256),
+                       kw.get("lda", 256), FAKE, kw.get("bits", 4), FAKE, FAKE, None,
+                       kw.get("g", 128), kw.get("ng", 2), 64, FAKE, 64, None]
+    assert f(*ok(A=None)) == n.ERR_INVALID_ARG
+    assert f(*ok(adt=n.F32)) == n.ERR_INVALID_ARG
+    assert f(*ok(bits=5)) == n.ERR_INVALID_ARG
+    assert f(*ok(lda=100)) == n.ERR_INVALID_ARG
+    assert f(*ok(g=48)) == n.ERR_UNSUPPORTED
+    assert f(*ok(ng=1)) == n.ERR_INVALID_ARG

@@ -469,3 +469,44 @@ def test_obq_matches_oracle(m, d, bits, sym):
         e_rtn = oracle.layer_error(W64, oracle.rtn_grouped(W64, bits, -1)[3], H32)
         log(f"OBQ m={m} d={d} b={bits}: layer error OBQ {e_gpu:.4e}, GPTQ {e_gptq:.4e}, RTN {e_rtn:.4e} "
             f"(GPTQ/OBQ {e_gptq / e_gpu:.4f})")
+
+
+@pytest.mark.parametrize("M,act,bits,g,act_order", [
+    (1, "f16", 4, 128, False), (3, "bf16", 4, 128, False), (1, "f16", 3, 128, False),
+    (4, "f16", 2, 64, False), (2, "bf16", 8, -1, False), (1, "f16", 4, 128, True),
+    (64, "f16", 4, 128, False), (37, "bf16", 3, 128, False), (100, "f16", 4, 128, True)])
+def test_w4a16_gemm_matches_oracle(M, act, bits, g, act_order):
+    """The exported layer's product with 16-bit activations: Ŵ dequantized as
+    (q − z)·s rounded once to the activation format, products exact, fp32
+    accumulation within its recursive-summation bound of the exact sum."""
+    torch = torch_mod()
+    g_ = gq()
+    wl = synth.WORKLOADS["llama7b-attn"].scaled(d_out=300, d_in=520, n_tok=4096, act_order=act_order)
+    W, X = _inputs(wl)
+    gp, _ = params_of(wl, bits=bits, group_size=g)
+    Wd = to_dev(W, wl.w_dtype)
+    H = torch.zeros(520, 520, device="cuda")
+    g_.hessian_accumulate(H, to_dev(X, wl.x_dtype))
+    prep = g_.prepare_hinv(H, gp)
+    q = g_.quantize_layer(Wd, prep, gp)
+    ex = g_.export(q, gp, 520)
+    rng = np.random.default_rng(M * 7 + bits)
+    a32 = (rng.standard_normal((M, 520)) * 2).astype(np.float32)
+    A_bits = a32.astype(np.float16).view(np.uint16) if act == "f16" else synth.f32_to_bf16_bits(a32)
+    A = (torch.from_numpy(A_bits.view(np.int16)).view(torch.float16 if act == "f16" else torch.bfloat16)
+         .cuda())
+    gi = q.g_idx if act_order else None
+    C = g_.w4a16_gemm(A, ex, bits, g, g_idx=gi)
+    torch.cuda.synchronize()
+    qd = ex.qweight.cpu().numpy().view(np.uint32)
+    s16 = ex.scales_f16.cpu().numpy().view(np.uint16)
+    z16 = ex.zeros_f16.cpu().numpy().view(np.uint16)
+    gidx = q.g_idx.cpu().numpy() if act_order else None
+    ref = oracle.w4a16.w4a16_matmul(A_bits, act, qd, bits, s16, z16, g, g_idx=gidx)
+    Wq = oracle.w4a16.dequantize(qd, bits, 520, s16, z16, g, g_idx=gidx, act=act)
+    bound = oracle.w4a16.accumulation_bound(A_bits, act, Wq, 520)
+    got = C.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    log(f"W4A16 M={M} {act} b={bits} g={g} act_order={act_order}: max |err| {err.max():.3e}, "
+        f"max err/bound {np.max(err / np.maximum(bound, 1e-30)):.3e}")
+    assert np.all(err <= bound + 1e-30)
