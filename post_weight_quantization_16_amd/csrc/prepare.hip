@@ -833,6 +833,44 @@ FarJob far_base(float* G, int64_t d, int64_t ld) {
 // rest of the factorization reads); everything after it is well scaled and
 // runs in fp32.
 
+// Whether the leading panel needs fp64.  Its elimination cancels when G
+// carries one large common part (activations sharing a channel mean make H
+// close to rank one on top of the rest), and that shows in the correlations
+// |G_ij|/sqrt(G_ii·G_jj) between the panel's 64 columns and the later ones:
+// near 1 for a common part, about 1/sqrt(tokens) for independent zero-mean
+// channels.  Their mean above kLeadCorr turns the fp64 panel on (for
+// d <= 64 the panel is the whole matrix and always runs in fp64).
+// lead_corr_kernel: one wave per row i >= 64 (its 64 panel entries are one
+// coalesced load), kCorrBlocks partial sums in a fixed order, so the
+// decision is deterministic; lead_panel_kernel adds them up.
+constexpr float kLeadCorr = 0.1f;
+constexpr int kCorrBlocks = 32;
+__global__ __launch_bounds__(256) void lead_corr_kernel(const float* __restrict__ G, int64_t d,
+                                                        double* __restrict__ part) {
+  __shared__ double wsum[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const float gj = G[(int64_t)lane * d + lane];
+  const float rs = gj > 0.f ? __builtin_amdgcn_rsqf(gj) : 0.f;
+  double acc = 0.0;
+  for (int64_t i = NB + (int64_t)blockIdx.x * 4 + wv; i < d; i += (int64_t)kCorrBlocks * 4) {
+    const float* row = G + i * d;
+    float v = fabsf(row[lane]) * rs;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const float gi = row[i];
+    acc += gi > 0.f ? (double)(v * __builtin_amdgcn_rsqf(gi)) : 0.0;
+  }
+  if (lane == 0) wsum[wv] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+__device__ __forceinline__ int lead_decide(const double* part, int64_t d) {
+  if (d <= NB) return 1;
+  double sum = 0.0;
+  for (int b = 0; b < kCorrBlocks; ++b) sum += part[b];
+  return sum / ((double)(d - NB) * (double)NB) > (double)kLeadCorr ? 1 : 0;
+}
+
 // The leading panel in fp64, one launch: every workgroup factors and inverts
 // the 64x64 leading block itself (no workgroup waits for another), then
 // workgroup b solves rows 64 + 64b .. +63 below it, L21 = G21·Xᵀ, and stores
@@ -852,7 +890,18 @@ FarJob far_base(float* G, int64_t d, int64_t ld) {
 __global__ __launch_bounds__(256) void lead_panel_kernel(const float* __restrict__ G, int64_t d,
                                                          int64_t ld, int kb, float* __restrict__ L21b,
                                                          float* __restrict__ X0b,
-                                                         int* __restrict__ status) {
+                                                         int* __restrict__ status,
+                                                         const double* __restrict__ part,
+                                                         int* __restrict__ flag) {
+  // every workgroup takes the decision itself; workgroup 0 publishes it for
+  // the kernels after this one
+  __shared__ int on;
+  if (threadIdx.x == 0) {
+    on = lead_decide(part, d);
+    if (blockIdx.x == 0) flag[0] = on;
+  }
+  __syncthreads();
+  if (!on) return;
   __shared__ double Lc[NB][NB + 1];   // L by columns as they are published
   __shared__ double Xs[NB][NB + 1];
   __shared__ double Rs[NB][NB + 1];   // this workgroup's rows of G21
@@ -954,7 +1003,9 @@ __global__ __launch_bounds__(256) void lead_panel_kernel(const float* __restrict
 // (t % 16) + 16b, a, b = 0..7, and keeps its 64 sums in fp64 registers.
 constexpr int LT = 128;
 __global__ __launch_bounds__(256) void lead_update_kernel(float* __restrict__ G, int64_t d, int64_t ld,
-                                                          const float* __restrict__ L21b) {
+                                                          const float* __restrict__ L21b,
+                                                          const int* __restrict__ flag) {
+  if (!flag[0]) return;
   int by = (int)((sqrtf(8.f * (float)blockIdx.x + 1.f) - 1.f) * 0.5f);
   while ((by + 1) * (by + 2) / 2 <= (int)blockIdx.x) ++by;
   while (by * (by + 1) / 2 > (int)blockIdx.x) --by;
@@ -1022,7 +1073,9 @@ __global__ __launch_bounds__(256) void lead_update_kernel(float* __restrict__ G,
 // act-order H_d write-back), so its first panel factors to I and applies a
 // zero update.  After it: the leading panel's own L21 and X = L11⁻¹ go back
 // into G and Linv for the triangular inverse.
-__global__ __launch_bounds__(256) void lead_identity_kernel(float* __restrict__ G, int64_t d) {
+__global__ __launch_bounds__(256) void lead_identity_kernel(float* __restrict__ G, int64_t d,
+                                                            const int* __restrict__ flag) {
+  if (!flag[0]) return;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < d * NB; e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / NB, c = e % NB;
     if (c <= r) G[r * d + c] = (r == c) ? 1.f : 0.f;
@@ -1031,7 +1084,9 @@ __global__ __launch_bounds__(256) void lead_identity_kernel(float* __restrict__ 
 __global__ __launch_bounds__(256) void lead_restore_kernel(float* __restrict__ G, float* __restrict__ Linv,
                                                            int64_t d, int kb,
                                                            const float* __restrict__ L21b,
-                                                           const float* __restrict__ X0b) {
+                                                           const float* __restrict__ X0b,
+                                                           const int* __restrict__ flag) {
+  if (!flag[0]) return;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < d * NB; e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / NB, c = e % NB;
     if (r >= NB) G[r * d + c] = L21b[(r - NB) * NB + c];
@@ -1040,13 +1095,14 @@ __global__ __launch_bounds__(256) void lead_restore_kernel(float* __restrict__ G
 }
 
 struct PrepWs {
-  int* status; float* lam; float* diag; int* perm; int* cnt; float* G; float* Linv; float* T;
+  int* status; double* corr; float* lam; float* diag; int* perm; int* cnt; float* G; float* Linv; float* T;
 };
 
 PrepWs carve(void* ws, int64_t d) {
   char* p = static_cast<char*>(ws);
   PrepWs w;
   w.status = reinterpret_cast<int*>(p); p += 256;
+  w.corr = reinterpret_cast<double*>(p); p += 256;
   w.lam = reinterpret_cast<float*>(p); p += 256;
   w.diag = reinterpret_cast<float*>(p); p += align_up((size_t)d * 4);
   w.perm = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
@@ -1062,7 +1118,7 @@ PrepWs carve(void* ws, int64_t d) {
 size_t prepare_ws_bytes(int64_t d) {
   // T: the doubling's products (d²/2 + 64² floats); the leading panel's fp64
   // inverse (64² doubles) uses it first
-  return 512 + 3 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
+  return 768 + 3 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
          align_up((size_t)(d * d / 2 + 2 * NB * NB) * 4);
 }
 
@@ -1114,15 +1170,22 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
   float* X0b = w.T + (size_t)std::max<int64_t>(d - NB, 0) * NB;
   {
     TimerScope lead_ts(kTimerLead, s);
+    int* flag = w.status + 2;
+    if (d > NB) {
+      lead_corr_kernel<<<kCorrBlocks, 256, 0, s>>>(w.G, d, w.corr);
+      GQ_CHECK();
+    }
     const int64_t nb = std::max<int64_t>(1, ceil_div(d - NB, NB));
-    lead_panel_kernel<<<(unsigned)nb, 256, 0, s>>>(w.G, d, d, kb0, L21b, X0b, w.status);
+    lead_panel_kernel<<<(unsigned)nb, 256, 0, s>>>(w.G, d, d, kb0, L21b, X0b, w.status, w.corr,
+                                                   flag);
     GQ_CHECK();
     if (d > NB) {
       const int64_t nt = ceil_div(d - NB, LT);
-      lead_update_kernel<<<(unsigned)(nt * (nt + 1) / 2), 256, 0, s>>>(w.G, d, d, L21b);
+      lead_update_kernel<<<(unsigned)(nt * (nt + 1) / 2), 256, 0, s>>>(w.G, d, d, L21b, flag);
       GQ_CHECK();
     }
-    lead_identity_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * NB, 256), 1024), 256, 0, s>>>(w.G, d);
+    lead_identity_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * NB, 256), 1024), 256, 0, s>>>(
+        w.G, d, flag);
     GQ_CHECK();
   }
   std::unique_ptr<TimerScope> chol_ts(new TimerScope(kTimerChol, s));
@@ -1155,7 +1218,7 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     GQ_CHECK();
   }
   lead_restore_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * NB, 256), 1024), 256, 0, s>>>(
-      w.G, w.Linv, d, kb0, L21b, X0b);
+      w.G, w.Linv, d, kb0, L21b, X0b, w.status + 2);
   GQ_CHECK();
   chol_ts.reset();
   // triangular inverse by recursive doubling on 64-aligned blocks

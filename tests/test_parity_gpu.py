@@ -73,13 +73,16 @@ def test_hessian_of_hadamard_columns_is_exact():
 
 
 # ---------------------------------------------------------------- prepare (fed the oracle's H)
-@pytest.mark.parametrize("d,act", [(256, False), (320, True), (1000, False), (700, True), (64, False), (5, True),
-                                   # several super-panels of far tasks, ragged end
-                                   (2100, False), (3072, True)])
-def test_prepare_matches_oracle(d, act):
+@pytest.mark.parametrize("d,act,mean", [(256, False, 0), (320, True, 0), (1000, False, 0), (700, True, 0),
+                                        (64, False, 0), (5, True, 0),
+                                        # several super-panels of far tasks, ragged end
+                                        (2100, False, 0), (3072, True, 0),
+                                        # a shared channel mean: the leading panel runs in fp64
+                                        (1000, False, 2.0), (1500, True, 1.0), (130, False, 3.0)])
+def test_prepare_matches_oracle(d, act, mean):
     torch = torch_mod()
     rng = np.random.default_rng(d)
-    x = rng.standard_normal((max(4 * d, 64), d))
+    x = rng.standard_normal((max(4 * d, 64), d)) + mean
     x[:, rng.choice(d, max(1, d // 100), replace=False)] *= 15
     x[:, d // 3] = 0.0  # a dead channel
     H_ex = oracle.hessian(x.astype(np.float32), "f32")
@@ -100,7 +103,7 @@ def test_prepare_matches_oracle(d, act):
     hrel = rel_fro(Hd, ora["Hd"])
     inv_err = np.abs(U.T @ U @ ora["Hd"] - np.eye(d)).max()
     hinv_rel = rel_fro(U.T @ U, ora["Hinv"])
-    log(f"PREPARE d={d} act={act}: U rel_fro={urel:.3e} Hinv rel_fro={hinv_rel:.3e} "
+    log(f"PREPARE d={d} act={act} mean={mean}: U rel_fro={urel:.3e} Hinv rel_fro={hinv_rel:.3e} "
         f"Hd rel_fro={hrel:.3e} |UᵀU·H_d − I|max={inv_err:.3e}")
     assert urel <= U_TOL and hrel <= 1e-6 and hinv_rel <= HINV_TOL
     assert np.array_equal(Hd, Hd.T)
