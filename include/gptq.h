@@ -110,6 +110,20 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
                             int64_t n_tok, int64_t ld_x, void* ws, size_t ws_bytes,
                             gptq_stream stream);
 
+/* gptq_hessian_accumulate for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arithmetic, with the library's own static device
+ * scratch of 65 MiB per GPU (held from the first call on that GPU until the
+ * process ends) in place of a workspace.  That holds one partial Hessian of
+ * d_in <= 4096; larger d_in returns GPTQ_ERR_UNSUPPORTED.  With less room
+ * for split partials than the workspace version, the token range may be cut
+ * into fewer splits, so H can differ from gptq_hessian_accumulate's in its
+ * rounding (both stay within the same error bound).  Every call on one GPU
+ * shares the scratch: calls that overlap on one GPU (other streams, other
+ * threads) race and must not be issued.  Allocates nothing; asynchronous. */
+int gptq_hessian_accumulate_noalloc(float* H, int64_t d_in, const void* X, int x_dtype,
+                                    int64_t n_tok, int64_t ld_x, gptq_stream stream);
+
 /* Prepare the inverse-Hessian factor ("Foundations": walkthrough steps 1-2,
  * Hessian Damping, Activation Ordering, Cholesky Decomposition):
  *   dead_i = (H_ii == 0) -> H_ii := 1;  λ = percdamp·mean(diag H);

@@ -19,7 +19,8 @@ import dataclasses
 from . import _native
 
 __all__ = [
-    "GPTQParams", "GPTQError", "NotPositiveDefinite", "hessian_accumulate", "prepare_hinv",
+    "GPTQParams", "GPTQError", "NotPositiveDefinite", "hessian_accumulate",
+    "hessian_accumulate_noalloc", "prepare_hinv",
     "quantize_layer", "quantize", "workspace_bytes", "version", "Prepared", "Quantized",
     "Exported", "export", "quantize_layers", "obq_layer", "timing", "timing_read", "w4a16_gemm",
 ]
@@ -161,6 +162,20 @@ def hessian_accumulate(H, X, ws=None):
     _ws_check(ws, X.device)
     _check(L.gptq_hessian_accumulate(_dev(H, "H"), d, _dev(X, "X"), xdt, n_tok,
                                      X.stride(0), _dev(ws, "ws"), ws.numel(), _stream(X.device)))
+    return H
+
+
+def hessian_accumulate_noalloc(H, X):
+    """H += 2·XᵀX without a workspace: the library's static device scratch
+    (for callers that cannot allocate; d_in <= 4096; calls that overlap on
+    one GPU race)."""
+    torch = _torch()
+    _matrix_rows(X, "X")
+    n_tok, d = X.shape
+    xdt = _dtype_code(X)
+    _require(H, "H", torch.float32, (d, d), X.device)
+    _check(_native.lib().gptq_hessian_accumulate_noalloc(_dev(H, "H"), d, _dev(X, "X"), xdt, n_tok,
+                                                         X.stride(0), _stream(X.device)))
     return H
 
 

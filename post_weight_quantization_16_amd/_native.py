@@ -20,6 +20,7 @@ WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ = 0, 1, 2, 3
 EXPORTS = (
     "gptq_workspace_bytes",
     "gptq_hessian_accumulate",
+    "gptq_hessian_accumulate_noalloc",
     "gptq_prepare_hinv",
     "gptq_quantize_layer",
     "gptq_quantize_layers",
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.gptq_workspace_bytes.restype = _sz
     L.gptq_hessian_accumulate.argtypes = [_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp]
     L.gptq_hessian_accumulate.restype = _int
+    L.gptq_hessian_accumulate_noalloc.argtypes = [_vp, _i64, _vp, _int, _i64, _i64, _vp]
+    L.gptq_hessian_accumulate_noalloc.restype = _int
     L.gptq_prepare_hinv.argtypes = [_vp, _i64, _pp, _vp, _vp, _vp, _vp, _sz,
                                     ctypes.POINTER(ctypes.c_int64), _vp]
     L.gptq_prepare_hinv.restype = _int

@@ -126,6 +126,28 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, 
   return GPTQ_OK;
 }
 
+int gptq_hessian_accumulate_noalloc(float* H, int64_t d_in, const void* X, int x_dtype,
+                                    int64_t n_tok, int64_t ld_x, gptq_stream stream) {
+  if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
+  if (d_in <= 0 || d_in > kMaxDin)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld] (got %lld)", (long long)kMaxDin,
+                (long long)d_in);
+  if (n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "n_tok must be >= 0");
+  if (!valid_dtype(x_dtype)) return fail(GPTQ_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
+  if (gq::hessian_min_ws_bytes(d_in) > gq::kScratchBytes)
+    return fail(GPTQ_ERR_UNSUPPORTED,
+                "hessian_accumulate_noalloc: d_in %lld needs %zu bytes of scratch, the static "
+                "scratch holds %zu (d_in <= 4096); use gptq_hessian_accumulate with a workspace",
+                (long long)d_in, gq::hessian_min_ws_bytes(d_in), gq::kScratchBytes);
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
+  if (ld_x < d_in) return fail(GPTQ_ERR_INVALID_ARG, "ld_x (%lld) < d_in (%lld)", (long long)ld_x,
+                               (long long)d_in);
+  hipError_t e = gq::hessian_launch_static(H, d_in, X, x_dtype, n_tok, ld_x, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("hessian_accumulate_noalloc", e);
+  return GPTQ_OK;
+}
+
 int gptq_prepare_hinv(float* H, int64_t d_in, const gptq_params* p, float* U, int32_t* perm,
                       uint8_t* dead_mask, void* ws, size_t ws_bytes, int64_t* info,
                       gptq_stream stream) {

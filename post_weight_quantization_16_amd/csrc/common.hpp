@@ -71,6 +71,11 @@ size_t hessian_ws_bytes(int64_t d, int64_t n_tok);
 size_t hessian_min_ws_bytes(int64_t d);
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
                           int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s);
+// the same with the library's static device scratch as the workspace (no
+// allocation); ERR: hipErrorInvalidValue when d needs more than it holds
+constexpr size_t kScratchBytes = (size_t)65 << 20;
+hipError_t hessian_launch_static(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                                 int64_t ld_x, hipStream_t s);
 
 // ---------------------------------------------------------------- prepare
 size_t prepare_ws_bytes(int64_t d);

@@ -35,6 +35,7 @@
 // fp32 inputs: the generic fp32 MFMA GEMM on op(A) = Xᵀ, op(B) = X.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -818,6 +819,55 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
     reduce_mirror_kernel<false><<<gr, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128, vec_h, mu_r,
                                                    shift_tok);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// A workspace in the library's own device memory: a file-scope array that
+// every GPU the library runs on holds until the process ends.  In host code
+// its name stands for a host-side shadow, not a device address, so the
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is passed to kernels.  Every
+// call on one GPU uses the same array: calls that overlap on one GPU race.
+// What must start at zero (the zero chunk) is written by a fill kernel on
+// every call; the partials and μ are fully written before they are read.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_for_device(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (e2 != hipSuccess) return e2;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t hessian_launch_static(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                                 int64_t ld_x, hipStream_t s) {
+  if (hessian_min_ws_bytes(d) > kScratchBytes) return hipErrorInvalidValue;
+  if (n_tok <= 0) return hipSuccess;
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  void* ws = nullptr;
+  if ((e = scratch_for_device(dev, &ws)) != hipSuccess) return e;
+  return hessian_launch(H, d, X, x_dtype, n_tok, ld_x, ws, kScratchBytes, s);
 }
 
 }  // namespace gq
