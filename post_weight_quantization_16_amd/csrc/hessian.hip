@@ -82,25 +82,26 @@ __device__ __forceinline__ uint16_t f32_to_half_rne(float f) {
 // μ_c for c < dp: the mean of column c over the first n0 tokens, rounded to
 // the 16-bit input format, or 0 when it is not significant (|mean| at most
 // 4·std/√n0: a zero-mean channel keeps the plain accumulation) or when
-// c >= d.  Workgroup: 64 columns (8 groups of 8 adjacent columns, 16-byte
-// loads) x 32 token lanes; the lanes' sums are combined in a fixed order, so
-// μ is deterministic.  The magnitude is kept below 2^10 so that 32·μ and
+// c >= d.  Workgroup: 16 columns (2 groups of 8 adjacent columns, 16-byte
+// loads) x 128 token lanes, so d/16 workgroups share the reads; the lanes'
+// sums are combined in a fixed order, so μ is deterministic.  The magnitude is kept below 2^10 so that 32·μ and
 // the shift products stay finite in either 16-bit format.
 template <bool BF16>
 __global__ __launch_bounds__(256) void shift_mean_kernel(const uint16_t* __restrict__ X, int64_t ld,
                                                          int d, int dp, int n0, int vec,
                                                          uint16_t* __restrict__ mu) {
-  __shared__ float S1[32][65], S2[32][65];
-  const int t = threadIdx.x, cg = t & 7, tl = t >> 3;
-  const int c0 = blockIdx.x * 64 + cg * 8;
+  constexpr int TL = 128, CW = 16;   // token lanes, columns per workgroup
+  __shared__ float S1[TL][CW + 1], S2[TL][CW + 1];
+  const int t = threadIdx.x, cg = t & 1, tl = t >> 1;
+  const int c0 = blockIdx.x * CW + cg * 8;
   float s1[8], s2[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) { s1[q] = 0.f; s2[q] = 0.f; }
-  for (int r0 = tl; r0 < n0; r0 += 32 * 4) {
+  for (int r0 = tl; r0 < n0; r0 += TL * 4) {
     uint16_t e[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r = r0 + 32 * u;
+      const int r = r0 + TL * u;
       const uint16_t* p = X + (int64_t)r * ld + c0;
       if (r < n0 && vec && c0 + 7 < d) {
         const uint4 v = *reinterpret_cast<const uint4*>(p);
@@ -124,10 +125,10 @@ __global__ __launch_bounds__(256) void shift_mean_kernel(const uint16_t* __restr
 #pragma unroll
   for (int q = 0; q < 8; ++q) { S1[tl][cg * 8 + q] = s1[q]; S2[tl][cg * 8 + q] = s2[q]; }
   __syncthreads();
-  if (t < 64) {
-    const int c = blockIdx.x * 64 + t;
+  if (t < CW) {
+    const int c = blockIdx.x * CW + t;
     double a = 0.0, b = 0.0;
-    for (int l = 0; l < 32; ++l) { a += S1[l][t]; b += S2[l][t]; }
+    for (int l = 0; l < TL; ++l) { a += S1[l][t]; b += S2[l][t]; }
     uint16_t m = 0;
     if (c < d && n0 > 1) {
       const double mean = a / n0;
@@ -756,7 +757,7 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   if (x_dtype != GPTQ_F32) {
     const int n0 = (int)std::min<int64_t>(n_tok, kShiftSample);
     const int vec = ((uintptr_t)X % 16 == 0) && (ld_x % 8 == 0);
-    const unsigned gm = (unsigned)ceil_div(dp, 64);
+    const unsigned gm = (unsigned)ceil_div(dp, 16);
     if (bf) shift_mean_kernel<true><<<gm, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
                                                         (int)dp, n0, vec, mu);
     else shift_mean_kernel<false><<<gm, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,

@@ -844,7 +844,7 @@ FarJob far_base(float* G, int64_t d, int64_t ld) {
 // coalesced load), kCorrBlocks partial sums in a fixed order, so the
 // decision is deterministic; lead_panel_kernel adds them up.
 constexpr float kLeadCorr = 0.1f;
-constexpr int kCorrBlocks = 32;
+constexpr int kCorrBlocks = 128;
 __global__ __launch_bounds__(256) void lead_corr_kernel(const float* __restrict__ G, int64_t d,
                                                         double* __restrict__ part) {
   __shared__ double wsum[4];
@@ -852,23 +852,34 @@ __global__ __launch_bounds__(256) void lead_corr_kernel(const float* __restrict_
   const float gj = G[(int64_t)lane * d + lane];
   const float rs = gj > 0.f ? __builtin_amdgcn_rsqf(gj) : 0.f;
   double acc = 0.0;
-  for (int64_t i = NB + (int64_t)blockIdx.x * 4 + wv; i < d; i += (int64_t)kCorrBlocks * 4) {
-    const float* row = G + i * d;
-    float v = fabsf(row[lane]) * rs;
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    const float gi = row[i];
-    acc += gi > 0.f ? (double)(v * __builtin_amdgcn_rsqf(gi)) : 0.0;
+  // two rows per iteration, both rows' loads issued before either is used
+  constexpr int64_t S = (int64_t)kCorrBlocks * 4;
+  for (int64_t i = NB + (int64_t)blockIdx.x * 4 + wv; i < d; i += 2 * S) {
+    const bool two = i + S < d;
+    const float* r0 = G + i * d;
+    const float* r1 = G + (two ? i + S : i) * d;
+    float v0 = fabsf(r0[lane]) * rs, v1 = fabsf(r1[lane]) * rs;
+    const float g0 = r0[i], g1 = r1[two ? i + S : i];
+    for (int o = 32; o > 0; o >>= 1) {
+      v0 += __shfl_xor(v0, o);
+      v1 += __shfl_xor(v1, o);
+    }
+    acc += g0 > 0.f ? (double)(v0 * __builtin_amdgcn_rsqf(g0)) : 0.0;
+    if (two) acc += g1 > 0.f ? (double)(v1 * __builtin_amdgcn_rsqf(g1)) : 0.0;
   }
   if (lane == 0) wsum[wv] = acc;
   __syncthreads();
   if (threadIdx.x == 0) part[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
 }
 
-__device__ __forceinline__ int lead_decide(const double* part, int64_t d) {
+// by one wave: lane l adds part[l] and part[l + 64], then a fixed tree; the
+// sum is lane 0's, so every workgroup takes the same decision
+__device__ __forceinline__ int lead_decide(const double* part, int64_t d, int lane) {
   if (d <= NB) return 1;
-  double sum = 0.0;
-  for (int b = 0; b < kCorrBlocks; ++b) sum += part[b];
-  return sum / ((double)(d - NB) * (double)NB) > (double)kLeadCorr ? 1 : 0;
+  static_assert(kCorrBlocks == 128, "two partial sums per lane");
+  double v = part[lane] + part[lane + 64];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_down(v, o);
+  return v / ((double)(d - NB) * (double)NB) > (double)kLeadCorr ? 1 : 0;
 }
 
 // The leading panel in fp64, one launch: every workgroup factors and inverts
@@ -896,9 +907,12 @@ __global__ __launch_bounds__(256) void lead_panel_kernel(const float* __restrict
   // every workgroup takes the decision itself; workgroup 0 publishes it for
   // the kernels after this one
   __shared__ int on;
-  if (threadIdx.x == 0) {
-    on = lead_decide(part, d);
-    if (blockIdx.x == 0) flag[0] = on;
+  if (threadIdx.x < 64) {
+    const int dec = lead_decide(part, d, threadIdx.x);
+    if (threadIdx.x == 0) {
+      on = dec;
+      if (blockIdx.x == 0) flag[0] = dec;
+    }
   }
   __syncthreads();
   if (!on) return;
@@ -1102,7 +1116,7 @@ PrepWs carve(void* ws, int64_t d) {
   char* p = static_cast<char*>(ws);
   PrepWs w;
   w.status = reinterpret_cast<int*>(p); p += 256;
-  w.corr = reinterpret_cast<double*>(p); p += 256;
+  w.corr = reinterpret_cast<double*>(p); p += 1024;
   w.lam = reinterpret_cast<float*>(p); p += 256;
   w.diag = reinterpret_cast<float*>(p); p += align_up((size_t)d * 4);
   w.perm = reinterpret_cast<int*>(p); p += align_up((size_t)d * 4);
@@ -1118,7 +1132,7 @@ PrepWs carve(void* ws, int64_t d) {
 size_t prepare_ws_bytes(int64_t d) {
   // T: the doubling's products (d²/2 + 64² floats); the leading panel's fp64
   // inverse (64² doubles) uses it first
-  return 768 + 3 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
+  return 1536 + 3 * align_up((size_t)d * 4) + 2 * align_up((size_t)d * d * 4) +
          align_up((size_t)(d * d / 2 + 2 * NB * NB) * 4);
 }
 
