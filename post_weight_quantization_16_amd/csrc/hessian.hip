@@ -581,15 +581,17 @@ __global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z
 }
 
 // H[i][j] += 2·(Σ_s P_s[i][j] + c·μ_iμ_j) over the upper triangle, and the
-// mirrored H[j][i] = H[i][j], one 128x128 upper tile (ti <= tj) per
-// workgroup.  c·μ_iμ_j restores what the shift MFMAs took out (c tokens'
-// worth, mu = null when no shift was applied).  The sum is formed in fp64 in
-// a fixed order (deterministic) and rounded once.  Each thread
-// owns 16 float4 runs of the tile and issues all of a split's loads before
-// adding them, and all of its H reads before any H write (reads after a
-// write through the same pointer would each wait a memory round trip); the
-// finished tile goes through LDS to be written transposed, so both writes
-// are coalesced.
+// mirrored H[j][i] = H[i][j], one 32-row strip of a 128x128 upper tile
+// (ti <= tj) per workgroup (four per tile, so the strips fill the CUs with
+// a short last round).  c·μ_iμ_j restores what the shift MFMAs took out (c
+// tokens' worth, mu = null when no shift was applied).  The sum is formed
+// in fp64 in a fixed order (deterministic) and rounded once.  Each thread
+// owns 4 float4 runs of the strip and issues the loads of four splits
+// before adding them, and all of its H reads before any H write (reads
+// after a write through the same pointer would each wait a memory round
+// trip); the finished strip goes through LDS to be written transposed, so
+// both writes are coalesced.
+constexpr int RS = 32;   // strip rows
 template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
                                                             const float* __restrict__ P,
@@ -598,32 +600,41 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
                                                             const uint16_t* __restrict__ mu,
                                                             double shift_tok) {
   int ti, tj;
-  tile_of(blockIdx.x, nt, ti, tj);
-  __shared__ float T[HT][HT + 1];
-  __shared__ double mr[HT], mc[HT];
+  tile_of(blockIdx.x >> 2, nt, ti, tj);
+  const int r0 = (blockIdx.x & 3) * RS;   // the strip's first row inside the tile
+  __shared__ float T[RS][HT + 1];
+  __shared__ double mr[RS], mc[HT];
   const int t = threadIdx.x;
-  constexpr int NR = HT * HT / (256 * 4);   // float4 runs per thread (16)
+  constexpr int NR = RS * HT / (256 * 4);   // float4 runs per thread (4)
   const int64_t pstride = dp * dp;
-  const float* src = P + (int64_t)(ti * HT) * dp + tj * HT;   // always inside the partials
-  if (mu && t < HT) {
-    mr[t] = shift_tok * (double)half_to_f32<BF16>(mu[ti * HT + t]);
-    mc[t] = (double)half_to_f32<BF16>(mu[tj * HT + t]);
+  const float* src = P + (int64_t)(ti * HT + r0) * dp + tj * HT;   // always inside the partials
+  if (mu) {
+    if (t < RS) mr[t] = shift_tok * (double)half_to_f32<BF16>(mu[ti * HT + r0 + t]);
+    if (t < HT) mc[t] = (double)half_to_f32<BF16>(mu[tj * HT + t]);
   }
   typedef __attribute__((ext_vector_type(4))) double f64x4;
   f64x4 acc[NR];
 #pragma unroll
   for (int it = 0; it < NR; ++it) acc[it] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int sp = 0; sp < splits; ++sp) {
-    f32x4 v[NR];
+  constexpr int SG = 4;   // splits whose loads are in flight together
+  for (int sp0 = 0; sp0 < splits; sp0 += SG) {
+    f32x4 v[SG][NR];
 #pragma unroll
-    for (int it = 0; it < NR; ++it) {
-      const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
-      v[it] = *reinterpret_cast<const f32x4*>(src + sp * pstride + (int64_t)a * dp + b4);
-    }
+    for (int u = 0; u < SG; ++u)
 #pragma unroll
-    for (int it = 0; it < NR; ++it)
+      for (int it = 0; it < NR; ++it) {
+        const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
+        const int sp = sp0 + u < splits ? sp0 + u : sp0;
+        v[u][it] = *reinterpret_cast<const f32x4*>(src + sp * pstride + (int64_t)a * dp + b4);
+      }
+    // splits in index order (the loads of a missing split are not added)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[it][q] += (double)v[it][q];
+    for (int u = 0; u < SG; ++u)
+      if (sp0 + u < splits)
+#pragma unroll
+        for (int it = 0; it < NR; ++it)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[it][q] += (double)v[u][it][q];
   }
   if (mu) {
     __syncthreads();
@@ -634,27 +645,28 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
       for (int q = 0; q < 4; ++q) acc[it][q] = fma(mr[a], mc[b4 + q], acc[it][q]);
     }
   }
+  const int i0 = ti * HT + r0;   // the strip's first row of H
   const bool full = vec_h && ti < tj && (tj + 1) * HT <= d;
   if (full) {
     f32x4 h[NR];
 #pragma unroll
     for (int it = 0; it < NR; ++it) {
       const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
-      h[it] = *reinterpret_cast<const f32x4*>(H + (int64_t)(ti * HT + a) * d + tj * HT + b4);
+      h[it] = *reinterpret_cast<const f32x4*>(H + (int64_t)(i0 + a) * d + tj * HT + b4);
     }
 #pragma unroll
     for (int it = 0; it < NR; ++it) {
       const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
 #pragma unroll
       for (int q = 0; q < 4; ++q) h[it][q] = (float)fma(2.0, acc[it][q], (double)h[it][q]);
-      *reinterpret_cast<f32x4*>(H + (int64_t)(ti * HT + a) * d + tj * HT + b4) = h[it];
+      *reinterpret_cast<f32x4*>(H + (int64_t)(i0 + a) * d + tj * HT + b4) = h[it];
 #pragma unroll
       for (int q = 0; q < 4; ++q) T[a][b4 + q] = h[it][q];
     }
   } else {
     for (int it = 0; it < NR; ++it) {
       const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
-      const int i = ti * HT + a;
+      const int i = i0 + a;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int jq = tj * HT + b4 + q;
@@ -668,10 +680,10 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
     }
   }
   __syncthreads();
-  // lower triangle: row tj*HT + bb, columns ti*HT + aa (contiguous in aa)
-  for (int e = t; e < HT * HT; e += 256) {
-    const int bb = e / HT, aa = e % HT;
-    const int r = tj * HT + bb, c = ti * HT + aa;
+  // lower triangle: row tj*HT + bb, columns i0 + aa (contiguous in aa)
+  for (int e = t; e < RS * HT; e += 256) {
+    const int bb = e / RS, aa = e % RS;
+    const int r = tj * HT + bb, c = i0 + aa;
     if (r < d && c < d && c < r) H[(int64_t)r * d + c] = T[aa][bb];
   }
 }
@@ -811,7 +823,7 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   }
   const int nt128 = (int)(dp / HT);
   const int vec_h = ((uintptr_t)H % 16 == 0) && (d % 4 == 0);
-  const unsigned gr = (unsigned)(nt128 * (nt128 + 1) / 2);
+  const unsigned gr = (unsigned)(4 * nt128 * (nt128 + 1) / 2);   // four strips per tile
   const uint16_t* mu_r = x_dtype == GPTQ_F32 ? nullptr : mu;
   if (bf || x_dtype == GPTQ_F32)
     reduce_mirror_kernel<true><<<gr, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128, vec_h, mu_r,
