@@ -63,15 +63,15 @@ def cpu_model() -> str:
 
 # HBM bytes per gptq_hessian_accumulate call on the 4096x4096, 131072-token
 # workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
-# `bench.py --steps 2 --warmup 1 --no-cpu-baseline` (KiB per dispatch, summed
-# over the call's two kernels), each scaled by the counter's reading for a
+# `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras` (KiB per
+# dispatch, summed over the call's four kernels), each scaled by the counter's reading for a
 # plain copy of known size (`bench.py --copy-calibration 512`).  Valid only
 # for the Hessian source they were taken on: any change to it reports null.
 HESSIAN_TRAFFIC = {
-    "source_sha256": "f02b59cf2282f2d04e0f8cfb33a2b948c71b5a9e45235e99ec2d766f33e9a542",
-    # zero_chunk_kernel + syrk256_kernel + reduce_mirror_kernel, KiB per call
-    "fetch_kib": 1.5 + 2255284.3 + 134888.2, "fetch_scale": 524288 / 262159.7,
-    "write_kib": 0.3 + 236544.0 + 65652.9, "write_scale": 524288 / 524288.0,
+    "source_sha256": "bb2d706c5dc5e41c9dfeabc7797e6e3f7d33429349b503d30d11c27ba52a6561",
+    # zero_chunk + shift_mean + syrk256 + reduce_mirror kernels, KiB per call
+    "fetch_kib": 1.1 + 16411.3 + 2143930.1 + 134918.5, "fetch_scale": 524288 / 262159.2,
+    "write_kib": 0.2 + 8.0 + 236544.0 + 65756.4, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -151,11 +151,14 @@ def cpu_baseline(wl, W, X, tok_sample, row_sample):
 
 
 def time_events(fn, reps, stream):
-    """Average milliseconds of fn() over reps calls, HIP events on `stream`."""
+    """Average milliseconds of fn() over reps calls, HIP events on `stream`.
+    A spin kernel first holds the GPU while the host queues all the calls, so
+    short calls are timed back to back on the GPU, not at the host's pace."""
     import torch
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
     torch.cuda.synchronize()
+    torch.cuda._sleep(10_000_000)
     a.record(stream)
     for _ in range(reps):
         fn()
@@ -202,10 +205,12 @@ def extras(gq, torch, wl, W, X, params, H, ws_h, ws_p, stream):
     q = gq.quantize_layer(W, prep, params)
     ex = gq.export(q, params, d)
     ng = ex.scales_f16.shape[1]
-    for M in (1, 64):
+    for M in (1, 4, 64, 512):
         A = torch.randn(M, d, device=W.device).to(torch.float16)
         C = torch.empty(M, m, device=W.device)
-        t = time_events(lambda: gq.w4a16_gemm(A, ex, params.bits, params.group_size, out=C), 50, stream)
+        ws_w = torch.empty(gq.workspace_bytes(4, m, d, M), dtype=torch.uint8, device=W.device)
+        t = time_events(lambda: gq.w4a16_gemm(A, ex, params.bits, params.group_size, out=C, ws=ws_w),
+                        50, stream)
         wbytes = m * ((d * params.bits + 31) // 32) * 4 + 2 * 2 * m * ng
         byts = wbytes + M * d * 2 + M * m * 4
         flop = 2 * M * m * d

@@ -86,10 +86,12 @@ typedef struct {
 
 typedef void* gptq_stream;
 
-enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2, GPTQ_WS_OBQ = 3 };
+enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2, GPTQ_WS_OBQ = 3,
+       GPTQ_WS_W4A16 = 4 };
 
 /* Workspace size in bytes that call `which` (GPTQ_WS_*) needs for the given
  * shape.  n_tok is used by the Hessian call only; p may be NULL for it.
+ * For GPTQ_WS_W4A16 the shape is d_out = N, d_in = K, n_tok = M (p unused).
  * Returns 0 for invalid arguments.  Workspaces need 256-byte alignment
  * (every hipMalloc'd pointer has it). */
 size_t gptq_workspace_bytes(int which, int64_t d_out, int64_t d_in, int64_t n_tok,
@@ -273,12 +275,18 @@ int gptq_export(int bits, int64_t d_out, int64_t d_in, int64_t n_groups, const u
  *  g_idx      [K] group of each column (act-order layers) or NULL: column k
  *             is then in group k / group_size (group_size -1: one group).
  *  C          out [M x N] fp32, row stride ldc >= N.
+ *  ws         NULL, or a workspace of gptq_workspace_bytes(GPTQ_WS_W4A16, N,
+ *             K, M, NULL): products with few output tiles then split K and
+ *             sum the fp32 partials in a fixed order (same result on every
+ *             run); with NULL they run unsplit.  A non-NULL ws smaller than
+ *             that size returns GPTQ_ERR_WORKSPACE.
  * M <= 4 runs a GEMV bound by the weights' HBM traffic; larger M an MFMA
  * product.  Asynchronous; argument errors only. */
 int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
                     const uint32_t* qweight, int bits, const uint16_t* scales_f16,
                     const uint16_t* zeros_f16, const int32_t* g_idx, int group_size,
-                    int64_t n_groups, int64_t N, float* C, int64_t ldc, gptq_stream stream);
+                    int64_t n_groups, int64_t N, float* C, int64_t ldc, void* ws,
+                    size_t ws_bytes, gptq_stream stream);
 
 /* Per-stage timing, for measurement only.  gptq_timing(1) clears what was
  * recorded and starts bracketing, on the caller's stream, the launches of

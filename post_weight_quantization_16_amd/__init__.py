@@ -368,8 +368,9 @@ def export(q: Quantized, params: GPTQParams, d_in: int) -> Exported:
     return Exported(qd, s16, z16)
 
 
-def w4a16_gemm(A, ex: Exported, bits: int, group_size: int, g_idx=None, out=None):
-    """C = A·Ŵᵀ from an export: A [M, K] float16/bfloat16, C [M, N] float32."""
+def w4a16_gemm(A, ex: Exported, bits: int, group_size: int, g_idx=None, out=None, ws=None):
+    """C = A·Ŵᵀ from an export: A [M, K] float16/bfloat16, C [M, N] float32.
+    ws: the split-K workspace (allocated here when None; pass one to reuse)."""
     torch = _torch()
     _matrix_rows(A, "A")
     M, K = A.shape
@@ -384,10 +385,15 @@ def w4a16_gemm(A, ex: Exported, bits: int, group_size: int, g_idx=None, out=None
         _require(g_idx, "g_idx", torch.int32, (K,), dev)
     C = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=dev)
     _require(C, "C", torch.float32, (M, N), dev)
-    _check(_native.lib().gptq_w4a16_gemm(
+    L = _native.lib()
+    if ws is None:
+        ws = _workspace(L.gptq_workspace_bytes(_native.WS_W4A16, N, K, M, None), dev)
+    _ws_check(ws, dev)
+    _check(L.gptq_w4a16_gemm(
         _dev(A, "A"), _dtype_code(A), M, K, A.stride(0), _dev(ex.qweight, "qweight"), bits,
         _dev(ex.scales_f16, "scales_f16"), _dev(ex.zeros_f16, "zeros_f16"),
-        _dev(g_idx, "g_idx"), group_size, ng, N, _dev(C, "C"), N, _stream(dev)))
+        _dev(g_idx, "g_idx"), group_size, ng, N, _dev(C, "C"), N, _dev(ws, "ws"), ws.numel(),
+        _stream(dev)))
     return C
 
 

@@ -15,7 +15,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NOT_SPD, ERR_WORKSPACE, ERR_HIP, ERR_I
 # gptq_dtype
 F32, BF16, F16 = 0, 1, 2
 # workspace kinds
-WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ = 0, 1, 2, 3
+WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ, WS_W4A16 = 0, 1, 2, 3, 4
 
 EXPORTS = (
     "gptq_workspace_bytes",
@@ -101,7 +101,7 @@ def lib() -> ctypes.CDLL:
     L.gptq_export.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.gptq_export.restype = _int
     L.gptq_w4a16_gemm.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _int, _vp, _vp, _vp, _int,
-                                  _i64, _i64, _vp, _i64, _vp]
+                                  _i64, _i64, _vp, _i64, _vp, _sz, _vp]
     L.gptq_w4a16_gemm.restype = _int
     L.gptq_timing.argtypes = [_int]
     L.gptq_timing.restype = _int

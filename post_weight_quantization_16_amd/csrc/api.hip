@@ -98,6 +98,9 @@ size_t gptq_workspace_bytes(int which, int64_t d_out, int64_t d_in, int64_t n_to
     case GPTQ_WS_OBQ:
       if (d_in > gq::obq_max_din()) return 0;
       return gq::obq_ws_bytes(d_in);
+    case GPTQ_WS_W4A16:   // d_out = N, d_in = K, n_tok = M
+      if (d_out <= 0 || d_out > kMaxDout || n_tok <= 0 || n_tok > kMaxDout) return 0;
+      return gq::w4a16_ws_bytes(n_tok, d_out, d_in);
     default:
       return 0;
   }
@@ -290,7 +293,8 @@ int gptq_obq_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int6
 int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
                     const uint32_t* qweight, int bits, const uint16_t* scales_f16,
                     const uint16_t* zeros_f16, const int32_t* g_idx, int group_size,
-                    int64_t n_groups, int64_t N, float* C, int64_t ldc, gptq_stream stream) {
+                    int64_t n_groups, int64_t N, float* C, int64_t ldc, void* ws,
+                    size_t ws_bytes, gptq_stream stream) {
   if (!A || !qweight || !scales_f16 || !zeros_f16 || !C)
     return fail(GPTQ_ERR_INVALID_ARG, "A, qweight, scales, zeros and C must not be NULL");
   if (a_dtype != GPTQ_F16 && a_dtype != GPTQ_BF16)
@@ -305,8 +309,12 @@ int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t ld
     return fail(GPTQ_ERR_UNSUPPORTED, "group_size must be a multiple of 32 (or -1)");
   if (n_groups < ceil_div64(K, g) || n_groups > K)
     return fail(GPTQ_ERR_INVALID_ARG, "n_groups must cover the groups of K columns");
+  if (ws) {
+    const int rc = check_ws(ws, ws_bytes, gq::w4a16_ws_bytes(M, N, K), "w4a16_gemm");
+    if (rc != GPTQ_OK) return rc;
+  }
   hipError_t e = gq::w4a16_launch(A, a_dtype, M, K, lda, qweight, bits, scales_f16, zeros_f16,
-                                  g_idx, g, n_groups, N, C, ldc, (hipStream_t)stream);
+                                  g_idx, g, n_groups, N, C, ldc, ws, ws_bytes, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("w4a16_gemm", e);
   return GPTQ_OK;
 }

@@ -149,7 +149,8 @@ hipError_t obq_launch(const void* W, int w_dtype, int64_t m, int64_t d, int64_t 
 hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
                         const uint32_t* qweight, int bits, const uint16_t* s16, const uint16_t* z16,
                         const int32_t* g_idx, int64_t g, int64_t ng, int64_t N, float* C,
-                        int64_t ldc, hipStream_t s);
+                        int64_t ldc, void* ws, size_t ws_bytes, hipStream_t s);
+size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K);
 
 // ---------------------------------------------------------------- export
 hipError_t export_launch(int bits, int64_t m, int64_t d, int64_t ng, const uint32_t* qweight,

@@ -269,10 +269,16 @@ def test_w4a16_validation():
     f = L.gptq_w4a16_gemm
     ok = lambda **kw: [kw.get("A", FAKE), kw.get("adt", n.F16), kw.get("M", 1), kw.get("K", 256),
                        kw.get("lda", 256), FAKE, kw.get("bits", 4), FAKE, FAKE, None,
-                       kw.get("g", 128), kw.get("ng", 2), 64, FAKE, 64, None]
+                       kw.get("g", 128), kw.get("ng", 2), 64, FAKE, 64, kw.get("ws", None),
+                       kw.get("ws_bytes", 0), None]
     assert f(*ok(A=None)) == n.ERR_INVALID_ARG
     assert f(*ok(adt=n.F32)) == n.ERR_INVALID_ARG
     assert f(*ok(bits=5)) == n.ERR_INVALID_ARG
     assert f(*ok(lda=100)) == n.ERR_INVALID_ARG
     assert f(*ok(g=48)) == n.ERR_UNSUPPORTED
     assert f(*ok(ng=1)) == n.ERR_INVALID_ARG
+    # a given workspace must hold the split-K partials
+    need = L.gptq_workspace_bytes(n.WS_W4A16, 64, 256, 64, None)
+    assert need >= 64 * 64 * 4 * 2
+    assert f(*ok(M=64, ws=FAKE, ws_bytes=need - 4)) == n.ERR_WORKSPACE
+    assert L.gptq_workspace_bytes(n.WS_W4A16, 64, 256, 0, None) == 0

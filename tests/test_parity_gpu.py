@@ -513,3 +513,53 @@ def test_w4a16_gemm_matches_oracle(M, act, bits, g, act_order):
     log(f"W4A16 M={M} {act} b={bits} g={g} act_order={act_order}: max |err| {err.max():.3e}, "
         f"max err/bound {np.max(err / np.maximum(bound, 1e-30)):.3e}")
     assert np.all(err <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("M,act,bits,K,split", [
+    (1, "f16", 4, 4096, True), (3, "bf16", 4, 4000, True), (1, "bf16", 3, 4096, True),
+    (64, "f16", 4, 4096, True), (64, "f16", 4, 4096, False), (200, "bf16", 3, 4000, True),
+    (17, "f16", 8, 4096, False), (5, "bf16", 2, 4064, True)])
+def test_w4a16_gemm_large_k(M, act, bits, K, split):
+    """Long rows (K up to 4096, ragged) and a ragged N: any word stream is a
+    valid dense code stream, so the codes are random words; scales are random
+    halves and zeros random codes.  With a workspace, products with few tiles
+    split K (fixed-order sum of fp32 partials); without one they run unsplit.
+    Both stay within the fp32 recursive-summation bound of the exact sum."""
+    import ctypes
+    torch = torch_mod()
+    g_ = gq()
+    n = g_._native
+    N, g = 1000, 128
+    ng = (K + g - 1) // g
+    rng = np.random.default_rng(M * 1000 + K + bits)
+    rw = (K * bits + 31) // 32
+    qd = rng.integers(0, 2**32, size=(N, rw), dtype=np.uint64).astype(np.uint32)
+    s16 = (rng.uniform(1e-3, 1e-2, size=(N, ng))).astype(np.float16).view(np.uint16)
+    z16 = rng.integers(0, 2**bits, size=(N, ng)).astype(np.float16).view(np.uint16)
+    a32 = (rng.standard_normal((M, K)) * 2).astype(np.float32)
+    A_bits = a32.astype(np.float16).view(np.uint16) if act == "f16" else synth.f32_to_bf16_bits(a32)
+    tdt = torch.float16 if act == "f16" else torch.bfloat16
+    A = torch.from_numpy(A_bits.view(np.int16)).view(tdt).cuda()
+    q_t = torch.from_numpy(qd.view(np.int32)).cuda()
+    s_t = torch.from_numpy(s16.view(np.int16)).view(torch.float16).cuda()
+    z_t = torch.from_numpy(z16.view(np.int16)).view(torch.float16).cuda()
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    L = n.lib()
+    need = L.gptq_workspace_bytes(n.WS_W4A16, N, K, M, None)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if split else None
+    rc = L.gptq_w4a16_gemm(
+        ctypes.c_void_p(A.data_ptr()), n.F16 if act == "f16" else n.BF16, M, K, K,
+        ctypes.c_void_p(q_t.data_ptr()), bits, ctypes.c_void_p(s_t.data_ptr()),
+        ctypes.c_void_p(z_t.data_ptr()), None, g, ng, N, ctypes.c_void_p(C.data_ptr()), N,
+        ctypes.c_void_p(ws.data_ptr()) if split else None, need if split else 0,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == n.OK, n.last_error()
+    torch.cuda.synchronize()
+    ref = oracle.w4a16.w4a16_matmul(A_bits, act, qd, bits, s16, z16, g)
+    Wq = oracle.w4a16.dequantize(qd, bits, K, s16, z16, g, act=act)
+    bound = oracle.w4a16.accumulation_bound(A_bits, act, Wq, K)
+    got = C.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    log(f"W4A16 M={M} K={K} {act} b={bits} split={split} (ws {need} B): max |err| {err.max():.3e}, "
+        f"max err/bound {np.max(err / np.maximum(bound, 1e-30)):.3e}")
+    assert np.all(err <= bound + 1e-30)
