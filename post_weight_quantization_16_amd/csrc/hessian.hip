@@ -367,9 +367,60 @@ __device__ __forceinline__ void block_tile(int r, int nt, int& ti, int& tj) {
   ti = tj = 0;   // not reached for r < nt(nt+1)/2
 }
 
-__device__ __forceinline__ void fast_tile(int L, int nt, int tiles, int& ti, int& tj, int& split) {
+// Token splits.  Every tile's token range is cut into S splits of `chunk`
+// tokens, except (mixed plan) the tiles of the blocks in `hi_mask`, cut into
+// S+1 splits of `chunk_hi`: with tiles·S workgroups a few short of a whole
+// number of rounds of the CUs, the extra splits fill the last round.  Each
+// XCD's run then starts with its share of the long workgroups (the S-split
+// tiles, split by split) and ends with its share of the short ones, so the
+// rounds stay nearly even (longest first).
+struct SplitPlan {
+  int64_t chunk, chunk_hi;
+  int S;
+  int hi_tiles;              // tiles in hi blocks (0: uniform plan)
+  int long_per_xcd, short_per_xcd;
+  uint64_t hi_mask;          // bit b: block b (upper blocks of 4x4 panels, row-major) has S+1 splits
+};
+
+__device__ __forceinline__ int block_size(int b, int ng) {
+  int I = 0;
+  while (b >= ng - I) { b -= ng - I; ++I; }
+  return b == 0 ? 10 : 16;   // the diagonal block of row I comes first
+}
+// the k-th tile (block order) among the blocks whose hi_mask bit equals `hi`
+__device__ __forceinline__ int select_tile(int k, int ng, uint64_t mask, bool hi) {
+  int r = 0;
+  const int nb = ng * (ng + 1) / 2;
+  for (int b = 0; b < nb; ++b) {
+    const int n = block_size(b, ng);
+    if ((((mask >> b) & 1u) != 0) == hi) {
+      if (k < n) return r + k;
+      k -= n;
+    }
+    r += n;
+  }
+  return r;   // not reached for k below the selected tiles' count
+}
+
+__device__ __forceinline__ void fast_tile(int L, int nt, int tiles, const SplitPlan& sp, int& ti,
+                                          int& tj, int& split, int64_t& chunk) {
   const int grid = (int)gridDim.x;
-  if (nt % 4 == 0 && grid % 8 == 0) {
+  chunk = sp.chunk;
+  if (sp.hi_tiles > 0) {
+    const int x = L & 7, p = L >> 3, ng = nt / 4;
+    int r;
+    if (p < sp.long_per_xcd) {
+      const int idx = x * sp.long_per_xcd + p, lo_tiles = tiles - sp.hi_tiles;
+      split = idx / lo_tiles;
+      r = select_tile(idx % lo_tiles, ng, sp.hi_mask, false);
+    } else {
+      const int idx = x * sp.short_per_xcd + (p - sp.long_per_xcd);
+      split = idx / sp.hi_tiles;
+      r = select_tile(idx % sp.hi_tiles, ng, sp.hi_mask, true);
+      chunk = sp.chunk_hi;
+    }
+    block_tile(r, nt, ti, tj);
+  } else if (nt % 4 == 0 && grid % 8 == 0) {
     const int u = (L & 7) * (grid / 8) + (L >> 3);
     split = u / tiles;
     block_tile(u % tiles, nt, ti, tj);
@@ -381,13 +432,14 @@ __device__ __forceinline__ void fast_tile(int L, int nt, int tiles, int& ti, int
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void syrk256_kernel(const uint16_t* __restrict__ X, int64_t ld,
-                                                       int d, int64_t n_tok, int64_t chunk, int nt,
+                                                       int d, int64_t n_tok, SplitPlan plan, int nt,
                                                        float* __restrict__ P, int64_t dp,
                                                        const uint16_t* __restrict__ zero16,
                                                        const uint16_t* __restrict__ mu) {
   const int tiles = nt * (nt + 1) / 2;
   int ti, tj, split;
-  fast_tile(blockIdx.x, nt, tiles, ti, tj, split);
+  int64_t chunk;
+  fast_tile(blockIdx.x, nt, tiles, plan, ti, tj, split, chunk);
   const int64_t t_begin = (int64_t)split * chunk;
   const int64_t t_end = min(n_tok, t_begin + chunk);
   // stages of FK tokens, rounded up to whole shift groups of kShiftTok
@@ -592,15 +644,32 @@ __global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z
 // trip); the finished strip goes through LDS to be written transposed, so
 // both writes are coalesced.
 constexpr int RS = 32;   // strip rows
+// Split counts per tile: S, or S+1 for the 128-tiles inside the hi blocks
+// of 4x4 256-tiles (ng_hi > 0 and the block's hi_mask bit set), with the
+// matching shift count.
+struct ReducePlan {
+  int S, ng_hi;
+  uint64_t hi_mask;
+  double shift_lo, shift_hi;
+};
 template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
                                                             const float* __restrict__ P,
-                                                            int64_t dp, int splits, int nt,
+                                                            int64_t dp, ReducePlan rp, int nt,
                                                             int vec_h,
-                                                            const uint16_t* __restrict__ mu,
-                                                            double shift_tok) {
+                                                            const uint16_t* __restrict__ mu) {
   int ti, tj;
   tile_of(blockIdx.x >> 2, nt, ti, tj);
+  int splits = rp.S;
+  double shift_tok = rp.shift_lo;
+  if (rp.ng_hi > 0) {
+    const int I = ti / 8, J = tj / 8;   // 128-tiles -> blocks of 4x4 256-tiles
+    const int b = I * rp.ng_hi - I * (I - 1) / 2 + (J - I);
+    if ((rp.hi_mask >> b) & 1u) {
+      splits = rp.S + 1;
+      shift_tok = rp.shift_hi;
+    }
+  }
   const int r0 = (blockIdx.x & 3) * RS;   // the strip's first row inside the tile
   __shared__ float T[RS][HT + 1];
   __shared__ double mr[RS], mc[HT];
@@ -727,13 +796,64 @@ int fast_splits(int64_t d, int64_t n_tok) {
   return (int)ceil_div(n_tok, chunk);
 }
 
+// Tokens' worth of μμᵀ the shift MFMAs take out of one tile over `splits`
+// splits of `chunk` tokens: one shift per started group of kShiftTok tokens
+// (stages of `step` tokens, groups rounded up).
+double shift_count(int64_t n_tok, int64_t chunk, int splits, int step) {
+  double c = 0.0;
+  for (int sp = 0; sp < splits; ++sp) {
+    const int64_t rows = std::min<int64_t>(n_tok, (sp + 1) * chunk) - sp * chunk;
+    c += (double)ceil_div(ceil_div(rows, step), kShiftTok / step) * kShiftTok;
+  }
+  return c;
+}
+
+// The mixed split plan for the 256-tile path: give the tiles of a few 4x4
+// blocks one split more so that the workgroup count becomes a whole number
+// of rounds of the CUs, with the same count of long and of short workgroups
+// on every XCD.  Returns the uniform plan when no set of blocks fits (the
+// blocks are chosen as the first `a` diagonal and `b` off-diagonal ones
+// with 10a + 16b the missing count).
+SplitPlan mixed_plan(int64_t d, int64_t n_tok, int S, int64_t chunk) {
+  SplitPlan u{chunk, chunk, S, 0, 0, 0, 0};
+  const int nt = (int)ceil_div(d, FT);
+  if (nt % 4 != 0 || S < 2) return u;
+  const int ng = nt / 4, nb = ng * (ng + 1) / 2;
+  if (nb > 64) return u;
+  const int tiles = nt * (nt + 1) / 2;
+  const int64_t chunk_hi = ceil_div(ceil_div(n_tok, S + 1), FK) * FK;
+  if (ceil_div(n_tok, chunk_hi) != S + 1) return u;
+  const int units = tiles * S;
+  const int need = (int)(ceil_div(units, kCUs) * kCUs) - units;
+  if (need == 0) return u;
+  for (int a = 0; a <= ng; ++a) {
+    const int rest = need - 10 * a;
+    if (rest < 0) break;
+    if (rest % 16 != 0 || rest / 16 > ng * (ng - 1) / 2) continue;
+    const int b = rest / 16;
+    const int hi_tiles = need;   // 10a + 16b tiles gain one split each
+    const int lo_units = (tiles - hi_tiles) * S, hi_units = hi_tiles * (S + 1);
+    if (lo_units % 8 != 0 || hi_units % 8 != 0) continue;
+    uint64_t mask = 0;
+    int da = 0, db = 0, blk = 0;
+    for (int I = 0; I < ng; ++I)
+      for (int J = I; J < ng; ++J, ++blk) {
+        if (I == J && da < a) { mask |= 1ull << blk; ++da; }
+        if (I != J && db < b) { mask |= 1ull << blk; ++db; }
+      }
+    SplitPlan p{chunk, chunk_hi, S, hi_tiles, lo_units / 8, hi_units / 8, mask};
+    return p;
+  }
+  return u;
+}
+
 }  // namespace
 
 int hessian_splits(int64_t d, int64_t n_tok) { return fast_splits(d, n_tok); }
 
 size_t hessian_ws_bytes(int64_t d, int64_t n_tok) {
   const int64_t dpg = ceil_div(d, FT) * FT;
-  const size_t fast = (size_t)fast_splits(d, n_tok) * dpg * dpg * sizeof(float);
+  const size_t fast = (size_t)(fast_splits(d, n_tok) + 1) * dpg * dpg * sizeof(float);   // + mixed plan's
   const size_t gen = (size_t)generic_splits(d, n_tok) * dpg * dpg * sizeof(float);
   // partials, then the shift μ (dp 16-bit values), then a 256-byte zero
   // chunk (source of out-of-range copies)
@@ -762,10 +882,14 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   const int step = fast ? FK : HK;
   const int64_t chunk = ceil_div(ceil_div(n_tok, std::min(want, fit)), step) * step;
   const int splits = (int)ceil_div(n_tok, chunk);
-  uint16_t* mu = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(part * splits));
+  SplitPlan plan{chunk, chunk, splits, 0, 0, 0, 0};
+  if (fast && fit > splits) plan = mixed_plan(d, n_tok, splits, chunk);
+  const int nslots = plan.hi_tiles > 0 ? splits + 1 : splits;   // partial Hessians written
+  uint16_t* mu = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(part * nslots));
   uint16_t* zero16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(mu) + align_up((size_t)dp * 2));
   const bool bf = x_dtype == GPTQ_BF16;
   double shift_tok = 0.0;   // tokens' worth of μμᵀ the shift MFMAs took out
+  ReducePlan rp{splits, 0, 0, 0.0, 0.0};
   if (x_dtype != GPTQ_F32) {
     const int n0 = (int)std::min<int64_t>(n_tok, kShiftSample);
     const int vec = ((uintptr_t)X % 16 == 0) && (ld_x % 8 == 0);
@@ -779,19 +903,23 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   if (fast) {
     const int nt = (int)ceil_div(d, FT);
     const int tiles = nt * (nt + 1) / 2;
-    const unsigned grid = (unsigned)(tiles * splits);
-    for (int sp = 0; sp < splits; ++sp) {   // shift MFMAs per split: one per started 16 stages
-      const int64_t rows = std::min<int64_t>(n_tok, (sp + 1) * chunk) - sp * chunk;
-      shift_tok += (double)ceil_div(ceil_div(rows, FK), kShiftTok / FK) * kShiftTok;
+    const unsigned grid = (unsigned)(plan.hi_tiles > 0
+                                         ? (tiles - plan.hi_tiles) * splits + plan.hi_tiles * (splits + 1)
+                                         : tiles * splits);
+    shift_tok = shift_count(n_tok, chunk, splits, FK);
+    if (plan.hi_tiles > 0) {
+      rp.ng_hi = nt / 4;
+      rp.hi_mask = plan.hi_mask;
+      rp.shift_hi = shift_count(n_tok, plan.chunk_hi, splits + 1, FK);
     }
     zero_chunk_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(zero16));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (x_dtype == GPTQ_BF16)
       syrk256_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d, n_tok,
-                                                chunk, nt, P, dp, zero16, mu);
+                                                plan, nt, P, dp, zero16, mu);
     else
       syrk256_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(X), ld_x, (int)d,
-                                                 n_tok, chunk, nt, P, dp, zero16, mu);
+                                                 n_tok, plan, nt, P, dp, zero16, mu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
     const int nt = (int)ceil_div(d, HT);
@@ -825,12 +953,11 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   const int vec_h = ((uintptr_t)H % 16 == 0) && (d % 4 == 0);
   const unsigned gr = (unsigned)(4 * nt128 * (nt128 + 1) / 2);   // four strips per tile
   const uint16_t* mu_r = x_dtype == GPTQ_F32 ? nullptr : mu;
+  rp.shift_lo = shift_tok;
   if (bf || x_dtype == GPTQ_F32)
-    reduce_mirror_kernel<true><<<gr, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128, vec_h, mu_r,
-                                                  shift_tok);
+    reduce_mirror_kernel<true><<<gr, 256, 0, s>>>(H, (int)d, P, dp, rp, nt128, vec_h, mu_r);
   else
-    reduce_mirror_kernel<false><<<gr, 256, 0, s>>>(H, (int)d, P, dp, splits, nt128, vec_h, mu_r,
-                                                   shift_tok);
+    reduce_mirror_kernel<false><<<gr, 256, 0, s>>>(H, (int)d, P, dp, rp, nt128, vec_h, mu_r);
   return hipGetLastError();
 }
 
