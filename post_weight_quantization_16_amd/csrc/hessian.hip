@@ -38,6 +38,7 @@
 #include <mutex>
 
 #include "common.hpp"
+#include "split_plan.hpp"
 
 namespace gq {
 namespace {
@@ -143,12 +144,6 @@ __global__ __launch_bounds__(256) void shift_mean_kernel(const uint16_t* __restr
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-__device__ __forceinline__ void tile_of(int idx, int nt, int& ti, int& tj) {
-  int r = 0;
-  while (idx >= nt - r) { idx -= nt - r; ++r; }
-  ti = r;
-  tj = r + idx;
-}
 
 // 8x8 transpose of 16-bit values: in[r] holds columns 0..7 of token row r;
 // out[c] holds token rows 0..7 of column c.
@@ -341,85 +336,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int fswz(int row) { return (row & 3) << 2; }
 
-// Tile order for L2 reuse.  The upper-triangle tiles of one split are listed
-// block by block: panels are grouped in fours, blocks (I, J) with I <= J in
-// row-major order, tiles inside a block row-major (upper triangle only on
-// the diagonal).  The list is repeated for every split (split-major), cut
-// into 8 contiguous runs, and workgroup L (which runs on XCD L % 8) takes
-// element L / 8 of run L % 8.  The 32 tiles an XCD runs at once then come
-// from two or three neighbouring blocks of one split, so they read about a
-// dozen panels at the same tokens from one L2.
-__device__ __forceinline__ void block_tile(int r, int nt, int& ti, int& tj) {
-  const int ng = nt / 4;
-  for (int I = 0; I < ng; ++I)
-    for (int J = I; J < ng; ++J) {
-      const int n = (I == J) ? 10 : 16;
-      if (r < n) {
-        int a, b;
-        if (I == J) tile_of(r, 4, a, b);
-        else { a = r / 4; b = r % 4; }
-        ti = 4 * I + a;
-        tj = 4 * J + b;
-        return;
-      }
-      r -= n;
-    }
-  ti = tj = 0;   // not reached for r < nt(nt+1)/2
-}
 
-// Token splits.  Every tile's token range is cut into S splits of `chunk`
-// tokens, except (mixed plan) the tiles of the blocks in `hi_mask`, cut into
-// S+1 splits of `chunk_hi`: with tiles·S workgroups a few short of a whole
-// number of rounds of the CUs, the extra splits fill the last round.  Each
-// XCD's run then starts with its share of the long workgroups (the S-split
-// tiles, split by split) and ends with its share of the short ones, so the
-// rounds stay nearly even (longest first).
-struct SplitPlan {
-  int64_t chunk, chunk_hi;
-  int S;
-  int hi_tiles;              // tiles in hi blocks (0: uniform plan)
-  int long_per_xcd, short_per_xcd;
-  uint64_t hi_mask;          // bit b: block b (upper blocks of 4x4 panels, row-major) has S+1 splits
-};
-
-__device__ __forceinline__ int block_size(int b, int ng) {
-  int I = 0;
-  while (b >= ng - I) { b -= ng - I; ++I; }
-  return b == 0 ? 10 : 16;   // the diagonal block of row I comes first
-}
-// the k-th tile (block order) among the blocks whose hi_mask bit equals `hi`
-__device__ __forceinline__ int select_tile(int k, int ng, uint64_t mask, bool hi) {
-  int r = 0;
-  const int nb = ng * (ng + 1) / 2;
-  for (int b = 0; b < nb; ++b) {
-    const int n = block_size(b, ng);
-    if ((((mask >> b) & 1u) != 0) == hi) {
-      if (k < n) return r + k;
-      k -= n;
-    }
-    r += n;
-  }
-  return r;   // not reached for k below the selected tiles' count
-}
 
 __device__ __forceinline__ void fast_tile(int L, int nt, int tiles, const SplitPlan& sp, int& ti,
                                           int& tj, int& split, int64_t& chunk) {
   const int grid = (int)gridDim.x;
   chunk = sp.chunk;
   if (sp.hi_tiles > 0) {
-    const int x = L & 7, p = L >> 3, ng = nt / 4;
-    int r;
-    if (p < sp.long_per_xcd) {
-      const int idx = x * sp.long_per_xcd + p, lo_tiles = tiles - sp.hi_tiles;
-      split = idx / lo_tiles;
-      r = select_tile(idx % lo_tiles, ng, sp.hi_mask, false);
-    } else {
-      const int idx = x * sp.short_per_xcd + (p - sp.long_per_xcd);
-      split = idx / sp.hi_tiles;
-      r = select_tile(idx % sp.hi_tiles, ng, sp.hi_mask, true);
-      chunk = sp.chunk_hi;
-    }
-    block_tile(r, nt, ti, tj);
+    mixed_unit(L, nt, tiles, sp, ti, tj, split, chunk);
   } else if (nt % 4 == 0 && grid % 8 == 0) {
     const int u = (L & 7) * (grid / 8) + (L >> 3);
     split = u / tiles;
@@ -644,14 +568,6 @@ __global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z
 // trip); the finished strip goes through LDS to be written transposed, so
 // both writes are coalesced.
 constexpr int RS = 32;   // strip rows
-// Split counts per tile: S, or S+1 for the 128-tiles inside the hi blocks
-// of 4x4 256-tiles (ng_hi > 0 and the block's hi_mask bit set), with the
-// matching shift count.
-struct ReducePlan {
-  int S, ng_hi;
-  uint64_t hi_mask;
-  double shift_lo, shift_hi;
-};
 template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
                                                             const float* __restrict__ P,
@@ -660,16 +576,9 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
                                                             const uint16_t* __restrict__ mu) {
   int ti, tj;
   tile_of(blockIdx.x >> 2, nt, ti, tj);
-  int splits = rp.S;
-  double shift_tok = rp.shift_lo;
-  if (rp.ng_hi > 0) {
-    const int I = ti / 8, J = tj / 8;   // 128-tiles -> blocks of 4x4 256-tiles
-    const int b = I * rp.ng_hi - I * (I - 1) / 2 + (J - I);
-    if ((rp.hi_mask >> b) & 1u) {
-      splits = rp.S + 1;
-      shift_tok = rp.shift_hi;
-    }
-  }
+  const bool hi = reduce_tile_hi(rp, ti, tj);
+  const int splits = hi ? rp.S + 1 : rp.S;
+  const double shift_tok = hi ? rp.shift_hi : rp.shift_lo;
   const int r0 = (blockIdx.x & 3) * RS;   // the strip's first row inside the tile
   __shared__ float T[RS][HT + 1];
   __shared__ double mr[RS], mc[HT];
@@ -796,56 +705,7 @@ int fast_splits(int64_t d, int64_t n_tok) {
   return (int)ceil_div(n_tok, chunk);
 }
 
-// Tokens' worth of μμᵀ the shift MFMAs take out of one tile over `splits`
-// splits of `chunk` tokens: one shift per started group of kShiftTok tokens
-// (stages of `step` tokens, groups rounded up).
-double shift_count(int64_t n_tok, int64_t chunk, int splits, int step) {
-  double c = 0.0;
-  for (int sp = 0; sp < splits; ++sp) {
-    const int64_t rows = std::min<int64_t>(n_tok, (sp + 1) * chunk) - sp * chunk;
-    c += (double)ceil_div(ceil_div(rows, step), kShiftTok / step) * kShiftTok;
-  }
-  return c;
-}
 
-// The mixed split plan for the 256-tile path: give the tiles of a few 4x4
-// blocks one split more so that the workgroup count becomes a whole number
-// of rounds of the CUs, with the same count of long and of short workgroups
-// on every XCD.  Returns the uniform plan when no set of blocks fits (the
-// blocks are chosen as the first `a` diagonal and `b` off-diagonal ones
-// with 10a + 16b the missing count).
-SplitPlan mixed_plan(int64_t d, int64_t n_tok, int S, int64_t chunk) {
-  SplitPlan u{chunk, chunk, S, 0, 0, 0, 0};
-  const int nt = (int)ceil_div(d, FT);
-  if (nt % 4 != 0 || S < 2) return u;
-  const int ng = nt / 4, nb = ng * (ng + 1) / 2;
-  if (nb > 64) return u;
-  const int tiles = nt * (nt + 1) / 2;
-  const int64_t chunk_hi = ceil_div(ceil_div(n_tok, S + 1), FK) * FK;
-  if (ceil_div(n_tok, chunk_hi) != S + 1) return u;
-  const int units = tiles * S;
-  const int need = (int)(ceil_div(units, kCUs) * kCUs) - units;
-  if (need == 0) return u;
-  for (int a = 0; a <= ng; ++a) {
-    const int rest = need - 10 * a;
-    if (rest < 0) break;
-    if (rest % 16 != 0 || rest / 16 > ng * (ng - 1) / 2) continue;
-    const int b = rest / 16;
-    const int hi_tiles = need;   // 10a + 16b tiles gain one split each
-    const int lo_units = (tiles - hi_tiles) * S, hi_units = hi_tiles * (S + 1);
-    if (lo_units % 8 != 0 || hi_units % 8 != 0) continue;
-    uint64_t mask = 0;
-    int da = 0, db = 0, blk = 0;
-    for (int I = 0; I < ng; ++I)
-      for (int J = I; J < ng; ++J, ++blk) {
-        if (I == J && da < a) { mask |= 1ull << blk; ++da; }
-        if (I != J && db < b) { mask |= 1ull << blk; ++db; }
-      }
-    SplitPlan p{chunk, chunk_hi, S, hi_tiles, lo_units / 8, hi_units / 8, mask};
-    return p;
-  }
-  return u;
-}
 
 }  // namespace
 
@@ -883,7 +743,7 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   const int64_t chunk = ceil_div(ceil_div(n_tok, std::min(want, fit)), step) * step;
   const int splits = (int)ceil_div(n_tok, chunk);
   SplitPlan plan{chunk, chunk, splits, 0, 0, 0, 0};
-  if (fast && fit > splits) plan = mixed_plan(d, n_tok, splits, chunk);
+  if (fast && fit > splits) plan = mixed_plan(d, n_tok, splits, chunk, FT, FK, kCUs);
   const int nslots = plan.hi_tiles > 0 ? splits + 1 : splits;   // partial Hessians written
   uint16_t* mu = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(part * nslots));
   uint16_t* zero16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(mu) + align_up((size_t)dp * 2));
@@ -906,11 +766,11 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
     const unsigned grid = (unsigned)(plan.hi_tiles > 0
                                          ? (tiles - plan.hi_tiles) * splits + plan.hi_tiles * (splits + 1)
                                          : tiles * splits);
-    shift_tok = shift_count(n_tok, chunk, splits, FK);
+    shift_tok = shift_count(n_tok, chunk, splits, FK, kShiftTok);
     if (plan.hi_tiles > 0) {
       rp.ng_hi = nt / 4;
       rp.hi_mask = plan.hi_mask;
-      rp.shift_hi = shift_count(n_tok, plan.chunk_hi, splits + 1, FK);
+      rp.shift_hi = shift_count(n_tok, plan.chunk_hi, splits + 1, FK, kShiftTok);
     }
     zero_chunk_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(zero16));
     if ((e = hipGetLastError()) != hipSuccess) return e;
