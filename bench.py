@@ -218,6 +218,28 @@ def extras(gq, torch, wl, W, X, params, H, ws_h, ws_p, stream):
             "ms": t, "GB_per_s": byts / (t * 1e-3) / 1e9, "frac_hbm": byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "TFLOP_per_s": flop / (t * 1e-3) / 1e12,
             "frac_f16_mfma": flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bytes": byts}
+    # the same product on a large layer's shape (28672 x 8192, 4-bit g128): any
+    # word stream is a valid dense code stream, so the export is random words
+    # with random half scales and zero codes
+    Nl, Kl = 28672, 8192
+    gen = torch.Generator(device=W.device).manual_seed(7)
+    exl = gq.Exported(
+        torch.randint(-2**31, 2**31 - 1, (Nl, Kl * 4 // 32), dtype=torch.int32, device=W.device,
+                      generator=gen),
+        (torch.rand(Nl, Kl // 128, device=W.device, generator=gen) * 0.01 + 1e-3).to(torch.float16),
+        torch.randint(0, 16, (Nl, Kl // 128), device=W.device, generator=gen).to(torch.float16))
+    for M in (1, 4, 64):
+        A = torch.randn(M, Kl, device=W.device).to(torch.float16)
+        C = torch.empty(M, Nl, device=W.device)
+        ws_w = torch.empty(gq.workspace_bytes(4, Nl, Kl, M), dtype=torch.uint8, device=W.device)
+        t = time_events(lambda: gq.w4a16_gemm(A, exl, 4, 128, out=C, ws=ws_w), 20, stream)
+        byts = Nl * Kl // 2 + 2 * 2 * Nl * (Kl // 128) + M * Kl * 2 + M * Nl * 4
+        flop = 2 * M * Nl * Kl
+        out[f"w4a16_28672x8192_M{M}"] = {
+            "ms": t, "GB_per_s": byts / (t * 1e-3) / 1e9, "frac_hbm": byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "TFLOP_per_s": flop / (t * 1e-3) / 1e12,
+            "frac_f16_mfma": flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bytes": byts}
+    del exl
     # OBQ comparator on a tiny layer: 2048 rows x 128 columns
     Wt = torch.randn(2048, 128, device=W.device) * 0.02
     Xt = torch.randn(4096, 128, device=W.device).to(torch.bfloat16)

@@ -22,16 +22,17 @@
 // same way ((a_j, a_j+4) inside each group of 8), which leaves every dot
 // product and MFMA sum unchanged.
 //   gemv_kernel  (M <= 4): bound by the weights' HBM traffic and the
-//                dequantization.  A sits in LDS as packed 16-bit pairs
-//                (staged while the first two chunks' words are in flight); a wave
-//                takes 2 weight rows at a time, lane l their chunks l, l+64,
-//                ... (the next chunk's words are in flight while the current
-//                one is used); dot products with v_dot2_f32_{f16,bf16} on
-//                packed pairs, reduced across the wave.
+//                dequantization.  A sits in LDS as packed 16-bit pairs,
+//                staged once per workgroup (at most four per CU) while the
+//                first weight words are in flight; a wave takes 2 weight rows
+//                at a time, lane l their chunks l, l+64, ..., and walks its
+//                row sets as one stream with the words of the next two items
+//                in flight; dot products with v_dot2_f32_{f16,bf16} on packed
+//                pairs, reduced across the wave at the end of each row set.
 //   gemm_kernel  (M > 4): 64x64 output tiles, K in steps of 128 staged in
 //                LDS as packed pairs (the W tile dequantized by all 256
 //                threads, one 32-code chunk each), v_mfma_f32_32x32x16_{f16,
-//                bf16}, the next step's global reads in flight during the
+//                bf16}, the next two steps' global reads in flight during the
 //                current one.  Few tiles (small M·N) split K over blockIdx.z
 //                into fp32 partials in the caller's workspace, summed in split
 //                order by reduce_kernel, so the result does not depend on
@@ -54,7 +55,13 @@ struct WArgs {
   const int32_t* g_idx;
   int64_t N; float* C; int64_t ldc;
   float* P; int64_t kper;   // split-K partials [splits x M x N] (null: no split) and K per split
+  uint64_t cpg_magic;       // ceil(2^32 / chunks per group), up to 2^32
 };
+// group of chunk c: c / (chunks per group) as a multiply-high, exact for
+// c < 2^11 (K <= 65536) and at most 2^20 chunks per group
+__device__ __forceinline__ int chunk_group(const WArgs& a, int c) {
+  return (int)(((uint64_t)(uint32_t)c * a.cpg_magic) >> 32);
+}
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
@@ -81,8 +88,8 @@ __device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ row, int
                                            int64_t c, uint32_t (&w)[BITS]) {
   const int64_t w0 = c * BITS;
   if (w0 + BITS <= row_words) {
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) w[i] = row[w0 + i];
+    // one vector load (dwordx2/x3/x4; global loads need 4-byte alignment only)
+    __builtin_memcpy(w, row + w0, sizeof(w));
   } else {
 #pragma unroll
     for (int i = 0; i < BITS; ++i) w[i] = w0 + i < row_words ? row[w0 + i] : 0u;
@@ -186,16 +193,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
       f.s[r] = 0;
       f.z[r] = 0;
       if (!GIDX) {
-        const int64_t gi = c * 32 / a.g;
+        const int64_t gi = chunk_group(a, (int)c);
         f.s[r] = a.s16[n * a.ng + gi];
         f.z[r] = a.z16[n * a.ng + gi];
       }
     }
   };
+  // One stream per wave: item (set, j) is chunk slot j of row set `set`
+  // (rows n0 = (wave + set·nwaves)·RW .., chunk c = lane + 64j); every lane
+  // runs the same items (slots past the row's chunks add nothing), so the
+  // wave reduction at each row set's last slot is uniform.  The words of the
+  // next two items are always in flight, across row sets too; the first two
+  // are issued before A is staged.  Item positions advance by additions.
+  const int cps = (int)((nch + 63) / 64);
+  const int64_t set_stride = nwaves * RW;
+  int64_t f_n0 = wave * RW;   // the next item to fetch
+  int f_j = 0;
+  auto fetch_next = [&](Fetch<BITS>& f) {
+    const int c = lane + 64 * f_j;
+    if (f_n0 < a.N && c < nch) fetch(f_n0, c, f);
+    if (++f_j == cps) { f_j = 0; f_n0 += set_stride; }
+  };
   Fetch<BITS> cur, nxt;
-  // the first rows' first two chunks are in flight while A is staged
-  if (wave * RW < a.N && lane < nch) fetch(wave * RW, lane, cur);
-  if (wave * RW < a.N && lane + 64 < nch) fetch(wave * RW, lane + 64, nxt);
+  fetch_next(cur);
+  fetch_next(nxt);
   for (int64_t e = t; e < MM * Kp / 8; e += 256) {   // 8 values (16 bytes) per item
     const int64_t m = e / (Kp / 8), k = (e % (Kp / 8)) * 8;
     u32x4 v = {0u, 0u, 0u, 0u};
@@ -215,20 +236,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
     *reinterpret_cast<u32x4*>(Ap + m * KW + k / 2) = v;
   }
   __syncthreads();
-  for (int64_t n0 = wave * RW; n0 < a.N; n0 += nwaves * RW) {
-    float acc[RW][MM];
+  float acc[RW][MM];
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+  for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
-    int64_t c = lane;
-    const bool first = n0 == wave * RW;
-    if (!first && c < nch) fetch(n0, c, cur);
-    bool have_next = first;   // the first rows' second chunk is already on its way
-    while (c < nch) {
-      const int64_t cn = c + 64;
-      if (cn < nch && !have_next) fetch(n0, cn, nxt);   // in flight while this chunk is used
-      have_next = false;
+    for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
+  int64_t n0 = wave * RW;
+  int j = 0;
+  while (n0 < a.N) {
+    const int c = lane + 64 * j;
+    Fetch<BITS> nx2;
+    fetch_next(nx2);   // two items ahead
+    if (c < nch) {
       uint32_t ap[MM][16];
 #pragma unroll
       for (int m = 0; m < MM; ++m)
@@ -248,17 +267,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
 #pragma unroll
           for (int p = 0; p < 16; ++p) acc[r][m] = dot2<F16>(ap[m][p], wp[p], acc[r][m]);
       }
-      cur = nxt;
-      c = cn;
     }
+    cur = nxt;
+    nxt = nx2;
+    if (j == cps - 1) {   // the row set's last slot: reduce and store
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int m = 0; m < MM; ++m) {
-        float v = acc[r][m];
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-        if (lane == 0 && m < a.M && n0 + r < a.N) a.C[m * a.ldc + n0 + r] = v;
-      }
+        for (int m = 0; m < MM; ++m) {
+          float v = acc[r][m];
+          for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+          if (lane == 0 && m < a.M && n0 + r < a.N) a.C[m * a.ldc + n0 + r] = v;
+          acc[r][m] = 0.f;
+        }
+    }
+    if (++j == cps) { j = 0; n0 += set_stride; }
   }
 }
 
@@ -281,6 +304,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(WArgs a) {
   const int ar = t >> 2, ak = (t & 3) * 32;
   const int wr = t & 63, wc = t >> 6;
   const int64_t am = m0 + ar;
+  const int nch = (int)((a.K + 31) / 32);
   const int64_t wnr = n0 + wr < a.N ? n0 + wr : a.N - 1;   // rows past N: never stored
   const uint32_t* wrow = a.q + wnr * a.row_words;
   struct Stage {
@@ -307,12 +331,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(WArgs a) {
         for (int j = 0; j < 4; ++j) st.av[q][j] = h[2 * j] | (h[2 * j + 1] << 16);
       }
     }
-    const int64_t c = k0 / 32 + wc;
+    const int c = (int)(k0 >> 5) + wc;
     load_chunk<BITS>(wrow, a.row_words, c, st.w);
     st.s = 0;
     st.z = 0;
     if (!GIDX) {
-      const int64_t gi = (c * 32 < a.K ? c * 32 : a.K - 1) / a.g;
+      const int64_t gi = chunk_group(a, c < nch ? c : nch - 1);
       st.s = a.s16[wnr * a.ng + gi];
       st.z = a.z16[wnr * a.ng + gi];
     }
@@ -320,11 +344,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(WArgs a) {
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  Stage cur, nxt;
+  // three stages: the current one and the next two in flight
+  Stage cur, nxt, nx2;
   if (kb < ke) fetch(kb, cur);
+  if (kb + TK < ke) fetch(kb + TK, nxt);
   for (int64_t k0 = kb; k0 < ke; k0 += TK) {
     const bool more = k0 + TK < ke;
-    if (more) fetch(k0 + TK, nxt);   // in flight during this step
+    if (k0 + 2 * TK < ke) fetch(k0 + 2 * TK, nx2);
     // this step's tiles into LDS: A as loaded; W dequantized (codes past K
     // pair with zero activations, so their values do not matter)
 #pragma unroll
@@ -351,7 +377,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(WArgs a) {
                                                       __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
     }
     __syncthreads();
-    if (more) cur = nxt;
+    if (more) {
+      cur = nxt;
+      nxt = nx2;
+    }
   }
   float* out = a.P ? a.P + (int64_t)blockIdx.z * a.M * a.N : a.C;
   const int64_t ldo = a.P ? a.N : a.ldc;
@@ -398,14 +427,17 @@ hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_
                         const int32_t* g_idx, int64_t g, int64_t ng, int64_t N, float* C,
                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t s) {
   const int vec_a = ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
+  const uint64_t cpg = g >= K ? (1u << 20) : (uint64_t)(g / 32);   // one group: all in group 0
+  const uint64_t magic = ((uint64_t)1 << 32) / cpg + (((uint64_t)1 << 32) % cpg != 0);
   WArgs a{static_cast<const uint16_t*>(A), M, K, lda, vec_a, qweight, bits, ceil_div(K * bits, 32),
-          s16, z16, ng, g, g_idx, N, C, ldc, nullptr, K};
+          s16, z16, ng, g, g_idx, N, C, ldc, nullptr, K, magic};
   const bool f16 = a_dtype == GPTQ_F16;
   const bool gx = g_idx != nullptr;
   const int mm = M <= 1 ? 1 : M <= 2 ? 2 : 4;
   const int64_t Kp = ceil_div(K, 32) * 32;
   if (M <= 4 && (int64_t)mm * Kp * 2 <= kGemvLds) {
-    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(N, 4 * RW), 4096));
+    // at most four workgroups per CU: each stages A once and loops over rows
+    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(N, 4 * RW), 1024));
     const size_t lds = (size_t)mm * Kp * 2;
 #define GQ_GEMV(F, B, MM, GX) gemv_kernel<F, B, MM, GX><<<grid, 256, lds, s>>>(a)
 #define GQ_GEMV_G(F, B, MM) \
