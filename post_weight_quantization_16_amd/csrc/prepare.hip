@@ -242,149 +242,452 @@ struct PanelArgs {
   float* G; int64_t d; int k0, kb;   // G: the n x n matrix being factored (n = d here)
   float* Linv; int* status;
   int np;          // panel workgroups in the launch
-  int spin_limit;  // bound on every flag wait (polls)
+  int spin_limit;  // bound on every flag wait (polls; 0 allows none)
   int64_t ld;      // row stride of G and Linv
   int piv_base;    // index of G's first column in the whole factorization
 };
 
-constexpr int LS = NB + 2;       // LDS row stride: the half-waves' MFMA reads hit disjoint banks
-constexpr int PXS = NB + 1;      // stride of the published x rows (strip MFMA reads of 16 rows)
-constexpr int BLK = NB * LS;     // one 64x64 block in LDS (floats)
-static_assert(4 * BLK + 4 * NB <= gemm_detail::GEMM_SMEM_FLOATS, "panel LDS exceeds the shared buffer");
+// A panel workgroup keeps four 64x64 blocks in LDS with float4-aligned rows
+// and works on them as 16x16 tiles.  In the tile layout a lane (l16, kq) of
+// a wave (l16 = lane % 16, kq = lane / 16) holds row l16, columns
+// 4kq..4kq+3 of a tile: one float4 in registers, one ds_read_b128 in LDS.
+constexpr int PS = NB + 4;       // LDS row stride (floats)
+constexpr int PBLK = NB * PS;    // one block
 
-// row / column of accumulator element e in the 32x32 tile (mi, ni)
-__device__ __forceinline__ int acc_row(int mi, int lane, int e) {
-  return 32 * mi + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+__device__ __forceinline__ float* tile(float* B, int i, int j) { return B + 16 * i * PS + 16 * j; }
+__device__ __forceinline__ f32x4 ld_t(const float* T, int l16, int kq) {
+  return *reinterpret_cast<const f32x4*>(T + l16 * PS + 4 * kq);
+}
+__device__ __forceinline__ void st_t(float* T, int l16, int kq, f32x4 v) {
+  *reinterpret_cast<f32x4*>(T + l16 * PS + 4 * kq) = v;
 }
 
-// One 64-wide Cholesky panel at column k0 (kb <= 64 columns), for workgroup
-// b of the panel's grid:
-//   the previous panel's contribution to this panel's columns,
-//     G[:, panel] −= L21ₚ·L21ₚ[panel rows]ᵀ (the trailing updates of the
-//     previous launch skip these columns so this launch can run it): the
-//     diagonal block's part before the sweep, the workgroup's rows' part
-//     (only the L21 solve needs it) by wave 0 after its own steps,
-//   L11 = chol(G11),  X = L11⁻¹,  L21 = G21·Xᵀ.
-// Every workgroup (4 waves) factors and inverts the small diagonal block
-// itself, so no workgroup waits for another; workgroup b then solves the
-// 64 rows k0+kb+64b .. +63 of the panel in place in G, and workgroup 0
-// stores X into the diagonal block of Linv (L11 itself is not needed
-// later).  The block is padded to 64 with the identity.
-//
-// The factor and the inverse are one right-looking sweep.  Lane i of wave w
-// holds A[i][16w..16w+15] (a) and X[16w..16w+15][i] (r).  Wave w owns steps
-// 16w..16w+15: step j takes the pivot from lane j, scales column j into
-// l_ij = a_ij / l_jj (zeroed for i <= j), finishes x_j = r_j / l_jj,
-// applies a_ik −= l_ij·l_kj and r_k −= l_kj·x_j to its next column at once
-// (l_kj from lane k by readlane: that column's pivot is next), publishes l
-// and x for step j in LDS, updates its remaining columns with l_kj read back
-// from the published row, and raises the step's flag.  Before its own
-// steps, wave w consumes steps 0 .. 16w−1 four at a time as their flags
-// appear, applying the same update to its 16 columns; the last four are
-// held in registers and applied to each column just before its pivot, so
-// the hand-over from wave w−1 waits for one batch of reads, not for the
-// whole batch's arithmetic.  The owner of a step never waits for another
-// wave, so the serial chain carries no workgroup barrier; every wait is on a
-// step some wave has already begun or will begin without waiting (wave 0
-// waits for nothing), and is bounded.  A non-positive (or NaN/inf) pivot is
-// recorded in *status (smallest index wins) and replaced by 1 so the
-// arithmetic stays finite.
-//
-// L21's 16-column strips: X's rows 16w..16w+15 are final once wave w's
-// steps are done, so wave w (w < 3) solves its strip L21[:, 16w..] =
-// G21·X[16w..16w+15, :]ᵀ (v_mfma_f32_16x16x4f32, 64 rows) while the later
-// waves are still sweeping, and workgroup 0's wave w stores those X rows to
-// Linv from its registers.  The last strip is split over the four waves
-// after the sweep.
-// L21[16rb.., 16c..16c+15] for row blocks rb in [rb0, rb1) of this
-// workgroup's 64 rows: G21 (BS, already reduced by the pre-update) times the
-// published X rows 16c..16c+15 (PX), v_mfma_f32_16x16x4f32 (A: lane holds
-// (row lane%16, k lane/16), B: (k lane/16, column lane%16), C: rows
-// 4·(lane/16) + v, column lane%16), stored to G.
-__device__ __forceinline__ void strip(const float* BS, const float* PX, float* G, int64_t d,
-                                      int64_t ld, int64_t R0, int k0, int kb, int c, int rb0,
-                                      int rb1, int lane) {
-  const int m = lane & 15, kq = lane >> 4;
-  for (int rb = rb0; rb < rb1; ++rb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+// acc + sign·R·Sᵀ for 16-row operands R and S of K columns, in the tile
+// layout.  v_mfma_f32_16x16x4f32 takes a[x][k] = S[x][k] and b[k][y] =
+// R[y][k] (lane (l16, kq) supplies row l16 of each) and leaves D[x][y] at
+// lane (y, kq), rows x = 4kq + v: D = S·Rᵀ = (R·Sᵀ)ᵀ, i.e. row y of R·Sᵀ.
+// Lane group kq takes k = (K/4)·kq + step, the same permutation for both
+// operands, so each lane reads whole float4s.
+template <int K>
+__device__ __forceinline__ f32x4 mm_rs(const float* R, const float* S, f32x4 acc, float sign,
+                                       int l16, int kq) {
+  constexpr int NQ = K / 16;
+  f32x4 rv[NQ], sv[NQ];
 #pragma unroll
-    for (int k4 = 0; k4 < NB; k4 += 4) {
-      const float av = BS[(16 * rb + m) * LS + k4 + kq];
-      const float bv = PX[(16 * c + m) * PXS + k4 + kq];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-    }
-    const int col = 16 * c + m;
+  for (int q = 0; q < NQ; ++q) {
+    rv[q] = *reinterpret_cast<const f32x4*>(R + l16 * PS + (K / 4) * kq + 4 * q);
+    sv[q] = *reinterpret_cast<const f32x4*>(S + l16 * PS + (K / 4) * kq + 4 * q);
+  }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t row = R0 + 16 * rb + 4 * kq + v;
-      if (row < d && col < kb) G[row * ld + k0 + col] = acc[v];
-    }
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sign * sv[q][u], rv[q][u], acc, 0, 0, 0);
+  return acc;
+}
+
+// acc + sign·R·Z for 16x16 tiles, Z read by columns (a[x][k] = Z[k][x]).
+__device__ __forceinline__ f32x4 mm_rz(const float* R, const float* Z, f32x4 acc, float sign,
+                                       int l16, int kq) {
+  const f32x4 rv = ld_t(R, l16, kq);
+  float zv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) zv[u] = Z[(4 * kq + u) * PS + l16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sign * zv[u], rv[u], acc, 0, 0, 0);
+  return acc;
+}
+
+// lane J of every 16-lane row (DPP row_newbcast)
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xf, 0xf, true));
+}
+// the value of 16-lane row Gr, at the same position, in all four rows (a
+// permlane32 swap brings Gr's half to both halves, a permlane16 swap its row
+// to both rows of each half)
+template <int Gr>
+__device__ __forceinline__ float grp_bcast(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned y = (Gr < 2) ? p[0] : p[1];
+  const auto q = __builtin_amdgcn_permlane16_swap(y, y, false, false);
+  return __uint_as_float((Gr & 1) ? q[1] : q[0]);
+}
+
+template <int J>
+__device__ __forceinline__ void f16_step(float (&a)[4], float (&r)[4], float& piv, float& inv_row,
+                                         int i, int& bad) {
+  constexpr int g = J >> 2, e = J & 3;
+  const bool b = !(piv > 0.f) || !(piv < INFINITY);
+  bad = (b && bad < 0) ? J : bad;
+  // one hardware reciprocal square root on the serial chain (about 1 ulp)
+  const float inv = b ? 1.f : __builtin_amdgcn_rsqf(piv);
+  if constexpr (J < 15) {
+    constexpr int g1 = (J + 1) >> 2, e1 = (J + 1) & 3;
+    const float sa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[e]), 16 * g + J + 1));
+    const float s1 =
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[e1]), 16 * g1 + J + 1));
+    const float c = sa * inv;   // l[J+1][J]
+    piv = fmaf(-c, c, s1);
+  }
+  const float col = grp_bcast<g>(a[e]);   // A[i][J]
+  const float m = i > J ? -(col * (inv * inv)) : 0.f;
+  inv_row = i == J ? inv : inv_row;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    a[q] = fmaf(row_bcast<J>(a[q]), m, a[q]);
+    r[q] = fmaf(row_bcast<J>(r[q]), m, r[q]);
   }
 }
 
-// The rows' share of the pre-update, BS −= Q·Pᵀ with Q = the previous
-// panel's values in this workgroup's 64 rows and P = its values in the
-// panel's rows, by one wave from registers (v_mfma_f32_32x32x2f32; lanes
-// 0-31 take k in [0, 32), lanes 32-63 k in [32, 64), so each lane's 32
-// values of a row are contiguous).  Rows past d or kb count as zero.
-__device__ __forceinline__ void rows_preupdate(const float* G, int64_t d, int64_t ld, int64_t R0,
-                                               int k0, int kb, int kp, float* BS, int lane) {
-  const int h = lane >> 5, l32 = lane & 31;
-  const bool vec = (ld & 3) == 0;
-  float qv[2][32], pv[2][32];
+template <int J>
+__device__ __forceinline__ void f16_steps(float (&a)[4], float (&r)[4], float& piv, float& inv_row,
+                                          int i, int& bad) {
+  f16_step<J>(a, r, piv, inv_row, i, bad);
+  if constexpr (J < 15) f16_steps<J + 1>(a, r, piv, inv_row, i, bad);
+}
+
+// Cholesky factor and inverse of a 16x16 SPD tile held by one wave in the
+// tile layout (both triangles): x receives X = L⁻¹ (lower, exact zeros
+// above the diagonal) in the same layout; bad the first non-positive (or
+// NaN/inf) pivot's index, else −1 (such a pivot is replaced by 1 so the
+// arithmetic stays finite).  Right-looking, one step per column j: with p
+// the pivot and m_i = A[i][j]/p for i > j, A[i][k] −= m_i·A[j][k] (the
+// rank-1 update by l = A[:, j]/√p, row j standing in for column j by
+// symmetry) and R[i][k] −= m_i·R[j][k] on rows R of the identity, which
+// turns R into √p-scaled rows of X; row i of X is R's row i times 1/√p of
+// step i.  Row j is lane j of each 16-lane row (one DPP source operand);
+// column j sits in one 16-lane row and reaches the other three by two
+// permlane swaps.  The next pivot comes from two entries read before the
+// step's update, so the serial chain per step is rsq, mul, fma.
+__device__ __forceinline__ void factor16(const f32x4 acc, float (&x)[4], int l16, int kq,
+                                         int& bad) {
+  float a[4] = {acc[0], acc[1], acc[2], acc[3]};
+  float r[4];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int64_t qr = R0 + 32 * x + l32;
-    const int pr = 32 * x + l32;
-    const bool qok = qr < d, pok = pr < kb;
-    const float* qs = G + (qok ? qr : 0) * ld + kp + 32 * h;
-    const float* ps = G + (int64_t)(k0 + (pok ? pr : 0)) * ld + kp + 32 * h;
-    if (vec) {
+  for (int e = 0; e < 4; ++e) r[e] = (l16 == 4 * kq + e) ? 1.f : 0.f;
+  float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[0]), 0));
+  float inv_row = 0.f;
+  bad = -1;
+  f16_steps<0>(a, r, piv, inv_row, l16, bad);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f32x4 q4 = *reinterpret_cast<const f32x4*>(qs + 4 * j);
-        const f32x4 p4 = *reinterpret_cast<const f32x4*>(ps + 4 * j);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          qv[x][4 * j + u] = qok ? q4[u] : 0.f;
-          pv[x][4 * j + u] = pok ? p4[u] : 0.f;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        qv[x][kk] = qok ? qs[kk] : 0.f;
-        pv[x][kk] = pok ? ps[kk] : 0.f;
-      }
-    }
-  }
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      f32x16 acc;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[mi][kk], pv[ni][kk], acc, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) BS[acc_row(mi, lane, e) * LS + 32 * ni + l32] -= acc[e];
-    }
+  for (int e = 0; e < 4; ++e) x[e] = r[e] * inv_row;
 }
 
 constexpr int kSpinLimit = 1 << 20;   // default bound on a flag wait (never reached)
 
+// What the routines of one panel workgroup's waves share.
+struct PanelCtx {
+  float *AS, *BS, *PP, *QQ;   // LDS blocks (see panel_body)
+  int* fl;                    // L_{i,s} published: fl[4i + s]
+  float *G, *Linv;
+  int64_t d, ld, R0;
+  int k0, kb, l16, kq, spin_limit;
+  bool upd, rows, stalled;
+};
+
+// Bounded wait for a flag; after one expired wait a wave stops waiting and
+// status[1] later marks the whole call, whose outputs are then undefined.
+__device__ __forceinline__ void wait_flag(PanelCtx& c, int f) {
+  for (int spin = 0; !c.stalled; ++spin) {
+    if (spin >= c.spin_limit) {
+      c.stalled = true;
+      break;
+    }
+    if (__hip_atomic_load(&c.fl[f], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+// one wave's LDS operations complete in order, so a flag stored after a
+// tile vouches for it
+__device__ __forceinline__ void publish(PanelCtx& c, int f) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __hip_atomic_store(&c.fl[f], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// a tile-layout value to row `row` (0..63 of the block), columns col..col+3
+// of a 64-column block of G (L21) or Linv (X), within [0, kb) columns
+__device__ __forceinline__ void store_row4(float* dst, bool vec, int col, int kb, f32x4 v) {
+  if (vec && col + 3 < kb) {
+    *reinterpret_cast<f32x4*>(dst) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < kb) dst[e] = v[e];
+  }
+}
+// L21 tile (rb, s) of this workgroup's rows
+__device__ __forceinline__ void store_l21(const PanelCtx& c, f32x4 v, int rb, int s) {
+  const int64_t row = c.R0 + 16 * rb + c.l16;
+  const int col = 16 * s + 4 * c.kq;
+  if (row < c.d) store_row4(c.G + row * c.ld + c.k0 + col, (c.ld & 3) == 0, col, c.kb, v);
+}
+// X tile (i, j) into Linv's diagonal block
+__device__ __forceinline__ void store_x(const PanelCtx& c, f32x4 v, int i, int j) {
+  const int row = 16 * i + c.l16, col = 16 * j + 4 * c.kq;
+  if (row < c.kb)
+    store_row4(c.Linv + (int64_t)(c.k0 + row) * c.ld + c.k0 + col, (c.ld & 3) == 0, col, c.kb, v);
+}
+
+// acc + sign·R·Sᵀ with both 16x16 operands in registers (tile layout)
+__device__ __forceinline__ f32x4 mm_reg(f32x4 r, f32x4 s, f32x4 acc, float sign) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sign * s[u], r[u], acc, 0, 0, 0);
+  return acc;
+}
+
+// X's off-diagonal tile (s, j), j < s: X_{s,j} = −X_s·Σ_{k=j}^{s−1} L_{s,k}·X_{k,j}
+// (the off-diagonal block of the inverse of a block-lower-triangular
+// matrix, one block row at a time).  Row block s >= 1 of X lives in PP's
+// row block s−1; scr is a scratch tile.
+__device__ __forceinline__ f32x4 x_tile(const PanelCtx& c, int s, int j, float* scr) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = j; k < s; ++k) {
+    const float* Z = k == j ? tile(c.AS, j, j) : tile(c.PP, k - 1, j);   // X_{k,j}
+    acc = mm_rz(tile(c.AS, s, k), Z, acc, 1.f, c.l16, c.kq);
+  }
+  st_t(scr, c.l16, c.kq, acc);
+  return mm_rz(tile(c.AS, s, s), scr, f32x4{0.f, 0.f, 0.f, 0.f}, -1.f, c.l16, c.kq);
+}
+
+// Slab 0, waves 1-3 (h = wave − 1): the previous panel's contribution to
+// A's tiles below A_00 (9 tiles) and to B's first column tile (4), K = 64
+// each; tasks h, h+3, ... two at a time so their MFMA chains interleave.
+__device__ __forceinline__ void pre_tasks(const PanelCtx& c, int h) {
+  const int l16 = c.l16, kq = c.kq;
+  for (int t0 = h; t0 < 13; t0 += 6) {
+    float* C[2];
+    const float* R[2];
+    const float* S[2];
+    bool ok[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int task = t0 + 3 * x;
+      ok[x] = task < 9 || (task < 13 && c.rows);
+      if (task < 9) {
+        const int ti = task < 2 ? 1 : (task < 5 ? 2 : 3);
+        const int tj = task < 2 ? task : (task < 5 ? task - 2 : task - 5);
+        C[x] = tile(c.AS, ti, tj);
+        R[x] = c.PP + 16 * ti * PS;
+        S[x] = c.PP + 16 * tj * PS;
+      } else {
+        const int rb = task < 13 ? task - 9 : 0;
+        C[x] = tile(c.BS, rb, 0);
+        R[x] = c.QQ + 16 * rb * PS;
+        S[x] = c.PP;
+      }
+    }
+    f32x4 rv[2][4], sv[2][4], acc[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      acc[x] = ld_t(C[x], l16, kq);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rv[x][q] = *reinterpret_cast<const f32x4*>(R[x] + l16 * PS + 16 * kq + 4 * q);
+        sv[x][q] = *reinterpret_cast<const f32x4*>(S[x] + l16 * PS + 16 * kq + 4 * q);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(-sv[x][q][u], rv[x][q][u], acc[x], 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      if (ok[x]) st_t(C[x], l16, kq, acc[x]);
+  }
+}
+
+// Slab PH−1 on A (wave 1): the slab's L tiles below row block PH
+// (L_{i,s} = A_{i,s}·X_sᵀ, published), its update of the trailing tiles
+// (i, j), PH <= j <= i, except A_PH,PH (wave 0's), and on workgroup 0 row
+// block PH−1 of X.  Operands of each group are read first and the MFMA
+// chains interleaved.
+template <int PH>
+__device__ __forceinline__ void a_helper(PanelCtx& c, bool xduty) {
+  constexpr int S = PH - 1, NA = 3 - PH;
+  const int l16 = c.l16, kq = c.kq;
+  if constexpr (NA > 0) {
+    constexpr int NO = NA * (NA + 1) / 2;
+    const f32x4 xs = ld_t(tile(c.AS, S, S), l16, kq);
+    f32x4 ai[NA], la[NA], co[NO], cw[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      ai[i] = ld_t(tile(c.AS, PH + 1 + i, S), l16, kq);
+      cw[i] = ld_t(tile(c.AS, PH + 1 + i, PH), l16, kq);
+    }
+    {
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) co[n++] = ld_t(tile(c.AS, PH + 1 + i, PH + 1 + j), l16, kq);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) la[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NA; ++i) la[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[u], ai[i][u], la[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      st_t(tile(c.AS, PH + 1 + i, S), l16, kq, la[i]);
+      publish(c, 4 * (PH + 1 + i) + S);
+    }
+    {
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j, ++n) co[n] = mm_reg(la[i], la[j], co[n], -1.f);
+    }
+    wait_flag(c, 4 * PH + S);
+    const f32x4 lph = ld_t(tile(c.AS, PH, S), l16, kq);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) cw[i] = mm_reg(la[i], lph, cw[i], -1.f);
+    {
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        st_t(tile(c.AS, PH + 1 + i, PH), l16, kq, cw[i]);
+#pragma unroll
+        for (int j = 0; j <= i; ++j, ++n) st_t(tile(c.AS, PH + 1 + i, PH + 1 + j), l16, kq, co[n]);
+      }
+    }
+  }
+  if constexpr (S >= 1) {
+    if (xduty) {
+      float* xrow = c.PP + 16 * (S - 1) * PS;
+#pragma unroll
+      for (int j = 0; j < S; ++j) st_t(xrow + 16 * j, l16, kq, x_tile(c, S, j, xrow + 48));
+    }
+  }
+}
+
+// Slab PH−1 on B row tiles rb0 .. rb0+NR−1 of this workgroup's rows: the
+// slab's L21 tile (LB = B_{rb,s}·X_sᵀ, to G), the previous panel's part of
+// column tile PH (K = 64), then the slab's update of column tiles PH..3
+// (B_{rb,j} −= LB·L_{j,s}ᵀ) as the L tiles are published.
+template <int PH, int NR>
+__device__ __forceinline__ void b_rows(PanelCtx& c, int rb0) {
+  constexpr int S = PH - 1, NJ = 4 - PH;
+  const int l16 = c.l16, kq = c.kq;
+  const f32x4 xs = ld_t(tile(c.AS, S, S), l16, kq);
+  f32x4 bs[NR], cc[NR][NJ], qv[NR][4], pv[4], lb[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    bs[r] = ld_t(tile(c.BS, rb0 + r, S), l16, kq);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cc[r][j] = ld_t(tile(c.BS, rb0 + r, PH + j), l16, kq);
+  }
+  if (c.upd) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pv[q] = *reinterpret_cast<const f32x4*>(c.PP + (16 * PH + l16) * PS + 16 * kq + 4 * q);
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        qv[r][q] = *reinterpret_cast<const f32x4*>(c.QQ + (16 * (rb0 + r) + l16) * PS + 16 * kq + 4 * q);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) lb[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) lb[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[u], bs[r][u], lb[r], 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) store_l21(c, lb[r], rb0 + r, S);
+  if (c.upd) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          cc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(-pv[q][u], qv[r][q][u], cc[r][0], 0, 0, 0);
+  }
+  f32x4 lj[NJ];
+#pragma unroll
+  for (int j = NJ - 1; j >= 0; --j) {   // the later tiles' L (wave 1) come before L_PH,s (wave 0)
+    wait_flag(c, 4 * (PH + j) + S);
+    lj[j] = ld_t(tile(c.AS, PH + j, S), l16, kq);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        cc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(-lj[j][u], lb[r][u], cc[r][j], 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) st_t(tile(c.BS, rb0 + r, PH + j), l16, kq, cc[r][j]);
+}
+
+// Slab PH: wave 0 computes L_{PH,PH−1} = A_{PH,PH−1}·X_{PH−1}ᵀ (published),
+// applies it to A_PH,PH and factors that; waves 1-3 apply slab PH−1 (B row
+// tiles 3 on wave 1 beside A, 0 and 1 on wave 2, 2 on wave 3).
+template <int PH>
+__device__ __forceinline__ void phase(PanelCtx& c, int w, float (&xr)[4], int& bad_j, bool xduty) {
+  constexpr int S = PH - 1;
+  const int l16 = c.l16, kq = c.kq;
+  if (w == 0) {
+    const f32x4 av = ld_t(tile(c.AS, PH, S), l16, kq);
+    f32x4 cc = ld_t(tile(c.AS, PH, PH), l16, kq);
+    f32x4 l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) l = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[u], av[u], l, 0, 0, 0);
+    st_t(tile(c.AS, PH, S), l16, kq, l);
+    publish(c, 4 * PH + S);
+    cc = mm_reg(l, l, cc, -1.f);
+    int bd;
+    factor16(cc, xr, l16, kq, bd);
+    if (bad_j < 0 && bd >= 0) bad_j = 16 * PH + bd;
+    st_t(tile(c.AS, PH, PH), l16, kq, f32x4{xr[0], xr[1], xr[2], xr[3]});
+  } else if (w == 1) {
+    a_helper<PH>(c, xduty);
+    if (c.rows) b_rows<PH, 1>(c, 3);
+  } else if (w == 2) {
+    if (c.rows) b_rows<PH, 2>(c, 0);
+  } else {
+    if (c.rows) b_rows<PH, 1>(c, 2);
+  }
+  __syncthreads();
+}
+
+// One 64-wide Cholesky panel at column k0 (kb <= 64 columns, padded with
+// the identity), for workgroup b of the panel's grid:
+//   the previous panel's contribution to this panel's columns,
+//     G[:, panel] −= L21ₚ·L21ₚ[panel rows]ᵀ (the trailing updates of the
+//     previous launch skip these columns so this launch can run it),
+//   L11 = chol(G11),  X = L11⁻¹,  L21 = G21·Xᵀ.
+// Every workgroup factors the diagonal block itself, so no workgroup waits
+// for another; workgroup b solves the 64 rows k0+kb+64b .. +63 of the panel
+// in place in G, and workgroup 0 also writes X into the diagonal block of
+// Linv (L11 itself is not needed later).
+//
+// Blocked in four 16-column slabs s.  Wave 0 runs the serial chain in
+// registers: L_{s,s−1} = A_{s,s−1}·X_{s−1}ᵀ, A_ss −= L_{s,s−1}·L_{s,s−1}ᵀ,
+// then the 16x16 factor of A_ss (factor16) gives X_s.  Waves 1-3 apply slab
+// s−1 meanwhile: the other L tiles of the slab, its update of the trailing
+// A tiles, and for this workgroup's rows the slab's L21 tile (stored to G)
+// and its update of the later B tiles; they also apply the previous panel's
+// contribution to B one 16-column tile ahead of its use, and (workgroup 0)
+// build X's off-diagonal tiles.  One workgroup barrier per slab; inside a
+// slab the L tiles are published through LDS flags, every wait bounded.  All
+// products are v_mfma_f32_16x16x4f32 on 16x16 tiles.
 __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __restrict__ smem) {
-  float* AS = smem;              // G11 (lower, identity-padded)
-  float* BS = smem + BLK;        // this workgroup's 64 rows of G21
-  float* XS = smem + 2 * BLK;    // before the sweep: the previous panel's rows k0..k0+63
-  // during and after the sweep: published l [64][64] in AS's place, x [64][PXS]
-  // (= X by rows) in XS's place, flags [65] after it
-  float* PL = smem;
-  float* PX = smem + 2 * BLK;
-  int* flag = reinterpret_cast<int*>(smem + 3 * BLK);
-  static_assert(NB * NB <= BLK && NB * PXS <= BLK, "published steps exceed their LDS region");
+  float* AS = smem;              // G11; its tiles become X_s (diagonal) and L_{i,s} (below)
+  float* BS = smem + PBLK;       // this workgroup's 64 rows of G21
+  float* PP = smem + 2 * PBLK;   // the previous panel's values in the panel's rows; row block
+                                 // m is free after slab m's pre-update and holds X's row m+1
+  float* QQ = smem + 3 * PBLK;   // the previous panel's values in this workgroup's rows
+  int* fl = reinterpret_cast<int*>(smem + 4 * PBLK);
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t d = p.d, ld = p.ld;
@@ -393,253 +696,120 @@ __device__ __forceinline__ void panel_body(const PanelArgs& p, int b, float* __r
   const bool upd = k0 > 0;       // previous panels are full width
   const int kp = k0 - NB;
   float* G = p.G;
-
   {
-    // all loads first, then the masks and the LDS stores (a select right
-    // after its load, or a load-store pair per element, would wait for the
-    // load at once).  Full-width panels of a 4-aligned G load float4: thread
-    // t covers rows (t >> 4) + 16u, columns 4(t & 15) .. +3.
+    // all loads first, then the masks and the LDS stores.  A keeps its lower
+    // triangle and, inside the diagonal tiles, the mirrored upper part (read
+    // transposed).  Full-width panels of a 4-aligned G load float4: thread t
+    // covers rows (t >> 4) + 16u, columns 4(t & 15) .. +3.
     if ((ld & 3) == 0 && k0 + NB <= d) {
       const int c4 = 4 * (t & 15);
-      f32x4 va[4], vb[4], vp[4];
+      f32x4 va[4], vb[4], vp[4], vq[4];
+      float vt[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = (t >> 4) + 16 * u;
-        const int64_t ra = k0 + (i < kb ? i : 0), rb = R0 + i < d ? R0 + i : 0;
+        const int64_t ra = k0 + i, rb = R0 + i < d ? R0 + i : 0;
         va[u] = *reinterpret_cast<const f32x4*>(G + ra * ld + k0 + c4);
         vb[u] = *reinterpret_cast<const f32x4*>(G + rb * ld + k0 + c4);
-        if (upd) vp[u] = *reinterpret_cast<const f32x4*>(G + ra * ld + kp + c4);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = (t >> 4) + 16 * u;
+        if (upd) {
+          vp[u] = *reinterpret_cast<const f32x4*>(G + ra * ld + kp + c4);
+          vq[u] = *reinterpret_cast<const f32x4*>(G + rb * ld + kp + c4);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = c4 + e;
-          AS[i * LS + k] = (i < kb && k <= i) ? va[u][e] : (i == k ? 1.f : 0.f);
-          BS[i * LS + k] = R0 + i < d ? vb[u][e] : 0.f;
-          if (upd) XS[i * LS + k] = i < kb ? vp[u][e] : 0.f;
+          vt[u][e] = (k > i && (k >> 4) == (i >> 4)) ? G[(int64_t)(k0 + k) * ld + k0 + i] : 0.f;
         }
       }
-    } else {
-      float va[16], vb[16], vp[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-        const bool okd = i < kb && k <= i;
-        va[u] = G[(int64_t)(k0 + (okd ? i : 0)) * ld + k0 + (okd ? k : 0)];
-        const bool okb = R0 + i < d && k < kb;
-        vb[u] = G[(okb ? R0 + i : 0) * ld + (okb ? k0 + k : 0)];
-        if (upd) vp[u] = G[(int64_t)(k0 + (i < kb ? i : 0)) * ld + kp + k];
+      for (int u = 0; u < 4; ++u) {
+        const int i = (t >> 4) + 16 * u;
+        const bool okb = R0 + i < d;
+        f32x4 oa, ob, op, oq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = c4 + e;
+          oa[e] = k <= i ? va[u][e] : vt[u][e];
+          ob[e] = okb ? vb[u][e] : 0.f;
+          op[e] = upd ? vp[u][e] : 0.f;
+          oq[e] = (upd && okb) ? vq[u][e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(AS + i * PS + c4) = oa;
+        *reinterpret_cast<f32x4*>(BS + i * PS + c4) = ob;
+        *reinterpret_cast<f32x4*>(PP + i * PS + c4) = op;
+        *reinterpret_cast<f32x4*>(QQ + i * PS + c4) = oq;
       }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int idx = t + 256 * u, i = idx >> 6, k = idx & 63;
-        AS[i * LS + k] = (i < kb && k <= i) ? va[u] : (i == k ? 1.f : 0.f);
-        BS[i * LS + k] = (R0 + i < d && k < kb) ? vb[u] : 0.f;
-        if (upd) XS[i * LS + k] = i < kb ? vp[u] : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-  // The diagonal block's pre-update, AS −= P·Pᵀ (P = XS, the previous
-  // panel's values in this panel's rows), in 16x16 tiles (rb, s): rows
-  // 16rb.., columns 16s.., rb >= s (v_mfma_f32_16x16x4f32, A: (row lane%16,
-  // k lane/16), B: (k lane/16, column lane%16), C: rows 4·(lane/16) + v,
-  // column lane%16).  Column slab 0 is shared out over the four waves so
-  // wave 0 can start its steps after one barrier; every later wave updates
-  // its own slab afterwards, in the time it waits for the earlier waves'
-  // steps.  (What the steps publish overwrites AS and XS from their start,
-  // slab 0's rows; the later slabs lie beyond every row published before
-  // their wave has read them.)  The rows' pre-update (E) waits for wave 0's
-  // idle time after its own steps, as only the L21 strips need it.
-  auto pre_tile = [&](int rb, int sl) {
-    const int m = lane & 15, kq = lane >> 4;
-    // all 32 operands first: left to itself the compiler waits for each
-    // pair of reads before its two MFMAs (eight LDS round trips a tile)
-    float av[NB / 4], bv[NB / 4];
-#pragma unroll
-    for (int k = 0; k < NB / 4; ++k) {
-      av[k] = XS[(16 * rb + m) * LS + 4 * k + kq];
-      bv[k] = XS[(16 * sl + m) * LS + 4 * k + kq];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < NB / 4; ++k)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], acc, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) AS[(16 * rb + 4 * kq + v) * LS + 16 * sl + m] -= acc[v];
-  };
-  if (upd) pre_tile(w, 0);
-  // flags: steps 0..63; at NB "E applied"; at NB+1, NB+2 "slab 1's tile in
-  // row block 2 (3) done"
-  if (t <= NB + 2) flag[t] = 0;
-  __syncthreads();
-  int bad_j = -1;
-  // after one expired wait a wave stops waiting; status[1] then flags the
-  // whole call, whose outputs are undefined
-  bool stalled = false;
-  if (upd && w > 0) {
-    // wave 1 is the first to need its slab and must keep up with wave 0's
-    // steps, so waves 2 and 3 take slab 1's tiles in their row blocks first
-    // and release them with a flag each; then every wave updates its own slab
-    if (w >= 2) {
-      pre_tile(w, 1);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __hip_atomic_store(&flag[NB + w - 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      for (int rb = w; rb < 4; ++rb) pre_tile(rb, w);
     } else {
-      pre_tile(1, 1);
-      for (int f = NB + 1; f <= NB + 2; ++f) {
-        int spin = 0;
-        while (!stalled &&
-               __hip_atomic_load(&flag[f], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-          if (++spin > p.spin_limit) stalled = true;
-          __builtin_amdgcn_s_sleep(1);
+      // ragged or unaligned panels (rare): four batches of four elements per
+      // array keep the registers of this path below the float4 path's
+      for (int u0 = 0; u0 < 16; u0 += 4) {
+        float va[4], vb[4], vp[4], vq[4];
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          const int idx = t + 256 * (u0 + uu), i = idx >> 6, k = idx & 63;
+          const bool in = i < kb && k < kb, tr = k > i && (k >> 4) == (i >> 4);
+          const bool oka = in && (k <= i || tr);
+          const int ai = k <= i ? i : k, ak = k <= i ? k : i;
+          va[uu] = G[(int64_t)(k0 + (oka ? ai : 0)) * ld + k0 + (oka ? ak : 0)];
+          const bool okb = R0 + i < d && k < kb;
+          vb[uu] = G[(okb ? R0 + i : 0) * ld + (okb ? k0 + k : 0)];
+          const bool okp = upd && i < kb, okq = upd && R0 + i < d;
+          vp[uu] = G[(int64_t)(okp ? k0 + i : 0) * ld + (okp ? kp + k : 0)];
+          vq[uu] = G[(okq ? R0 + i : 0) * ld + (okq ? kp + k : 0)];
+        }
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          const int idx = t + 256 * (u0 + uu), i = idx >> 6, k = idx & 63;
+          const bool in = i < kb && k < kb, tr = k > i && (k >> 4) == (i >> 4);
+          AS[i * PS + k] = in ? ((k <= i || tr) ? va[uu] : 0.f) : (i == k ? 1.f : 0.f);
+          BS[i * PS + k] = (R0 + i < d && k < kb) ? vb[uu] : 0.f;
+          PP[i * PS + k] = (upd && i < kb) ? vp[uu] : 0.f;
+          QQ[i * PS + k] = (upd && R0 + i < d) ? vq[uu] : 0.f;
         }
       }
     }
   }
-  float a[16], r[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    a[q] = AS[lane * LS + 16 * w + q];
-    r[q] = (16 * w + q == lane) ? 1.f : 0.f;
-  }
+  if (t < 16) fl[t] = 0;
+  __syncthreads();
 
-  // consume the steps of the waves before this one, four at a time: one
-  // wait on the fourth step's flag covers all four (one wave publishes them
-  // in order, each flag a release of the writes before it); the last four
-  // stay pending (pl, px, pc) and meet each column just before its pivot
-  float pl[4], px[4];
-  f32x4 pc[4][4];
-  auto read_batch = [&](int j0) {
+  PanelCtx c{AS, BS, PP, QQ, fl, G, p.Linv, d, ld, R0, k0, kb, lane & 15, lane >> 4,
+             p.spin_limit, upd, R0 < d, false};
+  const int l16 = c.l16, kq = c.kq;
+  const bool xduty = b == 0;
+  float xr[4];    // wave 0: X of the slab it factored last
+  int bad_j = -1;
+  // slab 0: wave 0 applies the previous panel to A_00 and factors it; the
+  // other waves apply it to the rest of A and to B's first column tile
+  if (w == 0) {
+    f32x4 acc = ld_t(tile(AS, 0, 0), l16, kq);
+    if (upd) acc = mm_rs<64>(PP, PP, acc, -1.f, l16, kq);
+    factor16(acc, xr, l16, kq, bad_j);
+    st_t(tile(AS, 0, 0), l16, kq, f32x4{xr[0], xr[1], xr[2], xr[3]});
+  } else if (upd) {
+    pre_tasks(c, w - 1);
+  }
+  __syncthreads();
+  phase<1>(c, w, xr, bad_j, xduty);
+  phase<2>(c, w, xr, bad_j, xduty);
+  phase<3>(c, w, xr, bad_j, xduty);
+
+  // slab 3's L21 tiles (one per wave); workgroup 0: X's last row block
+  // (waves 1-3) and the rest of X (wave 0) to Linv
+  if (c.rows) store_l21(c, mm_rs<16>(tile(BS, w, 3), tile(AS, 3, 3), f32x4{0.f, 0.f, 0.f, 0.f}, 1.f, l16, kq), w, 3);
+  if (xduty) {
+    if (w > 0) {
+      const int j = w - 1;
+      store_x(c, x_tile(c, 3, j, tile(PP, 2, j)), 3, j);
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pl[u] = PL[(j0 + u) * NB + lane];
-      px[u] = PX[(j0 + u) * PXS + lane];
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        pc[u][h] = *reinterpret_cast<const f32x4*>(PL + (j0 + u) * NB + 16 * w + 4 * h);
-    }
-  };
-  for (int j0 = 0; j0 < 16 * w; j0 += 4) {
-    // first look: the flag and the batch are read together, without a wait
-    // between them (this wave's LDS reads complete in order, so a flag
-    // found set vouches for the reads issued after it); only a flag not yet
-    // set is waited for and the batch read again
-    const int f = __hip_atomic_load(&flag[j0 + 3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    read_batch(j0);
-    if (f == 0) {
-      int spin = 0;
-      while (!stalled &&
-             __hip_atomic_load(&flag[j0 + 3], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-        if (++spin > p.spin_limit) stalled = true;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      read_batch(j0);
-    }
-    if (j0 + 4 < 16 * w) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const float c = pc[u][q >> 2][q & 3];
-          a[q] = fmaf(-pl[u], c, a[q]);
-          r[q] = fmaf(-c, px[u], r[q]);
-        }
+      for (int i = 0; i < 4; ++i) store_x(c, ld_t(tile(AS, i, i), l16, kq), i, i);
+      store_x(c, ld_t(tile(PP, 0, 0), l16, kq), 1, 0);
+      store_x(c, ld_t(tile(PP, 1, 0), l16, kq), 2, 0);
+      store_x(c, ld_t(tile(PP, 1, 1), l16, kq), 2, 1);
     }
   }
-  // own steps.  The next pivot is computed from two values read before
-  // this step's update, s_a = a[j+1][j] and s_1 = a[j+1][j+1] (every earlier
-  // step applied): l[j+1][j] = s_a·inv and the new pivot is fma(−l, l, s_1),
-  // the same operations on the same values as lane j+1's own update below,
-  // so the value is identical and the serial chain per step is rsq, mul, fma.
-  // The steps are instantiated with and without a pending batch, so the
-  // unrolled steps carry no branch and the scheduler can move each step's
-  // pivot chain ahead of the previous step's remaining updates.
-  auto own_steps = [&](auto pend) {
-    constexpr bool P = decltype(pend)::value;
-    float piv = 0.f;
-#pragma unroll
-    for (int q0 = 0; q0 < 16; ++q0) {
-      const int j = 16 * w + q0;
-      // the pending last batch meets column 0 here and column q0 + 1 below,
-      // so every column sees it exactly once, before its pivot
-      if (q0 == 0) {
-        if (P) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float c = pc[u][q0 >> 2][q0 & 3];
-            a[q0] = fmaf(-pl[u], c, a[q0]);
-            r[q0] = fmaf(-c, px[u], r[q0]);
-          }
-        }
-        piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j));
-      }
-      if (q0 + 1 < 16 && P) {   // the next column, before its pivot entry is read
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float c = pc[u][(q0 + 1) >> 2][(q0 + 1) & 3];
-          a[q0 + 1] = fmaf(-pl[u], c, a[q0 + 1]);
-          r[q0 + 1] = fmaf(-c, px[u], r[q0 + 1]);
-        }
-      }
-      const bool bad = !(piv > 0.f) || !(piv < INFINITY);
-      bad_j = (bad && bad_j < 0) ? j : bad_j;
-      // one hardware reciprocal square root on the serial chain (about 1 ulp)
-      const float inv = bad ? 1.f : __builtin_amdgcn_rsqf(piv);
-      const float l = lane > j ? a[q0] * inv : 0.f;
-      const float x = r[q0] * inv;
-      r[q0] = x;
-      if (q0 + 1 < 16) {   // the next column feeds the next pivot
-        const float sa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0]), j + 1));
-        const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[q0 + 1]), j + 1));
-        const float c = sa * inv;   // = l at lane j + 1
-        piv = fmaf(-c, c, s1);
-        a[q0 + 1] = fmaf(-l, c, a[q0 + 1]);
-        r[q0 + 1] = fmaf(-c, x, r[q0 + 1]);
-      }
-      PL[j * NB + lane] = l;
-      PX[j * PXS + lane] = x;
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __hip_atomic_store(&flag[j], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-      for (int q = q0 + 2; q < 16; ++q) {
-        const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 16 * w + q));
-        a[q] = fmaf(-l, c, a[q]);
-        r[q] = fmaf(-c, x, r[q]);
-      }
-    }
-  };
-  if (w > 0) own_steps(std::true_type{});
-  else own_steps(std::false_type{});
-  const bool rows = R0 < d;
-  if (upd && rows) {
-    if (w == 0) {
-      rows_preupdate(G, d, ld, R0, k0, kb, kp, BS, lane);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __hip_atomic_store(&flag[NB], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else if (w < 3) {
-      int spin = 0;
-      while (!stalled &&
-             __hip_atomic_load(&flag[NB], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-        if (++spin > p.spin_limit) stalled = true;
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-  }
-  if (b == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, p.piv_base + k0 + bad_j);
-  if (lane == 0 && stalled) atomicOr(p.status + 1, 1);
-  if (rows && w < 3) strip(BS, PX, G, d, ld, R0, k0, kb, w, 0, 4, lane);
-  __syncthreads();   // the last strip's X rows (published by wave 3) are visible
-  if (rows) strip(BS, PX, G, d, ld, R0, k0, kb, 3, w, w + 1, lane);
-  // X = L11⁻¹ to Linv's diagonal block, its rows spread over the panel's
-  // workgroups and waves (row j by workgroup j % np)
-  for (int jr = b + p.np * w; jr < kb; jr += 4 * p.np)
-    if (lane < kb) p.Linv[(int64_t)(k0 + jr) * ld + k0 + lane] = PX[jr * PXS + lane];
+  if (b == 0 && w == 0 && lane == 0 && bad_j >= 0) atomicMin(p.status, p.piv_base + k0 + bad_j);
+  if (lane == 0 && c.stalled) atomicOr(p.status + 1, 1);
 }
 
 // Lower-triangular tile enumeration: L -> (row by, column bx <= by).
@@ -703,7 +873,8 @@ struct TileJob {
   int dma;   // the shapes suit the DMA tile
 };
 // Far tasks: 128x128 tiles of G −= Lₛ·Lₛᵀ for super-panels s, one packed
-// (row tile, column tile, super-panel) word per workgroup.
+// (row tile, column tile, super-panel) word per task, four workgroups (the
+// tile's 64x64 quarters) per task.
 constexpr int kMaxFar = 512;
 struct FarJob {
   gemm_detail::KArgs g;   // A = B = C = G, K = 128; A and B move to super-panel s
@@ -715,14 +886,30 @@ constexpr int kRing128 = 4;
 static_assert(gemm_detail::DTile<64, kRing64>::SMEM <= gemm_detail::GEMM_SMEM_FLOATS * 4, "");
 static_assert(gemm_detail::DTile<128, kRing128>::SMEM <= gemm_detail::GEMM_SMEM_FLOATS * 4, "");
 
+// LDS of a Cholesky launch: the panel or one update tile.  Below half of
+// the CU's 160 KB, so two workgroups of a launch can share a CU (the
+// register count allows two waves per SIMD).  Without the DMA path a
+// 128-tile runs as four 64-tiles, whose operand buffers are smaller.
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kCholSmemFloats =
+    cmax(cmax(4 * PBLK + 16, 4 * gemm_detail::Tile<64>::OPF),
+         cmax(gemm_detail::DTile<64, kRing64>::SMEM, gemm_detail::DTile<128, kRing128>::SMEM) / 4);
+static_assert(kCholSmemFloats * 4 <= 72 * 1024, "a Cholesky launch's LDS must allow two workgroups per CU");
+
 template <int T>
 __device__ __forceinline__ void job_tile(const gemm_detail::KArgs& g, bool dma, int bx, int by,
                                          float* smem) {
   constexpr int NS = T == 64 ? kRing64 : kRing128;
-  if (dma)
+  if (dma) {
     gemm_detail::gemm_tile_dma<T, NS, false, true>(g, bx, by, 0, 1, reinterpret_cast<char*>(smem));
-  else
-    gemm_detail::gemm_tile<T, false, true>(g, bx, by, 0, 1, smem);
+  } else if constexpr (T == 64) {
+    gemm_detail::gemm_tile<64, false, true>(g, bx, by, 0, 1, smem);
+  } else {
+    for (int q = 0; q < 4; ++q) {
+      if (q > 0) __syncthreads();
+      gemm_detail::gemm_tile<64, false, true>(g, 2 * bx + (q & 1), 2 * by + (q >> 1), 0, 1, smem);
+    }
+  }
 }
 
 __device__ __forceinline__ void run_near_tile(const TileJob& j, int idx, float* smem) {
@@ -732,27 +919,32 @@ __device__ __forceinline__ void run_near_tile(const TileJob& j, int idx, float* 
   else job_tile<128>(j.g, j.dma, bx, bx + idx, smem);
 }
 
-__device__ __forceinline__ void run_far_tile(const FarJob& f, int idx, float* smem) {
+// One 64x64 quarter (sub: row half sub >> 1, column half sub & 1) of far
+// task idx; a diagonal task's quarter above the diagonal has nothing to do.
+__device__ __forceinline__ void run_far_tile(const FarJob& f, int idx, int sub, float* smem) {
   const uint32_t w = f.task[idx];   // chol_sched::far_word layout
   const int r = (int)(w & 1023u), t = (int)((w >> 10) & 1023u), sp = (int)((w >> 20) & 1023u);
+  const int by = 2 * r + (sub >> 1), bx = 2 * t + (sub & 1);
+  if (bx > by) return;
   gemm_detail::KArgs g = f.g;
   g.A += (int64_t)sp * chol_sched::kSW;
   g.B += (int64_t)sp * chol_sched::kSW;
-  job_tile<128>(g, f.dma, t, r, smem);
+  job_tile<64>(g, f.dma, bx, by, smem);
 }
 
 // One step of the blocked Cholesky: workgroups [0, nP) run panel k (its
 // columns first receive the previous panel's update), the rest run the
-// near job's tiles and then the far tasks listed for this launch.  The
+// near job's tiles and then the far tasks listed for this launch (four
+// workgroups each).  The
 // schedule guarantees that they all write disjoint parts of G and read
 // only finished panels.  A launch with nP = 0 runs far tasks only.
 __global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP, TileJob nj,
                                                         FarJob fj) {
-  __shared__ __attribute__((aligned(1024))) float smem[gemm_detail::GEMM_SMEM_FLOATS];
+  __shared__ __attribute__((aligned(1024))) float smem[kCholSmemFloats];
   const int L = blockIdx.x;
   if (L < nP) panel_body(p, L, smem);
   else if (L < nP + nj.count) run_near_tile(nj, L - nP, smem);
-  else run_far_tile(fj, L - nP - nj.count, smem);
+  else run_far_tile(fj, (L - nP - nj.count) >> 2, (L - nP - nj.count) & 3, smem);
 }
 
 // U[a][b] = Linv[d-1-a][d-1-b] for b >= a, 0 below the diagonal; four
@@ -1222,13 +1414,13 @@ hipError_t prepare_launch(float* H, int64_t d, float percdamp, int act_order, fl
     while (ft.size() - done > (size_t)kMaxFar) {
       fj.count = kMaxFar;
       std::copy(ft.begin() + (ptrdiff_t)done, ft.begin() + (ptrdiff_t)(done + kMaxFar), fj.task);
-      chol_step_kernel<<<(unsigned)kMaxFar, 256, 0, s>>>(pa, 0, TileJob{}, fj);
+      chol_step_kernel<<<(unsigned)(4 * kMaxFar), 256, 0, s>>>(pa, 0, TileJob{}, fj);
       GQ_CHECK();
       done += kMaxFar;
     }
     fj.count = (int)(ft.size() - done);
     std::copy(ft.begin() + (ptrdiff_t)done, ft.end(), fj.task);
-    chol_step_kernel<<<(unsigned)(nP + nj.count + fj.count), 256, 0, s>>>(pa, nP, nj, fj);
+    chol_step_kernel<<<(unsigned)(nP + nj.count + 4 * fj.count), 256, 0, s>>>(pa, nP, nj, fj);
     GQ_CHECK();
   }
   lead_restore_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * NB, 256), 1024), 256, 0, s>>>(
