@@ -68,10 +68,10 @@ def cpu_model() -> str:
 # plain copy of known size (`bench.py --copy-calibration 512`).  Valid only
 # for the Hessian source they were taken on: any change to it reports null.
 HESSIAN_TRAFFIC = {
-    "source_sha256": "bb2d706c5dc5e41c9dfeabc7797e6e3f7d33429349b503d30d11c27ba52a6561",
+    "source_sha256": "b1a5a5dea67eb5d206e9bb49d7b79dca2689516c06a93a343982f353bb7f62fe",
     # zero_chunk + shift_mean + syrk256 + reduce_mirror kernels, KiB per call
-    "fetch_kib": 1.1 + 16411.3 + 2143930.1 + 134918.5, "fetch_scale": 524288 / 262159.2,
-    "write_kib": 0.2 + 8.0 + 236544.0 + 65756.4, "write_scale": 524288 / 524288.0,
+    "fetch_kib": 1.1 + 16418.3 + 2619604.8 + 143627.6, "fetch_scale": 524288 / 262159.4,
+    "write_kib": 0.2 + 8.0 + 253952.0 + 65748.5, "write_scale": 524288 / 524288.0,
 }
 
 
