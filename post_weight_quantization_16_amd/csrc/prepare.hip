@@ -872,9 +872,9 @@ struct TileJob {
   int count, nby, tile;
   int dma;   // the shapes suit the DMA tile
 };
-// Far tasks: 128x128 tiles of G −= Lₛ·Lₛᵀ for super-panels s, one packed
-// (row tile, column tile, super-panel) word per task, four workgroups (the
-// tile's 64x64 quarters) per task.
+// Far tasks: 128x128 tiles of G −= Lₛ·Lₛᵀ for one super-panel s or a pair
+// s, s+1 (K = 128 or 256), one packed (row tile, column tile, super-panel,
+// pair) word per task, four workgroups (the tile's 64x64 quarters) per task.
 constexpr int kMaxFar = 512;
 struct FarJob {
   gemm_detail::KArgs g;   // A = B = C = G, K = 128; A and B move to super-panel s
@@ -922,13 +922,14 @@ __device__ __forceinline__ void run_near_tile(const TileJob& j, int idx, float* 
 // One 64x64 quarter (sub: row half sub >> 1, column half sub & 1) of far
 // task idx; a diagonal task's quarter above the diagonal has nothing to do.
 __device__ __forceinline__ void run_far_tile(const FarJob& f, int idx, int sub, float* smem) {
-  const uint32_t w = f.task[idx];   // chol_sched::far_word layout
-  const int r = (int)(w & 1023u), t = (int)((w >> 10) & 1023u), sp = (int)((w >> 20) & 1023u);
+  int r, t, sp, ns;
+  chol_sched::far_unpack(f.task[idx], r, t, sp, ns);
   const int by = 2 * r + (sub >> 1), bx = 2 * t + (sub & 1);
   if (bx > by) return;
   gemm_detail::KArgs g = f.g;
   g.A += (int64_t)sp * chol_sched::kSW;
   g.B += (int64_t)sp * chol_sched::kSW;
+  g.K = g.k_last = ns * chol_sched::kSW;   // one or two super-panels
   job_tile<64>(g, f.dma, bx, by, smem);
 }
 
@@ -1001,7 +1002,7 @@ TileJob near_job(float* G, int64_t d, int64_t ld, int64_t k) {
 
 FarJob far_base(float* G, int64_t d, int64_t ld) {
   FarJob f;
-  GemmArgs h{};  // tile (r, t): G[128r:, 128t:] −= G[128r:, 128s:+128] · G[128t:, 128s:+128]ᵀ
+  GemmArgs h{};  // tile (r, t): G[128r:, 128t:] −= G[128r:, 128s:+K] · G[128t:, 128s:+K]ᵀ
   h.M = (int)d; h.N = (int)d; h.K = chol_sched::kSW; h.k_last = chol_sched::kSW; h.batch = 1;
   h.alpha = -1.f; h.beta = 1.f;
   h.A = G; h.lda = ld; h.trans_a = false;

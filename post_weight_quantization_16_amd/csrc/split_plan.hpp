@@ -22,10 +22,12 @@
 
 #include <cstdint>
 
+#ifndef GQ_HD
 #if defined(__HIPCC__)
 #define GQ_HD __host__ __device__ __forceinline__
 #else
 #define GQ_HD inline
+#endif
 #endif
 
 namespace gq {

@@ -23,7 +23,7 @@ static int check(long d) {
   auto G = [&](long i, long j, long p) -> unsigned char& { return got[(size_t)((i * nb + j) * nb + p)]; };
   const auto far = far_schedule(d);
   if ((long)far.size() != nb) return fail(d, "schedule length", -1, -1, -1, -1);
-  long nfar = 0, peak = 0;
+  long nfar = 0, peak = 0, nupd = 0, cost = 0, peak_cost = 0;
   for (long k = 0; k < nb; ++k) {
     std::vector<signed char> wr((size_t)(nb * nb), 0);   // writer of each block in this launch
     auto write = [&](long i, long j, int who) -> bool {
@@ -58,31 +58,36 @@ static int check(long d) {
         }
       }
     }
-    long cnt = 0;
+    long cnt = 0, kcost = 0;
     for (uint32_t w : far[(size_t)k]) {
-      int r, t, s;
-      far_unpack(w, r, t, s);
+      int r, t, s, ns;
+      far_unpack(w, r, t, s, ns);
       ++cnt;
-      if (r < t || 2L * s + 1 >= k) return fail(d, "far task reads an unfinished panel", k, r, t, s);
+      nupd += ns;
+      kcost += ns == 2 ? 3 : 2;   // half single-task units (a pair costs 1.5)
+      if (r < t || 2L * (s + ns - 1) + 1 >= k) return fail(d, "far task reads an unfinished panel", k, r, t, s);
       for (long i = 2L * r; i < 2L * r + 2 && i < nb; ++i)
         for (long j = 2L * t; j < 2L * t + 2 && j < nb; ++j) {
           if (j > i) continue;
           if (j <= k) return fail(d, "far task writes the panel or left of it", k, i, j, s);
           if (!write(i, j, (int)(3 + (cnt % 100)))) return fail(d, "far write overlap", k, i, j, s);
-          for (long p = 2L * s; p < 2L * s + 2; ++p) {
+          for (long p = 2L * s; p < 2L * (s + ns); ++p) {
             if (G(i, j, p)) return fail(d, "far update twice", k, i, j, p);
             G(i, j, p) = 1;
           }
         }
     }
     nfar += cnt;
+    cost += kcost;
     peak = cnt > peak ? cnt : peak;
+    peak_cost = kcost > peak_cost ? kcost : peak_cost;
   }
   for (long j = 0; j < nb; ++j)
     for (long i = j; i < nb; ++i)
       for (long p = 0; p < j; ++p)
         if (G(i, j, p) != 1) return fail(d, "update missing at the end", nb, i, j, p);
-  std::printf("ok d=%ld launches=%ld far_tasks=%ld peak_per_launch=%ld\n", d, nb, nfar, peak);
+  std::printf("ok d=%ld launches=%ld far_tasks=%ld far_updates=%ld peak_per_launch=%ld cost=%ld peak_cost=%ld\n",
+              d, nb, nfar, nupd, peak, cost, peak_cost);
   return 0;
 }
 
