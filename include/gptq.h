@@ -281,7 +281,9 @@ int gptq_export(int bits, int64_t d_out, int64_t d_in, int64_t n_groups, const u
  *             run); with NULL they run unsplit.  A non-NULL ws smaller than
  *             that size returns GPTQ_ERR_WORKSPACE.
  * M <= 4 runs a GEMV bound by the weights' HBM traffic; larger M an MFMA
- * product.  Asynchronous; argument errors only. */
+ * product.  The weight words and A (from its first element to row M-1's
+ * K-th value) must each stay under 4 GiB (GPTQ_ERR_UNSUPPORTED otherwise).
+ * Asynchronous; argument errors only. */
 int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t lda,
                     const uint32_t* qweight, int bits, const uint16_t* scales_f16,
                     const uint16_t* zeros_f16, const int32_t* g_idx, int group_size,

@@ -304,6 +304,8 @@ int gptq_w4a16_gemm(const void* A, int a_dtype, int64_t M, int64_t K, int64_t ld
   if (M <= 0 || K <= 0 || N <= 0 || K > kMaxDin || N > kMaxDout || M > kMaxDout)
     return fail(GPTQ_ERR_INVALID_ARG, "M, K and N must be positive (K <= %lld)", (long long)kMaxDin);
   if (lda < K || ldc < N) return fail(GPTQ_ERR_INVALID_ARG, "lda < K or ldc < N");
+  if (N * ceil_div64(K * bits, 32) * 4 >= ((int64_t)1 << 32) || ((M - 1) * lda + K) * 2 >= ((int64_t)1 << 32))
+    return fail(GPTQ_ERR_UNSUPPORTED, "the weight words and A must each stay under 4 GiB");
   const int64_t g = (group_size <= 0 || group_size >= K) ? K : group_size;
   if (!g_idx && g % 32 != 0 && g != K)
     return fail(GPTQ_ERR_UNSUPPORTED, "group_size must be a multiple of 32 (or -1)");

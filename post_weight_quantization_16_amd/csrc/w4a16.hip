@@ -29,14 +29,13 @@
 //                row sets as one stream with the words of the next two items
 //                in flight; dot products with v_dot2_f32_{f16,bf16} on packed
 //                pairs, reduced across the wave at the end of each row set.
-//   gemm_kernel  (M > 4): 64x64 output tiles, K in steps of 128 staged in
-//                LDS as packed pairs (the W tile dequantized by all 256
-//                threads, one 32-code chunk each), v_mfma_f32_32x32x16_{f16,
-//                bf16}, the next two steps' global reads in flight during the
-//                current one.  Few tiles (small M·N) split K over blockIdx.z
-//                into fp32 partials in the caller's workspace, summed in split
-//                order by reduce_kernel, so the result does not depend on
-//                timing.
+//   gemm_kernel  (M > 4): (32·MT) x 128 output tiles, each lane dequantizing
+//                the codes of its own MFMA B operands into registers (every
+//                weight once per row tile), A staged in LDS per step of 64,
+//                v_mfma_f32_32x32x16_{f16,bf16}, the next three steps' codes
+//                and A values in flight.  Few tiles split K over blockIdx.z into fp32
+//                partials in the caller's workspace, summed in split order by
+//                reduce_kernel, so the result does not depend on timing.
 #include <utility>
 
 #include "common.hpp"
@@ -56,7 +55,16 @@ struct WArgs {
   int64_t N; float* C; int64_t ldc;
   float* P; int64_t kper;   // split-K partials [splits x M x N] (null: no split) and K per split
   uint64_t cpg_magic;       // ceil(2^32 / chunks per group), up to 2^32
+  uint32_t q_bytes;         // bytes of the weight words (< 2^32)
+  uint32_t a_bytes;         // bytes of A from its first element to the last row's K-th value
 };
+// Buffer resources (byte-addressed, stride 0): reads past num_records return
+// 0 without a branch, so the loads of the kernels' loops are straight-line
+// and the compiler can keep every prefetch in flight (divergent load paths
+// make it wait for all outstanding loads where they join).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
 // group of chunk c: c / (chunks per group) as a multiply-high, exact for
 // c < 2^11 (K <= 65536) and at most 2^20 chunks per group
 __device__ __forceinline__ int chunk_group(const WArgs& a, int c) {
@@ -82,17 +90,27 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            c, false);
 }
 
-// The BITS words of chunk c of a row (words beyond the row's end read as 0).
+// The BITS words of chunk c of row n (words past the row's end belong to
+// the next row, or read 0 past the buffer: they only ever pair with zero
+// activations).
 template <int BITS>
-__device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ row, int64_t row_words,
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int64_t row_words, int64_t n,
                                            int64_t c, uint32_t (&w)[BITS]) {
-  const int64_t w0 = c * BITS;
-  if (w0 + BITS <= row_words) {
-    // one vector load (dwordx2/x3/x4; global loads need 4-byte alignment only)
-    __builtin_memcpy(w, row + w0, sizeof(w));
+  const uint32_t off = (uint32_t)((n * row_words + c * BITS) * 4);
+  if constexpr (BITS == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (BITS == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else if constexpr (BITS == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) w[i] = w0 + i < row_words ? row[w0 + i] : 0u;
+    for (int i = 0; i < 4; ++i) { w[i] = v[i]; w[4 + i] = u[i]; }
   }
 }
 // code J of a chunk (J a compile-time constant: shifts and masks only)
@@ -152,9 +170,19 @@ __device__ __forceinline__ u32x4 pair_j_j4(u32x4 v) {
                (v[1] & 0xFFFFu) | (v[3] << 16), (v[1] >> 16) | (v[3] & 0xFFFF0000u)};
 }
 
+// Workgroup barrier for LDS data only: the LDS writes before it are visible
+// after it, and global loads in flight stay in flight (__syncthreads() would
+// also wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- GEMV
 constexpr int kGemvLds = 64 * 1024;   // bytes of A staged per workgroup
 constexpr int RW = 2;                 // weight rows per wave pass
+constexpr int GPD = 3;                // ring slots (items loaded GPD−1 ahead)
 
 template <int BITS>
 struct Fetch {
@@ -184,16 +212,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
   const int64_t Kp = (a.K + 31) / 32 * 32;   // A rows padded to whole chunks (zeros)
   const int64_t KW = Kp / 2;
   const int64_t nch = Kp / 32;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (t >> 6), nwaves = (int64_t)gridDim.x * 4;
+  // the wave index as a scalar: the item loop below is uniform per wave
+  const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q, a.q_bytes);
+  // rows past N and chunks past the row are fetched from the last row and
+  // chunk (in bounds, never used), so every fetch is the same straight-line
+  // code
   auto fetch = [&](int64_t n0, int64_t c, Fetch<BITS>& f) {
+    const int64_t cc = c < nch ? c : nch - 1;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int64_t n = n0 + r < a.N ? n0 + r : a.N - 1;   // rows past N: never stored
-      load_chunk<BITS>(a.q + n * a.row_words, a.row_words, c, f.w[r]);
+      load_chunk<BITS>(qrs, a.row_words, n, cc, f.w[r]);
       f.s[r] = 0;
       f.z[r] = 0;
       if (!GIDX) {
-        const int64_t gi = chunk_group(a, (int)c);
+        const int64_t gi = chunk_group(a, (int)cc);
         f.s[r] = a.s16[n * a.ng + gi];
         f.z[r] = a.z16[n * a.ng + gi];
       }
@@ -203,39 +238,70 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
   // (rows n0 = (wave + set·nwaves)·RW .., chunk c = lane + 64j); every lane
   // runs the same items (slots past the row's chunks add nothing), so the
   // wave reduction at each row set's last slot is uniform.  The words of the
-  // next two items are always in flight, across row sets too; the first two
-  // are issued before A is staged.  Item positions advance by additions.
+  // items are loaded into a ring of GPD slots, GPD−1 items ahead, across row
+  // sets too; the first ones are issued before A is staged.  Item positions
+  // advance by additions.
   const int cps = (int)((nch + 63) / 64);
   const int64_t set_stride = nwaves * RW;
+  const int64_t nsets = (a.N + RW - 1) / RW;
+  const int64_t items = wave < nsets ? ((nsets - 1 - wave) / nwaves + 1) * cps : 0;
   int64_t f_n0 = wave * RW;   // the next item to fetch
   int f_j = 0;
   auto fetch_next = [&](Fetch<BITS>& f) {
-    const int c = lane + 64 * f_j;
-    if (f_n0 < a.N && c < nch) fetch(f_n0, c, f);
+    fetch(f_n0 < a.N ? f_n0 : a.N - 1, lane + 64 * f_j, f);
     if (++f_j == cps) { f_j = 0; f_n0 += set_stride; }
   };
-  Fetch<BITS> cur, nxt;
-  fetch_next(cur);
-  fetch_next(nxt);
-  for (int64_t e = t; e < MM * Kp / 8; e += 256) {   // 8 values (16 bytes) per item
-    const int64_t m = e / (Kp / 8), k = (e % (Kp / 8)) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (m < a.M) {
-      const uint16_t* src = a.A + m * a.lda + k;
-      if (a.vec_a && k + 8 <= a.K) {
-        v = *reinterpret_cast<const u32x4*>(src);
+  // A into LDS, 16 bytes (8 values) per thread and item, four items per
+  // thread at a time, straight-line: rows past M read 0 (past the buffer),
+  // values past K are masked to 0; 4-byte aligned rows load as one dwordx4,
+  // others as eight 16-bit loads.  The first items of the weight stream are
+  // issued behind the first batch of A, so they stay in flight while it is
+  // written.
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A, a.a_bytes);
+  const int ipr = (int)(Kp / 8), nitems_a = MM * ipr;   // 16-byte items per row, in all
+  Fetch<BITS> ring[GPD];
+  auto stage_a = [&](int e0, auto first, auto vec) {
+    u32x4 v[4];
+    int ke[4], me[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + t + 256 * i;
+      me[i] = (int)((uint32_t)e / (uint32_t)ipr);
+      ke[i] = (e - me[i] * ipr) * 8;
+      const uint32_t off = e < nitems_a && me[i] < a.M ? (uint32_t)((me[i] * a.lda + ke[i]) * 2) : a.a_bytes;
+      if constexpr (decltype(vec)::value) {
+        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0));
       } else {
-        uint32_t h[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) h[j] = k + j < a.K ? src[j] : 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = h[2 * j] | (h[2 * j + 1] << 16);
+        for (int j = 0; j < 4; ++j)
+          v[i][j] = __builtin_amdgcn_raw_buffer_load_b16(ars, off + 4 * j, 0, 0) |
+                    ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ars, off + 4 * j + 2, 0, 0) << 16);
       }
     }
-    if (PERM) v = pair_j_j4(v);
-    *reinterpret_cast<u32x4*>(Ap + m * KW + k / 2) = v;
-  }
-  __syncthreads();
+    if constexpr (decltype(first)::value) {
+#pragma unroll
+      for (int p = 0; p < GPD - 1; ++p) fetch_next(ring[p]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + t + 256 * i;
+      if (e < nitems_a) {
+        const int64_t left = a.K - ke[i];   // values of this item inside K
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t keep = left >= 2 * j + 2 ? 0xFFFFFFFFu : (left == 2 * j + 1 ? 0xFFFFu : 0u);
+          v[i][j] &= keep;
+        }
+        *reinterpret_cast<u32x4*>(Ap + me[i] * KW + ke[i] / 2) = PERM ? pair_j_j4(v[i]) : v[i];
+      }
+    }
+  };
+  auto stage_all = [&](auto vec) {
+    stage_a(0, std::true_type{}, vec);
+    for (int e0 = 4 * 256; e0 < nitems_a; e0 += 4 * 256) stage_a(e0, std::false_type{}, vec);
+  };
+  if (a.vec_a) stage_all(std::true_type{}); else stage_all(std::false_type{});
+  lds_barrier();
   float acc[RW][MM];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -243,33 +309,35 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
     for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
   int64_t n0 = wave * RW;
   int j = 0;
-  while (n0 < a.N) {
+  auto item = [&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    // the slot of the previous item (already used) takes the item GPD−1 ahead
+    fetch_next(ring[(p + GPD - 1) % GPD]);
     const int c = lane + 64 * j;
-    Fetch<BITS> nx2;
-    fetch_next(nx2);   // two items ahead
-    if (c < nch) {
-      uint32_t ap[MM][16];
+    const bool valid = c < nch;
+    const int ca = valid ? c : (int)nch - 1;
+    uint32_t ap[MM][16];
 #pragma unroll
-      for (int m = 0; m < MM; ++m)
+    for (int m = 0; m < MM; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(Ap + m * KW + c * 16 + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Ap + m * KW + ca * 16 + 4 * q);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ap[m][4 * q + j] = v[j];
-        }
+        for (int i = 0; i < 4; ++i) ap[m][4 * q + i] = v[i];
+      }
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        uint32_t wp[16];
-        const int64_t n = n0 + r < a.N ? n0 + r : a.N - 1;
-        dequant_chunk<F16, BITS, GIDX>(a, cur.w[r], cur.s[r], cur.z[r], n, c, wp);
+    for (int r = 0; r < RW; ++r) {
+      uint32_t wp[16];
+      const int64_t n = n0 + r < a.N ? n0 + r : a.N - 1;
+      dequant_chunk<F16, BITS, GIDX>(a, ring[p].w[r], ring[p].s[r], ring[p].z[r], n, ca, wp);
 #pragma unroll
-        for (int m = 0; m < MM; ++m)
+      for (int m = 0; m < MM; ++m) {
+        float ps = 0.f;
 #pragma unroll
-          for (int p = 0; p < 16; ++p) acc[r][m] = dot2<F16>(ap[m][p], wp[p], acc[r][m]);
+        for (int i = 0; i < 16; ++i) ps = dot2<F16>(ap[m][i], wp[i], ps);
+        acc[r][m] += valid ? ps : 0.f;
       }
     }
-    cur = nxt;
-    nxt = nx2;
     if (j == cps - 1) {   // the row set's last slot: reduce and store
 #pragma unroll
       for (int r = 0; r < RW; ++r)
@@ -282,113 +350,188 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
         }
     }
     if (++j == cps) { j = 0; n0 += set_stride; }
+  };
+  static_assert(GPD == 3, "the loop below is unrolled for GPD = 3");
+  int64_t it = 0;
+  for (; it + GPD <= items; it += GPD) {
+    item(std::integral_constant<int, 0>{});
+    item(std::integral_constant<int, 1>{});
+    item(std::integral_constant<int, 2>{});
   }
+  if (it < items) item(std::integral_constant<int, 0>{});
+  if (it + 1 < items) item(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------- GEMM
-constexpr int TM = 64, TN = 64, TK = 128;
-constexpr int LP = TK / 2 + 4;   // LDS row stride in packed pairs (pad: conflict-free reads)
 
-template <bool F16, int BITS, bool GIDX>
+// A workgroup computes a BM x 128 output tile (BM = 32·MT rows, MT <= 4; four
+// waves of 32 columns each) over its K range in steps of 64.  Each lane
+// dequantizes exactly the codes its own MFMA B operands need, straight into
+// registers: lane (n, h) (n = lane % 32, h = lane / 32) takes the 32-code
+// chunk h of the step for column n, and K-substep s (of four, 16 deep each)
+// reads its pairs 4s..4s+3, so the 64 codes of the step meet the A values
+// in the same permuted K order on both sides (MFMA sums over k in any
+// order).  Every weight is dequantized once per row tile, by one lane.  The
+// A tile (BM x 64 as packed pairs, re-paired like the weights) is staged in
+// LDS, double-buffered, one barrier per step; the codes and A values of the
+// next PD−1 steps are in flight while the current step is dequantized.
+constexpr int TKS = 64;          // K per step
+constexpr int LPA = TKS / 2 + 4; // LDS row stride of A in packed pairs (conflict-free b128 reads)
+constexpr int TNW = 32;          // columns per wave
+constexpr int TN = 4 * TNW;      // columns per workgroup
+constexpr int PD = 4;            // steps in flight (even: the A buffers alternate with the step)
+static_assert(PD % 2 == 0, "");
+
+template <bool F16, int BITS, int MT, bool GIDX, bool VA>
 __global__ __launch_bounds__(256) void gemm_kernel(WArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t As[TM * LP];
-  __shared__ __attribute__((aligned(16))) uint32_t Ws[TN * LP];
+  constexpr int BM = 32 * MT;
+  __shared__ __attribute__((aligned(16))) uint32_t As[2][BM * LPA];
   constexpr bool PERM = kHalfPairs<F16, BITS> && !GIDX;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wm = wv >> 1, wn = wv & 1;   // wave tile: rows 32·wm, columns 32·wn
-  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * TN;
   const int64_t kb = (int64_t)blockIdx.z * a.kper;
   const int64_t ke = kb + a.kper < a.K ? kb + a.kper : a.K;
-  // A loader: row t/4, 32 values at k offset 32·(t%4); W loader: tile row
-  // t%64, chunk t/64 of the step (all 32 codes)
-  const int ar = t >> 2, ak = (t & 3) * 32;
-  const int wr = t & 63, wc = t >> 6;
-  const int64_t am = m0 + ar;
   const int nch = (int)((a.K + 31) / 32);
-  const int64_t wnr = n0 + wr < a.N ? n0 + wr : a.N - 1;   // rows past N: never stored
-  const uint32_t* wrow = a.q + wnr * a.row_words;
+  const int64_t ncol = n0 + wv * TNW + l32;
+  const int64_t wn = ncol < a.N ? ncol : a.N - 1;   // columns past N: never stored
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q, a.q_bytes);
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.A, a.a_bytes);
+  // A loader: unit u = t + 256i (i < MT) is row u / 8, values 8(u % 8) .. +7
+  // of the step; rows past M read 0 (past the buffer); dword loads need
+  // 4-byte aligned rows (VA), else eight 16-bit loads.  The ring holds the
+  // raw loads: nothing touches them until the step's A goes to LDS, so the
+  // loads stay in flight meanwhile.
+  auto load_a = [&](int64_t k0, u32x4 (&av)[MT]) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int u = t + 256 * i, row = u >> 3, q8 = (u & 7) * 8;
+      const int64_t m = m0 + row, k = k0 + q8;
+      const uint32_t off = m < a.M ? (uint32_t)((m * a.lda + k) * 2) : a.a_bytes;
+      if constexpr (VA) {
+        av[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          av[i][j] = __builtin_amdgcn_raw_buffer_load_b16(ars, off + 4 * j, 0, 0) |
+                     ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ars, off + 4 * j + 2, 0, 0) << 16);
+      }
+    }
+  };
+  // values past K are masked to 0 (they would meet codes that do not belong
+  // to the row), then the pairs are re-paired like the weights
+  auto store_a = [&](const u32x4 (&av)[MT], int64_t k0, uint32_t* buf) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int u = t + 256 * i, row = u >> 3, q8 = (u & 7) * 8;
+      const int64_t left = a.K - (k0 + q8);   // values of this group of 8 inside K
+      u32x4 v = av[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t keep = left >= 2 * j + 2 ? 0xFFFFFFFFu : (left == 2 * j + 1 ? 0xFFFFu : 0u);
+        v[j] &= keep;
+      }
+      *reinterpret_cast<u32x4*>(buf + row * LPA + q8 / 2) = PERM ? pair_j_j4(v) : v;
+    }
+  };
   struct Stage {
-    u32x4 av[4];
     uint32_t w[BITS];
     uint16_t s, z;
   };
   auto fetch = [&](int64_t k0, Stage& st) {
-    const int64_t k = k0 + ak;
-    if (am < a.M && a.vec_a && k + 32 <= a.K) {
-      const uint16_t* src = a.A + am * a.lda + k;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) st.av[q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t h[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t kk = k + 8 * q + j;
-          h[j] = (am < a.M && kk < a.K) ? a.A[am * a.lda + kk] : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st.av[q][j] = h[2 * j] | (h[2 * j + 1] << 16);
-      }
-    }
-    const int c = (int)(k0 >> 5) + wc;
-    load_chunk<BITS>(wrow, a.row_words, c, st.w);
+    const int c0 = (int)(k0 >> 5) + h, c = c0 < nch ? c0 : nch - 1;
+    load_chunk<BITS>(qrs, a.row_words, wn, c, st.w);
     st.s = 0;
     st.z = 0;
     if (!GIDX) {
-      const int64_t gi = chunk_group(a, c < nch ? c : nch - 1);
-      st.s = a.s16[wnr * a.ng + gi];
-      st.z = a.z16[wnr * a.ng + gi];
+      const int64_t gi = chunk_group(a, c);
+      st.s = a.s16[wn * a.ng + gi];
+      st.z = a.z16[wn * a.ng + gi];
     }
   };
-  f32x16 acc;
+  f32x16 acc[MT];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  // three stages: the current one and the next two in flight
-  Stage cur, nxt, nx2;
-  if (kb < ke) fetch(kb, cur);
-  if (kb + TK < ke) fetch(kb + TK, nxt);
-  for (int64_t k0 = kb; k0 < ke; k0 += TK) {
-    const bool more = k0 + TK < ke;
-    if (k0 + 2 * TK < ke) fetch(k0 + 2 * TK, nx2);
-    // this step's tiles into LDS: A as loaded; W dequantized (codes past K
-    // pair with zero activations, so their values do not matter)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(As + ar * LP + ak / 2 + 4 * q) = PERM ? pair_j_j4(cur.av[q]) : cur.av[q];
-    uint32_t wp[16];
-    dequant_chunk<F16, BITS, GIDX>(a, cur.w, cur.s, cur.z, wnr, k0 / 32 + wc, wp);
-    uint32_t* wd = Ws + wr * LP + 16 * wc;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  // a ring of PD steps in flight: codes and A values of steps i+1 .. i+PD−1
+  // are loading while step i computes.  The loop is unrolled by PD so every
+  // ring slot is a fixed set of registers, and its body is straight-line:
+  // the refill of a slot is never skipped, it re-reads the last step (from
+  // cache) once no step is left to load.
+  Stage st[PD];
+  u32x4 av[PD][MT];
+  const int64_t nsteps = ke > kb ? (ke - kb + TKS - 1) / TKS : 0;
+  const int64_t klast = kb + (nsteps - 1) * TKS;
+  if (nsteps > 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(wd + 4 * q) = u32x4{wp[4 * q], wp[4 * q + 1], wp[4 * q + 2], wp[4 * q + 3]};
-    __syncthreads();
-    // eight k-steps of 16: lane holds 8 k (one group of 8) of row / column lane % 32
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      const int kk = ks * 8 + (lane >> 5) * 4;   // in pairs
-      const u32x4 av = *reinterpret_cast<const u32x4*>(As + (wm * 32 + (lane & 31)) * LP + kk);
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(Ws + (wn * 32 + (lane & 31)) * LP + kk);
-      if constexpr (F16)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
-                                                     __builtin_bit_cast(f16x8, bv), acc, 0, 0, 0);
-      else
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                      __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+    for (int p = 0; p < PD - 1; ++p) {
+      const int64_t kf = kb + p * TKS < klast ? kb + p * TKS : klast;
+      fetch(kf, st[p]);
+      load_a(kf, av[p]);
     }
-    __syncthreads();
-    if (more) {
-      cur = nxt;
-      nxt = nx2;
-    }
+    store_a(av[0], kb, As[0]);
+    lds_barrier();
   }
+  auto step = [&](auto pc, int64_t i) {
+    constexpr int p = decltype(pc)::value;
+    const int64_t k0 = kb + i * TKS;
+    // the slot of step i−1 (dequantized and its A stored) takes step i+PD−1
+    {
+      constexpr int q = (p + PD - 1) % PD;
+      const int64_t kf = k0 + (PD - 1) * TKS < klast ? k0 + (PD - 1) * TKS : klast;
+      fetch(kf, st[q]);
+      load_a(kf, av[q]);
+    }
+    // step i+1's A into the other buffer (read by no wave since the last
+    // barrier; after the last step nothing reads it)
+    store_a(av[(p + 1) % PD], k0 + TKS, As[(p + 1) & 1]);
+    // this lane's 32 codes of the step (codes past K pair with zero
+    // activations, so their values do not matter)
+    uint32_t wp[16];
+    dequant_chunk<F16, BITS, GIDX>(a, st[p].w, st[p].s, st[p].z, wn, k0 / 32 + h, wp);
+    const uint32_t* ab = As[p & 1];   // step i's buffer (i ≡ p mod PD, PD even)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 bv = {wp[4 * s], wp[4 * s + 1], wp[4 * s + 2], wp[4 * s + 3]};
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        const u32x4 avv = *reinterpret_cast<const u32x4*>(ab + (32 * mi + l32) * LPA + 16 * h + 4 * s);
+        if constexpr (F16)
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, avv), __builtin_bit_cast(f16x8, bv), acc[mi], 0, 0, 0);
+        else
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, avv), __builtin_bit_cast(bf16x8, bv), acc[mi], 0, 0, 0);
+      }
+    }
+    lds_barrier();
+    // keeps the next step's work (masking A values, dequantizing codes) from
+    // being scheduled up into this one, where it would wait for loads that
+    // are meant to stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int64_t i0 = 0;
+  for (; i0 + PD <= nsteps; i0 += PD) {
+    step(std::integral_constant<int, 0>{}, i0);
+    step(std::integral_constant<int, 1>{}, i0 + 1);
+    step(std::integral_constant<int, 2>{}, i0 + 2);
+    step(std::integral_constant<int, 3>{}, i0 + 3);
+  }
+  static_assert(PD == 4, "the loop above and the tail below are unrolled for PD = 4");
+  if (i0 < nsteps) step(std::integral_constant<int, 0>{}, i0);
+  if (i0 + 1 < nsteps) step(std::integral_constant<int, 1>{}, i0 + 1);
+  if (i0 + 2 < nsteps) step(std::integral_constant<int, 2>{}, i0 + 2);
   float* out = a.P ? a.P + (int64_t)blockIdx.z * a.M * a.N : a.C;
   const int64_t ldo = a.P ? a.N : a.ldc;
+  if (ncol < a.N) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t m = m0 + wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-    const int64_t n = n0 + wn * 32 + (lane & 31);
-    if (m < a.M && n < a.N) out[m * ldo + n] = acc[r];
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + 32 * i + (r >> 2) * 8 + h * 4 + (r & 3);
+        if (m < a.M) out[m * ldo + ncol] = acc[i][r];
+      }
   }
 }
 
@@ -404,13 +547,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ P
   }
 }
 
-// K splits for the GEMM: enough (tile, split) workgroups for two per CU
+constexpr int gemm_mt(int64_t M) { return M <= 32 ? 1 : M <= 128 ? 2 : 4; }
+
+// K splits for the GEMM: about 256 (tile, split) workgroups, at most eight
+// splits and at least eight steps of K per split
 int gemm_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ceil_div(M, TM) * ceil_div(N, TN);
-  const int64_t steps = ceil_div(K, TK);
-  int64_t s = std::min<int64_t>(ceil_div(512, tiles), std::min<int64_t>(steps, 16));
+  const int64_t tiles = ceil_div(M, 32 * gemm_mt(M)) * ceil_div(N, TN);
+  const int64_t steps = ceil_div(K, TKS);
+  const int64_t s = std::min<int64_t>(ceil_div(256, tiles), std::min<int64_t>(8, steps / 8));
   if (s < 2) return 1;
-  const int64_t kper = ceil_div(steps, s) * TK;
+  const int64_t kper = ceil_div(steps, s) * TKS;
   return (int)ceil_div(K, kper);
 }
 
@@ -426,11 +572,15 @@ hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_
                         const uint32_t* qweight, int bits, const uint16_t* s16, const uint16_t* z16,
                         const int32_t* g_idx, int64_t g, int64_t ng, int64_t N, float* C,
                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t s) {
-  const int vec_a = ((uintptr_t)A % 16 == 0) && (lda % 8 == 0);
+  const int vec_a = ((uintptr_t)A % 4 == 0) && (lda % 2 == 0);   // dword loads of A
   const uint64_t cpg = g >= K ? (1u << 20) : (uint64_t)(g / 32);   // one group: all in group 0
   const uint64_t magic = ((uint64_t)1 << 32) / cpg + (((uint64_t)1 << 32) % cpg != 0);
-  WArgs a{static_cast<const uint16_t*>(A), M, K, lda, vec_a, qweight, bits, ceil_div(K * bits, 32),
-          s16, z16, ng, g, g_idx, N, C, ldc, nullptr, K, magic};
+  const int64_t row_words = ceil_div(K * bits, 32);
+  const int64_t q_bytes = N * row_words * 4, a_bytes = ((M - 1) * lda + K) * 2;
+  if (q_bytes >= ((int64_t)1 << 32) || a_bytes >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  WArgs a{static_cast<const uint16_t*>(A), M, K, lda, vec_a, qweight, bits, row_words,
+          s16, z16, ng, g, g_idx, N, C, ldc, nullptr, K, magic, (uint32_t)q_bytes, (uint32_t)a_bytes};
+  const bool va = vec_a;
   const bool f16 = a_dtype == GPTQ_F16;
   const bool gx = g_idx != nullptr;
   const int mm = M <= 1 ? 1 : M <= 2 ? 2 : 4;
@@ -466,12 +616,21 @@ hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_
   if (splits > 1 && (!ws || ws_bytes < w4a16_ws_bytes(M, N, K))) splits = 1;
   if (splits > 1) {
     a.P = static_cast<float*>(ws);
-    a.kper = ceil_div(ceil_div(K, TK), splits) * TK;
+    a.kper = ceil_div(ceil_div(K, TKS), splits) * TKS;
     splits = (int)ceil_div(K, a.kper);
   }
-  const dim3 grid((unsigned)ceil_div(N, TN), (unsigned)ceil_div(M, TM), (unsigned)splits);
-#define GQ_GEMM_G(F, B) \
-  if (gx) gemm_kernel<F, B, true><<<grid, 256, 0, s>>>(a); else gemm_kernel<F, B, false><<<grid, 256, 0, s>>>(a);
+  const int mt = gemm_mt(M);
+  const dim3 grid((unsigned)ceil_div(N, TN), (unsigned)ceil_div(M, 32 * mt), (unsigned)splits);
+#define GQ_GEMM_V(F, B, MT, GX) \
+  if (va) gemm_kernel<F, B, MT, GX, true><<<grid, 256, 0, s>>>(a); else gemm_kernel<F, B, MT, GX, false><<<grid, 256, 0, s>>>(a);
+#define GQ_GEMM_K(F, B, MT) \
+  if (gx) { GQ_GEMM_V(F, B, MT, true) } else { GQ_GEMM_V(F, B, MT, false) }
+#define GQ_GEMM_G(F, B)                        \
+  switch (mt) {                                \
+    case 1: GQ_GEMM_K(F, B, 1); break;         \
+    case 2: GQ_GEMM_K(F, B, 2); break;         \
+    default: GQ_GEMM_K(F, B, 4); break;        \
+  }
 #define GQ_GEMM(F)                                \
   switch (bits) {                                 \
     case 2: GQ_GEMM_G(F, 2); break;               \
@@ -482,6 +641,8 @@ hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_
   if (f16) { GQ_GEMM(true) } else { GQ_GEMM(false) }
 #undef GQ_GEMM
 #undef GQ_GEMM_G
+#undef GQ_GEMM_K
+#undef GQ_GEMM_V
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const unsigned gr = (unsigned)std::min<int64_t>(ceil_div(M * N, 256), 4096);

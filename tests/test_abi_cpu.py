@@ -277,8 +277,10 @@ def test_w4a16_validation():
     assert f(*ok(lda=100)) == n.ERR_INVALID_ARG
     assert f(*ok(g=48)) == n.ERR_UNSUPPORTED
     assert f(*ok(ng=1)) == n.ERR_INVALID_ARG
+    # the kernels address A and the weight words with 32-bit byte offsets
+    assert f(*ok(M=2, lda=2**31)) == n.ERR_UNSUPPORTED and "4 GiB" in n.last_error()
     # a given workspace must hold the split-K partials
-    need = L.gptq_workspace_bytes(n.WS_W4A16, 64, 256, 64, None)
+    need = L.gptq_workspace_bytes(n.WS_W4A16, 64, 1024, 64, None)
     assert need >= 64 * 64 * 4 * 2
-    assert f(*ok(M=64, ws=FAKE, ws_bytes=need - 4)) == n.ERR_WORKSPACE
+    assert f(*ok(M=64, K=1024, lda=1024, ng=8, ws=FAKE, ws_bytes=need - 4)) == n.ERR_WORKSPACE
     assert L.gptq_workspace_bytes(n.WS_W4A16, 64, 256, 0, None) == 0

@@ -518,9 +518,10 @@ def test_w4a16_gemm_matches_oracle(M, act, bits, g, act_order):
 @pytest.mark.parametrize("M,act,bits,K,split", [
     (1, "f16", 4, 4096, True), (3, "bf16", 4, 4000, True), (1, "bf16", 3, 4096, True),
     (64, "f16", 4, 4096, True), (64, "f16", 4, 4096, False), (200, "bf16", 3, 4000, True),
-    (17, "f16", 8, 4096, False), (5, "bf16", 2, 4064, True)])
+    (17, "f16", 8, 4096, False), (5, "bf16", 2, 4064, True), (40, "bf16", 4, 630, False)])
 def test_w4a16_gemm_large_k(M, act, bits, K, split):
-    """Long rows (K up to 4096, ragged) and a ragged N: any word stream is a
+    """Long rows (K up to 4096, ragged; 630 leaves a GEMM tail of two 64-deep
+    steps after its unrolled loop) and a ragged N: any word stream is a
     valid dense code stream, so the codes are random words; scales are random
     halves and zeros random codes.  With a workspace, products with few tiles
     split K (fixed-order sum of fp32 partials); without one they run unsplit.
