@@ -23,7 +23,7 @@
 // product and MFMA sum unchanged.
 //   gemv_kernel  (M <= 4): bound by the weights' HBM traffic and the
 //                dequantization.  A sits in LDS as packed 16-bit pairs,
-//                staged once per workgroup (at most four per CU) while the
+//                staged once per workgroup (16 waves per CU) while the
 //                first weight words are in flight; a wave takes 2 weight rows
 //                at a time, lane l their chunks l, l+64, ..., and walks its
 //                row sets as one stream with the words of the next two items
@@ -204,8 +204,13 @@ __device__ __forceinline__ void dequant_chunk(const WArgs& a, const uint32_t (&w
   }
 }
 
+// threads per GEMV workgroup: four A rows take up to 64 KB of LDS, two
+// workgroups per CU, so they run eight waves each
+constexpr int gemv_threads(int MM) { return MM == 4 ? 512 : 256; }
+
 template <bool F16, int BITS, int MM, bool GIDX>
-__global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
+__global__ __launch_bounds__(gemv_threads(MM)) void gemv_kernel(WArgs a) {
+  constexpr int GT = gemv_threads(MM), GW = GT / 64;
   extern __shared__ __attribute__((aligned(16))) uint32_t Ap[];   // [MM][Kp/2] packed pairs
   constexpr bool PERM = kHalfPairs<F16, BITS> && !GIDX;
   const int t = threadIdx.x, lane = t & 63;
@@ -213,8 +218,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
   const int64_t KW = Kp / 2;
   const int64_t nch = Kp / 32;
   // the wave index as a scalar: the item loop below is uniform per wave
-  const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t wave = (int64_t)blockIdx.x * GW + __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * GW;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q, a.q_bytes);
   // rows past N and chunks past the row are fetched from the last row and
   // chunk (in bounds, never used), so every fetch is the same straight-line
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
     int ke[4], me[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = e0 + t + 256 * i;
+      const int e = e0 + t + GT * i;
       me[i] = (int)((uint32_t)e / (uint32_t)ipr);
       ke[i] = (e - me[i] * ipr) * 8;
       const uint32_t off = e < nitems_a && me[i] < a.M ? (uint32_t)((me[i] * a.lda + ke[i]) * 2) : a.a_bytes;
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = e0 + t + 256 * i;
+      const int e = e0 + t + GT * i;
       if (e < nitems_a) {
         const int64_t left = a.K - ke[i];   // values of this item inside K
 #pragma unroll
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(WArgs a) {
   };
   auto stage_all = [&](auto vec) {
     stage_a(0, std::true_type{}, vec);
-    for (int e0 = 4 * 256; e0 < nitems_a; e0 += 4 * 256) stage_a(e0, std::false_type{}, vec);
+    for (int e0 = 4 * GT; e0 < nitems_a; e0 += 4 * GT) stage_a(e0, std::false_type{}, vec);
   };
   if (a.vec_a) stage_all(std::true_type{}); else stage_all(std::false_type{});
   lds_barrier();
@@ -586,10 +591,13 @@ hipError_t w4a16_launch(const void* A, int a_dtype, int64_t M, int64_t K, int64_
   const int mm = M <= 1 ? 1 : M <= 2 ? 2 : 4;
   const int64_t Kp = ceil_div(K, 32) * 32;
   if (M <= 4 && (int64_t)mm * Kp * 2 <= kGemvLds) {
-    // at most four workgroups per CU: each stages A once and loops over rows
-    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(N, 4 * RW), 1024));
+    // 4096 waves (sixteen per CU): each workgroup stages A once and its
+    // waves loop over rows
+    const int gw = gemv_threads(mm) / 64;
+    const unsigned grid =
+        (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(N, gw * RW), 4096 / gw));
     const size_t lds = (size_t)mm * Kp * 2;
-#define GQ_GEMV(F, B, MM, GX) gemv_kernel<F, B, MM, GX><<<grid, 256, lds, s>>>(a)
+#define GQ_GEMV(F, B, MM, GX) gemv_kernel<F, B, MM, GX><<<grid, gemv_threads(MM), lds, s>>>(a)
 #define GQ_GEMV_G(F, B, MM) \
   if (gx) GQ_GEMV(F, B, MM, true); else GQ_GEMV(F, B, MM, false);
 #define GQ_GEMV_M(F, B)                          \
