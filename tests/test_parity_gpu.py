@@ -186,6 +186,22 @@ def test_layer_variants(kw):
     compare_layer(gpu, W, wl.w_dtype, oracle.hessian(X, wl.x_dtype), op, label=str(kw))
 
 
+@pytest.mark.parametrize("kw", [dict(group_size=1024), dict(group_size=512), dict(group_size=-1),
+                                dict(group_size=128, act_order=True), dict(group_size=64, bits=3)])
+def test_layer_wide_rows(kw):
+    """Rows of four and a half 512-column super-blocks (2304 columns): the
+    update after each super-block reaches every column to its right, the
+    last super-block and block are ragged, and groups of 1024 start in one
+    super-block and end in the next, so the columns their parameters read
+    must be current at the group start."""
+    wl = synth.WORKLOADS["llama7b-attn"].scaled(d_out=96, d_in=2304, n_tok=4096)
+    W, X = _inputs(wl)
+    gp, op = params_of(wl, **kw)
+    log(f"CASE wide rows {kw}: {wl.describe()}")
+    gpu = run_gpu(W, wl.w_dtype, X, wl.x_dtype, gp)
+    compare_layer(gpu, W, wl.w_dtype, oracle.hessian(X, wl.x_dtype), op, label=f"wide rows {kw}")
+
+
 def test_dead_channels():
     wl = synth.WORKLOADS["llama7b-attn"].scaled(d_out=128, d_in=384, n_tok=2048)
     W, X = _inputs(wl)
