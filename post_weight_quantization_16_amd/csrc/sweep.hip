@@ -65,6 +65,16 @@ __device__ __forceinline__ float row_max(float x) {
   return fmaxf(x, dpp<0x140>(x));
 }
 
+// One column's quantization: q = clamp(rint(w/s + z)) with 1/s as rs, and
+// x = w − s(q − z) rounded once, so err = x·(1/U_jj).  Written out so the
+// column loop and the write-back (which recomputes ŵ, err and q from the
+// weight each column was quantized from) round identically.
+struct QOut { float q, x; };
+__device__ __forceinline__ QOut quant1(float wj, float s, float rs, float z, float fmaxq) {
+  const float q = fminf(fmaxf(rintf(fmaf(wj, rs, z)), 0.f), fmaxq);
+  return QOut{q, fmaf(-s, q - z, wj)};
+}
+
 // G > 0: groups of G columns inside the block (parameters from registers);
 // G == 0: the block lies inside one group whose parameters are already in
 // scales/zeros.  bw = number of real columns in the block.
@@ -72,7 +82,7 @@ template <int G>
 __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   constexpr int GG = G > 0 ? G : 1;
   __shared__ __attribute__((aligned(16))) float Us[kBlock * kBlock];
-  __shared__ float rud[kBlock];
+  __shared__ __attribute__((aligned(16))) float rud[kBlock];
   const int nthr = blockDim.x, t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int c = lane & 15, rloc = lane >> 4;          // lane within the row, row in the wave
@@ -112,10 +122,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
     }
   }
   // slot sl < 4: column 4c+sl; slot sl >= 4: column 64+4c+sl-4; after
-  // column j the owner lane's slot holds ŵ (w), err (e) and the code (qc)
-  float w[QC], e[QC], qc[QC];
-#pragma unroll
-  for (int k = 0; k < QC; ++k) { e[k] = 0.f; qc[k] = 0.f; }
+  // column j the owner lane's slot keeps the weight column j was quantized
+  // from (U's diagonal is zeroed in LDS, and later columns' rows of U are
+  // zero there), from which the write-back recomputes ŵ, err and q
+  float w[QC];
   {
     const float* src = a.Wk + (live ? r : 0) * a.ldw + a.b0 + 4 * c;
     const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
@@ -127,7 +137,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): U copies and weights have landed
   __syncthreads();
-  for (int j = t; j < kBlock; j += nthr) rud[j] = 1.f / Us[j * kBlock + j];
+  for (int j = t; j < kBlock; j += nthr) {
+    rud[j] = 1.f / Us[j * kBlock + j];
+    Us[j * kBlock + j] = 0.f;
+  }
   __syncthreads();
 
   float s = 1.f, z = 0.f, rs = 1.f;
@@ -144,27 +157,31 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
   float gs[NG], gz[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) { gs[k] = 1.f; gz[k] = 0.f; }
-  // U row j and 1/U_jj are read from LDS two columns ahead; the scheduling
-  // barrier at the end of each column keeps the compiler from hoisting all
-  // 128 columns' reads (which would not fit in registers)
+  // U row j is read from LDS two columns ahead (its first half only while
+  // j < 64: afterwards the lanes' columns below 64 are all done) and 1/U_jj
+  // four at a time; the scheduling barrier at the end of each column keeps
+  // the compiler from hoisting all 128 columns' reads (which would not fit
+  // in registers)
   constexpr int PF = 2;
   f32x4 ub0[PF], ub1[PF];
-  float ubr[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     ub0[p] = *reinterpret_cast<const f32x4*>(Us + p * kBlock + 4 * c);
     ub1[p] = *reinterpret_cast<const f32x4*>(Us + p * kBlock + 64 + 4 * c);
-    ubr[p] = rud[p];
   }
+  f32x4 ru4 = *reinterpret_cast<const f32x4*>(rud), ru4n = *reinterpret_cast<const f32x4*>(rud + 4);
 #pragma unroll
   for (int j = 0; j < kBlock; ++j) {
     const int o = (j & 63) >> 2, slot = (j >> 6) * 4 + (j & 3);
     const f32x4 u0 = ub0[j % PF], u1 = ub1[j % PF];
-    const float ru = ubr[j % PF];
+    if (j % 4 == 0 && j > 0) {
+      ru4 = ru4n;
+      if (j + 4 < kBlock) ru4n = *reinterpret_cast<const f32x4*>(rud + j + 4);
+    }
+    const float ru = ru4[j % 4];
     if (j + PF < kBlock) {
-      ub0[j % PF] = *reinterpret_cast<const f32x4*>(Us + (j + PF) * kBlock + 4 * c);
+      if (j + PF < 64) ub0[j % PF] = *reinterpret_cast<const f32x4*>(Us + (j + PF) * kBlock + 4 * c);
       ub1[j % PF] = *reinterpret_cast<const f32x4*>(Us + (j + PF) * kBlock + 64 + 4 * c);
-      ubr[j % PF] = rud[j + PF];
     }
     if (G > 0 && j % GG == 0) {
       // the group's columns [j, j+G) ∩ real columns, spread over the row
@@ -188,26 +205,43 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       gz[j / GG] = z;
     }
     const float wj = row_bcast(w[slot], o);
-    const float v = wj * rs + z;
-    const float q = fminf(fmaxf(rintf(v), 0.f), fmaxq);
-    const float wq = s * (q - z);
-    const float err = (wj - wq) * ru;
+    const float err = quant1(wj, s, rs, z, fmaxq).x * ru;
+    // columns below 64 are all done once j >= 64 (U is upper triangular)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      w[q4] = fmaf(-err, u0[q4], w[q4]);
+      if (j < 64) w[q4] = fmaf(-err, u0[q4], w[q4]);
       w[4 + q4] = fmaf(-err, u1[q4], w[4 + q4]);
     }
-    // every lane of the row holds the same ŵ, err and q; the owner keeps
-    // them (a store to one LDS address from 16 lanes would serialize)
-    w[slot] = (c == o) ? wq : w[slot];
-    e[slot] = (c == o) ? err : e[slot];
-    qc[slot] = (c == o) ? q : qc[slot];
     // keep the compiler from deferring column updates to the end of the
     // block (which holds every column's err in registers): the updated
-    // weights and the kept values must exist here
+    // weights must exist here
 #pragma unroll
-    for (int k = 0; k < QC; ++k) asm volatile("" : "+v"(w[k]), "+v"(e[k]), "+v"(qc[k]));
+    for (int k = 0; k < QC; ++k) asm volatile("" : "+v"(w[k]));
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // ŵ, err and the code of each of the lane's columns, from the weight it
+  // was quantized from, with its group's parameters
+  float e[QC], qc[QC];
+  {
+    const f32x4 rlo = *reinterpret_cast<const f32x4*>(rud + 4 * c);
+    const f32x4 rhi = *reinterpret_cast<const f32x4*>(rud + 64 + 4 * c);
+#pragma unroll
+    for (int sl = 0; sl < QC; ++sl) {
+      const int col = (sl < 4) ? 4 * c + sl : 64 + 4 * c + (sl - 4);
+      float sv = s, zv = z, rsv = rs;
+      if (G > 0) {
+        const int gi = col / GG;
+        sv = gs[0];
+        zv = gz[0];
+#pragma unroll
+        for (int u = 1; u < NG; ++u) { sv = (gi == u) ? gs[u] : sv; zv = (gi == u) ? gz[u] : zv; }
+        rsv = 1.f / sv;
+      }
+      const QOut r1 = quant1(w[sl], sv, rsv, zv, fmaxq);
+      e[sl] = r1.x * (sl < 4 ? rlo[sl] : rhi[sl - 4]);
+      qc[sl] = r1.q;
+      w[sl] = sv * (r1.q - zv);
+    }
   }
   if (G > 0 && live && c == 0) {
     for (int k = 0; k < NG && k * GG < a.bw; ++k) {
