@@ -96,6 +96,10 @@ struct SweepArgs {
   float* Err; int64_t lde;        // the block's errors: [m x 128] at Err, row stride lde
   uint8_t* codes;                 // [m x ldw]
   float* row_loss;                // may be null
+  // the rest of the super-block, updated by the same kernel after the sweep:
+  // W[:, b0+128 : b0+128+nupd] −= Err·U[block, b0+128 : ...] with U's panel
+  // row j at Upan + j*ldu (nupd = 0: none; only for full blocks)
+  const float* Upan; int nupd;
 };
 template <int G> hipError_t launch_sweep(const SweepArgs& a, hipStream_t s);
 template <> hipError_t launch_sweep<0>(const SweepArgs& a, hipStream_t s);

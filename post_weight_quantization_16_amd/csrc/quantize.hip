@@ -536,12 +536,18 @@ hipError_t run_blocks(QWs& w, int64_t m, int64_t d, const float* U, const gptq_p
       a.maxq = maxq; a.sym = p.sym; a.scales = scales; a.zeros = zeros; a.ng = ng; a.g = g;
       a.Err = w.Err + (b0 - sb0); a.lde = lde;
       a.codes = w.codes; a.row_loss = row_loss;
+      // the rest of the super-block, W[:, b1:se] −= Err_b · U[b, b1:se], in
+      // the sweep kernel itself (a ragged block is the last one, so the
+      // update always follows a full block)
+      const int64_t b1 = b0 + bw;
+      const bool fused = b1 < se && bw == kBlock;
+      a.Upan = U + b0 * d + b1;
+      a.nupd = fused ? (int)(se - b1) : 0;
       {
         TimerScope ts(kTimerSweep, s);
         if ((e = launch_sweep<G>(a, s)) != hipSuccess) return e;
       }
-      const int64_t b1 = b0 + bw;
-      if (b1 < se) {  // the rest of the super-block: W[:, b1:se] −= Err_b · U[b, b1:se]
+      if (b1 < se && !fused) {  // the rest of the super-block: W[:, b1:se] −= Err_b · U[b, b1:se]
         GemmArgs u{};
         u.M = (int)m; u.N = (int)(se - b1); u.K = bw; u.k_last = bw; u.batch = 1;
         u.alpha = -1.f; u.beta = 1.f;

@@ -31,6 +31,7 @@ namespace gq {
 namespace {
 
 constexpr int QC = kBlock / 16;   // columns per lane
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -73,6 +74,92 @@ struct QOut { float q, x; };
 __device__ __forceinline__ QOut quant1(float wj, float s, float rs, float z, float fmaxq) {
   const float q = fminf(fmaxf(rintf(fmaf(wj, rs, z)), 0.f), fmaxq);
   return QOut{q, fmaf(-s, q - z, wj)};
+}
+
+// The rest of the super-block for the workgroup's rows (GPTQ's lazy batch
+// update, restricted to the super-block): W[rows, n] −= Σ_k E[rows][k]·U[k][n]
+// over the block's 128 k, for the nupd columns n after the block, on
+// v_mfma_f32_16x16x4f32: a[x][k] = −E[x][k] from lane (x, kq), b[k][y] =
+// U[k][y] from lane (y, kq), D[x][y] at lane (y, kq) for rows x = 4kq..4kq+3.
+// Lane group kq takes k = 32kq + s at step s (the same for both operands),
+// so a lane reads its E row as whole float4s.  The workgroup's 4·waves rows
+// are M (rows of 16 beyond them, or beyond m, are computed and dropped);
+// wave w takes the 16-column tiles w, w + waves, ...; each tile's 32 U values
+// and 4 weights per lane are loaded a tile ahead, from clamped positions
+// (columns past nupd are computed and dropped).
+constexpr int kEs = kBlock + 4;   // LDS row stride of E (floats)
+__device__ __forceinline__ void panel_update(const SweepArgs& a, float* Us, const float (&e)[8],
+                                             int wave, int lane) {
+  const int nw = blockDim.x >> 6, rows = 4 * nw;
+  const int c = lane & 15, rloc = lane >> 4;
+  __syncthreads();   // every wave is past the column loop: Us is free
+  float* Es = Us;    // [16][kEs]: E of the workgroup's rows
+  *reinterpret_cast<f32x4*>(Es + (4 * wave + rloc) * kEs + 4 * c) = f32x4{e[0], e[1], e[2], e[3]};
+  *reinterpret_cast<f32x4*>(Es + (4 * wave + rloc) * kEs + 64 + 4 * c) = f32x4{e[4], e[5], e[6], e[7]};
+  __syncthreads();
+  const int l16 = lane & 15, kq = lane >> 4;
+  float av[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(Es + l16 * kEs + 32 * kq + 4 * i);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) av[4 * i + u] = -v[u];
+  }
+  const int64_t row0 = (int64_t)blockIdx.x * rows;
+  const int ntiles = (a.nupd + 15) / 16;
+  // the workgroup's rows of W from the first updated column, as a buffer:
+  // lanes whose row or column is outside get an offset past its end, so
+  // their loads read 0 and their stores are dropped, with no branch
+  const int64_t c0 = a.b0 + kBlock;
+  const int64_t nrows = a.m - row0 < rows ? a.m - row0 : rows;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.Wk + row0 * a.ldw + c0, 0, (int)(nrows * a.ldw * 4), 0x00020000);
+  constexpr uint32_t kOut = 0x80000000u;   // past any workgroup's rows (< 2^31 bytes)
+  auto woff = [&](int v, int n) -> uint32_t {
+    const int x = 4 * kq + v;
+    const bool ok = (x < rows) & (n < a.nupd);   // no short-circuit branch
+    return ok ? (uint32_t)((x * a.ldw + n) * 4) : kOut;
+  };
+  // the tile's weights first (the accumulator needs them first), then its
+  // 32 U values (columns past nupd read the last column: computed, dropped)
+  auto load = [&](int tile, float (&bv)[32], f32x4& cv) {
+    const int tc = tile < ntiles ? tile : ntiles - 1;
+    const int n0 = 16 * tc + l16, n = n0 < a.nupd ? n0 : a.nupd - 1;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      cv[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wrs, woff(v, n0), 0, 0));
+    const float* ub = a.Upan + (int64_t)(32 * kq) * a.ldu + n;
+#pragma unroll
+    for (int s2 = 0; s2 < 32; ++s2) bv[s2] = ub[(int64_t)s2 * a.ldu];
+    __builtin_amdgcn_sched_barrier(0);   // all issued before the chain that follows
+  };
+  auto compute = [&](int tile, const float (&bv)[32], f32x4 acc) {
+#pragma unroll
+    for (int s2 = 0; s2 < 32; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], bv[s2], acc, 0, 0, 0);
+    const int n = 16 * tile + l16;
+    // bit-cast as a whole vector: a bit-cast of one element of a float4
+    // (acc[v]) was compiled as a bit-cast of its first element for every v
+    // (read in the ISA)
+    const u32x4 o = __builtin_bit_cast(u32x4, acc);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) __builtin_amdgcn_raw_buffer_store_b32(o[v], wrs, woff(v, n), 0, 0);
+    // one tile at a time: the next tile's loads then have this whole chain
+    // to land in
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // this wave's tiles w + i·waves, two buffers, each loaded a tile ahead
+  const int mine = wave < ntiles ? (ntiles - 1 - wave) / nw + 1 : 0;
+  float b0v[32], b1v[32];
+  f32x4 c0v, c1v;
+  load(wave, b0v, c0v);
+  int i = 0;
+  for (; i + 2 <= mine; i += 2) {
+    load(wave + (i + 1) * nw, b1v, c1v);
+    compute(wave + i * nw, b0v, c0v);
+    load(wave + (i + 2) * nw, b0v, c0v);
+    compute(wave + (i + 1) * nw, b1v, c1v);
+  }
+  if (i < mine) compute(wave + i * nw, b0v, c0v);
 }
 
 // G > 0: groups of G columns inside the block (parameters from registers);
@@ -282,6 +369,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepArgs a) {
       *reinterpret_cast<uint32_t*>(dq + 64 * h) = pk;
     }
   }
+  if (a.nupd > 0) panel_update(a, Us, e, wave, lane);
 }
 
 }  // namespace
