@@ -179,6 +179,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// f(integral_constant<int, I>) for I = B .. E−1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ---------------------------------------------------------------- GEMV
 constexpr int kGemvLds = 64 * 1024;   // bytes of A staged per workgroup
 constexpr int RW = 2;                 // weight rows per wave pass
@@ -517,16 +526,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(WArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
   int64_t i0 = 0;
-  for (; i0 + PD <= nsteps; i0 += PD) {
-    step(std::integral_constant<int, 0>{}, i0);
-    step(std::integral_constant<int, 1>{}, i0 + 1);
-    step(std::integral_constant<int, 2>{}, i0 + 2);
-    step(std::integral_constant<int, 3>{}, i0 + 3);
-  }
-  static_assert(PD == 4, "the loop above and the tail below are unrolled for PD = 4");
-  if (i0 < nsteps) step(std::integral_constant<int, 0>{}, i0);
-  if (i0 + 1 < nsteps) step(std::integral_constant<int, 1>{}, i0 + 1);
-  if (i0 + 2 < nsteps) step(std::integral_constant<int, 2>{}, i0 + 2);
+  for (; i0 + PD <= nsteps; i0 += PD)
+    static_for<0, PD>([&](auto pc) { step(pc, i0 + decltype(pc)::value); });
+  static_for<0, PD - 1>([&](auto pc) {
+    if (i0 + decltype(pc)::value < nsteps) step(pc, i0 + decltype(pc)::value);
+  });
   float* out = a.P ? a.P + (int64_t)blockIdx.z * a.M * a.N : a.C;
   const int64_t ldo = a.P ? a.N : a.ldc;
   if (ncol < a.N) {
