@@ -37,6 +37,25 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(KArgs g, int nx, int ny) 
   gemm_tile_dma<T, kRing<T>, TA, TB>(g, bx, by, blockIdx.z, gridDim.z, Sm);
 }
 
+// Triangular products (k_from_n: tile column bx runs K − bx·T of K; k_to_m:
+// tile row by runs (by+1)·T): workgroup L takes a tile and its mirror image
+// (bx and nx−1−bx, or by and ny−1−by) one after the other, so every
+// workgroup runs about K + T, and the launch is one even round instead of a
+// few long tiles that finish last (at d = 4096 the top level's two products
+// 115 -> 102 us each, the next level's 53 -> 40 us).
+template <int T, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_dma_pair_kernel(KArgs g, int nx, int ny) {
+  __shared__ __attribute__((aligned(1024))) char Sm[DTile<T, kRing<T>>::SMEM];
+  const int L = blockIdx.x;
+  int bx, by, bx2, by2;
+  if (g.k_from_n) { bx = L / ny; by = L % ny; bx2 = nx - 1 - bx; by2 = by; }
+  else { by = L / nx; bx = L % nx; bx2 = bx; by2 = ny - 1 - by; }
+  gemm_tile_dma<T, kRing<T>, TA, TB>(g, bx, by, blockIdx.z, gridDim.z, Sm);
+  if (bx2 == bx && by2 == by) return;
+  __syncthreads();   // the first tile's epilogue has read its LDS before the ring refills
+  gemm_tile_dma<T, kRing<T>, TA, TB>(g, bx2, by2, blockIdx.z, gridDim.z, Sm);
+}
+
 // Rectangular products whose 128-tiles fill whole rounds of the chip but
 // one: the last round's tiles run as four 64-tiles each (same launch, after
 // the 128-tiles), so that round takes about a quarter of a 128-tile's time
@@ -118,6 +137,19 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
     else if (!a.trans_a && a.trans_b) gemm_mixed_kernel<false, true><<<grid, 256, 0, s>>>(k, nx, (int)full);
     else if (a.trans_a && !a.trans_b) gemm_mixed_kernel<true, false><<<grid, 256, 0, s>>>(k, nx, (int)full);
     else gemm_mixed_kernel<true, true><<<grid, 256, 0, s>>>(k, nx, (int)full);
+    return hipGetLastError();
+  }
+  // paired triangular tiles once the 64-tiles fill the chip's workgroup
+  // slots (two per CU); with fewer, the single tiles all run side by side
+  const int64_t tiles64 = ceil_div(a.M, 64) * ceil_div(a.N, 64) * a.batch;
+  if ((a.k_from_n || a.k_to_m) && tiles64 >= kSlots128 && dma_ok(k, a.trans_a, a.trans_b)) {
+    const int nx = (int)ceil_div(a.N, 64), ny = (int)ceil_div(a.M, 64);
+    const int gx = a.k_from_n ? (nx + 1) / 2 * ny : (ny + 1) / 2 * nx;
+    dim3 grid((unsigned)gx, 1, (unsigned)a.batch);
+    if (!a.trans_a && !a.trans_b) gemm_dma_pair_kernel<64, false, false><<<grid, 256, 0, s>>>(k, nx, ny);
+    else if (!a.trans_a && a.trans_b) gemm_dma_pair_kernel<64, false, true><<<grid, 256, 0, s>>>(k, nx, ny);
+    else if (a.trans_a && !a.trans_b) gemm_dma_pair_kernel<64, true, false><<<grid, 256, 0, s>>>(k, nx, ny);
+    else gemm_dma_pair_kernel<64, true, true><<<grid, 256, 0, s>>>(k, nx, ny);
     return hipGetLastError();
   }
   const bool small = tiles128 < kSlots128 || ((a.k_from_n || a.k_to_m) && a.K >= 1024);
