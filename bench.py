@@ -177,8 +177,9 @@ def time_events(fn, reps, stream):
 
 def extras(gq, torch, wl, W, X, params, H, ws_h, ws_p, stream):
     """Throughput of the rows beyond the single layer, on the same inputs:
-    several layers against one factor, the exported layer's W4A16 product, and
-    the OBQ comparator on a tiny layer."""
+    several layers against one factor, independent small layers run
+    concurrently, the exported layer's W4A16 product, and the OBQ comparator
+    on a tiny layer."""
     import numpy as np
     import synth
     out = {}
@@ -206,6 +207,34 @@ def extras(gq, torch, wl, W, X, params, H, ws_h, ws_p, stream):
         "shape": f"3 x {m}x{d}, one H over {X.shape[0]} tokens", "ms": tb,
         "weights_per_s": 3 * m * d / (tb * 1e-3), "ms_separate_calls": ts,
         "weights_per_s_separate_calls": 3 * m * d / (ts * 1e-3)}
+    # independent small layers (each its own X, H and factor): eight
+    # 1024x1024 layers over 16384 tokens each, one concurrent call against the
+    # three calls per layer made one layer after the other
+    nl, ds, ns = 8, 1024, 16384
+    gen = torch.Generator(device=W.device).manual_seed(11)
+    small = [((torch.randn(ds, ds, device=W.device, generator=gen) * 0.02).to(torch.bfloat16),
+              torch.randn(ns, ds, device=W.device, generator=gen).to(torch.bfloat16))
+             for _ in range(nl)]
+    ws_l = [torch.empty(gq.workspace_bytes(5, ds, ds, ns, params), dtype=torch.uint8, device=W.device)
+            for _ in range(nl)]
+    Hs = torch.empty(ds, ds, device=W.device)
+    ws_hs = torch.empty(gq.workspace_bytes(0, 0, ds, ns), dtype=torch.uint8, device=W.device)
+    ws_ps = torch.empty(gq.workspace_bytes(1, 0, ds, 0, params), dtype=torch.uint8, device=W.device)
+    ws_qs = torch.empty(gq.workspace_bytes(2, ds, ds, 0, params), dtype=torch.uint8, device=W.device)
+
+    def one_by_one():
+        for Wi, Xi in small:
+            Hs.zero_()
+            gq.hessian_accumulate(Hs, Xi, ws=ws_hs)
+            gq.quantize_layer(Wi, gq.prepare_hinv(Hs, params, ws=ws_ps), params, ws=ws_qs)
+
+    ti = time_events(lambda: gq.quantize_independent(small, params, ws=ws_l), 5, stream)
+    to = time_events(one_by_one, 5, stream)
+    out["independent_layers"] = {
+        "shape": f"{nl} x {ds}x{ds}, each its own X of {ns} bf16 tokens", "ms": ti,
+        "weights_per_s": nl * ds * ds / (ti * 1e-3), "ms_one_after_another": to,
+        "weights_per_s_one_after_another": nl * ds * ds / (to * 1e-3)}
+    del small, ws_l
     # W4A16 product with the exported headline layer (4-bit, g128)
     H.zero_()
     gq.hessian_accumulate(H, X, ws=ws_h)

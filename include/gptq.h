@@ -87,10 +87,12 @@ typedef struct {
 typedef void* gptq_stream;
 
 enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2, GPTQ_WS_OBQ = 3,
-       GPTQ_WS_W4A16 = 4 };
+       GPTQ_WS_W4A16 = 4, GPTQ_WS_LAYER = 5 };
 
 /* Workspace size in bytes that call `which` (GPTQ_WS_*) needs for the given
- * shape.  n_tok is used by the Hessian call only; p may be NULL for it.
+ * shape.  n_tok is used by the Hessian call and GPTQ_WS_LAYER only; p may be
+ * NULL for the Hessian.  GPTQ_WS_LAYER is one job of
+ * gptq_quantize_independent (its Hessian, preparation and quantization).
  * For GPTQ_WS_W4A16 the shape is d_out = N, d_in = K, n_tok = M (p unused).
  * Returns 0 for invalid arguments.  Workspaces need 256-byte alignment
  * (every hipMalloc'd pointer has it). */
@@ -212,6 +214,58 @@ typedef struct {
 int gptq_quantize_layers(int n_layers, const gptq_layer* layers, int64_t d_in, const float* U,
                          const int32_t* perm, const uint8_t* dead_mask, const gptq_params* p,
                          int32_t* g_idx, void* ws, size_t ws_bytes, gptq_stream stream);
+
+/* One layer of gptq_quantize_independent: its own calibration inputs, weights,
+ * outputs and workspace.  Meaning, layout and NULL rules of the fields are
+ * those of the gptq_hessian_accumulate, gptq_prepare_hinv and
+ * gptq_quantize_layer arguments of the same names. */
+typedef struct {
+  const void* X;       /* [n_tok x d_in] of x_dtype, row stride ld_x               */
+  int32_t x_dtype;     /* GPTQ_F32 / GPTQ_BF16 / GPTQ_F16                          */
+  int32_t w_dtype;     /* GPTQ_F32 / GPTQ_BF16 / GPTQ_F16                          */
+  int64_t n_tok;       /* >= 0 (0: H is used as it comes)                          */
+  int64_t ld_x;
+  const void* W;       /* [d_out x d_in] of w_dtype, row stride ld_w               */
+  int64_t d_out;
+  int64_t d_in;
+  int64_t ld_w;
+  float* H;            /* in/out [d_in x d_in]: 2·XᵀX is added, then H_d replaces it */
+  float* U;            /* out [d_in x d_in]                                        */
+  int32_t* perm;       /* out [d_in]; required with act_order, else may be NULL    */
+  uint8_t* dead_mask;  /* out [d_in] or NULL                                       */
+  uint32_t* qweight;   /* out, packed codes                                        */
+  float* scales;       /* out [d_out x n_groups]                                   */
+  uint8_t* zeros;      /* out [d_out x n_groups]                                   */
+  float* W_hat;        /* out [d_out x d_in] or NULL                               */
+  int32_t* g_idx;      /* out [d_in] or NULL                                       */
+  float* row_loss;     /* out [d_out] or NULL                                      */
+  void* ws;            /* gptq_workspace_bytes(GPTQ_WS_LAYER, d_out, d_in, n_tok, p) */
+  size_t ws_bytes;
+  int32_t status;      /* out: this layer's factorization status (gptq_status)     */
+  int32_t reserved;    /* 0                                                        */
+  int64_t info;        /* out: failing pivot with GPTQ_ERR_NOT_SPD, else -1        */
+} gptq_layer_job;
+
+/* Independent layers -- each with its own inputs X, hence its own H and
+ * factor -- quantized concurrently ("Foundations", The Layer-Wise
+ * Reconstruction Problem: every layer is its own problem; "GPTQ" technology
+ * card, Parallelism: layers can be processed in parallel).  For every job:
+ * H += 2·XᵀX, the preparation of gptq_prepare_hinv, then gptq_quantize_layer
+ * with that factor.  Jobs run on streams of the library's own (default
+ * priority), forked from `stream` and joined back into it, so small layers
+ * fill the GPU together; each job's outputs are, bit for bit, those of the
+ * three calls made one after the other for that job alone.
+ *  jobs   host array of n_jobs (1..1024) descriptors; shapes may differ; the
+ *         workspaces must not overlap.
+ *  p      quantizer parameters shared by all jobs.
+ * Synchronizes `stream` once at the end (it reads every job's status).
+ * Returns GPTQ_OK when every job succeeded; otherwise the status of the
+ * first failed job (its `status` and `info` fields, like every job's, say
+ * which); a failed job's outputs are undefined, the others' are valid.
+ * Argument errors are found before anything is enqueued (no job runs then,
+ * and no status field is written). */
+int gptq_quantize_independent(int n_jobs, gptq_layer_job* jobs, const gptq_params* p,
+                              gptq_stream stream);
 
 /* Optimal Brain Quantization, the greedy-order comparator for GPTQ's fixed
  * order on tiny layers ("Foundations": Optimal Brain Surgeon (OBS) and

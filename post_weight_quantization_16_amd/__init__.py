@@ -292,6 +292,71 @@ def quantize_layers(Ws, prep: Prepared, params: GPTQParams, want_what: bool = Tr
     return outs
 
 
+def quantize_independent(layers, params: GPTQParams, want_what: bool = True, ws=None) -> list:
+    """Independent layers, each with its own inputs: ``layers`` is a list of
+    (W, X) device tensors (W [d_out, d_in], X [n_tok, d_in] token-major).
+    Every layer gets a fresh H = 2·XᵀX, its own factor and its quantization;
+    the library runs the layers concurrently and synchronizes once.  Returns
+    one (Quantized, Prepared, H_d) per layer, bitwise what hessian_accumulate,
+    prepare_hinv and quantize_layer give for that layer alone.  ``ws``: None,
+    or one workspace per layer (GPTQ_WS_LAYER bytes each).  Raises like
+    prepare_hinv when a layer's factorization fails (the first such layer);
+    the exception's ``statuses`` and ``results`` give every layer's status
+    and outputs (valid for the layers that succeeded)."""
+    torch = _torch()
+    if not layers:
+        raise ValueError("no layers")
+    L = _native.lib()
+    p = params.c()
+    cpw = 8 if params.bits <= 4 else 4
+    jobs = (_native.LayerJob * len(layers))()
+    out, keep = [], []
+    for i, (W, X) in enumerate(layers):
+        _matrix_rows(W, f"W[{i}]")
+        _matrix_rows(X, f"X[{i}]")
+        m, d = W.shape
+        n_tok = X.shape[0]
+        dev = W.device
+        if X.shape[1] != d or X.device != dev:
+            raise ValueError(f"X[{i}] must have {d} columns and live on {dev}")
+        ng = params.n_groups(d)
+        H = torch.zeros(d, d, dtype=torch.float32, device=dev)
+        prep = Prepared(torch.empty(d, d, dtype=torch.float32, device=dev),
+                        torch.empty(d, dtype=torch.int32, device=dev),
+                        torch.empty(d, dtype=torch.uint8, device=dev),
+                        natural=not params.act_order)
+        q = Quantized(torch.empty(m, (d + cpw - 1) // cpw, dtype=torch.int32, device=dev),
+                      torch.empty(m, ng, dtype=torch.float32, device=dev),
+                      torch.empty(m, ng, dtype=torch.uint8, device=dev),
+                      torch.empty(m, d, dtype=torch.float32, device=dev) if want_what else None,
+                      torch.empty(d, dtype=torch.int32, device=dev),
+                      torch.empty(m, dtype=torch.float32, device=dev))
+        w = ws[i] if ws is not None else _workspace(
+            L.gptq_workspace_bytes(_native.WS_LAYER, m, d, n_tok, ctypes.byref(p)), dev)
+        _ws_check(w, dev)
+        keep.append(w)
+        jobs[i] = _native.LayerJob(
+            _dev(X, "X"), _dtype_code(X), _dtype_code(W), n_tok, X.stride(0), _dev(W, "W"), m, d,
+            W.stride(0), _dev(H, "H"), _dev(prep.U, "U"), _dev(prep.perm, "perm"),
+            _dev(prep.dead, "dead"), _dev(q.qweight, "qweight"), _dev(q.scales, "scales"),
+            _dev(q.zeros, "zeros"), _dev(q.W_hat, "W_hat"), _dev(q.g_idx, "g_idx"),
+            _dev(q.row_loss, "row_loss"), _dev(w, "ws"), w.numel(), 0, 0, -1)
+        out.append((q, prep, H))
+    rc = L.gptq_quantize_independent(len(layers), jobs, ctypes.byref(p),
+                                     _stream(layers[0][0].device))
+    if rc != _native.OK:
+        if rc == _native.ERR_NOT_SPD:
+            bad = next(j for j in jobs if j.status == _native.ERR_NOT_SPD)
+            err = NotPositiveDefinite(rc, _native.last_error(), bad.info)
+        else:
+            err = GPTQError(rc, _native.last_error())
+        # per-layer statuses and results: the layers that succeeded are valid
+        err.statuses = [j.status for j in jobs]
+        err.results = out
+        raise err
+    return out
+
+
 def obq_layer(W, H, params: GPTQParams, ws=None):
     """OBQ (greedy order per row) of a tiny layer against the fp32 Hessian H.
 

@@ -15,7 +15,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NOT_SPD, ERR_WORKSPACE, ERR_HIP, ERR_I
 # gptq_dtype
 F32, BF16, F16 = 0, 1, 2
 # workspace kinds
-WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ, WS_W4A16 = 0, 1, 2, 3, 4
+WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ, WS_W4A16, WS_LAYER = 0, 1, 2, 3, 4, 5
 
 EXPORTS = (
     "gptq_workspace_bytes",
@@ -24,6 +24,7 @@ EXPORTS = (
     "gptq_prepare_hinv",
     "gptq_quantize_layer",
     "gptq_quantize_layers",
+    "gptq_quantize_independent",
     "gptq_obq_layer",
     "gptq_export",
     "gptq_w4a16_gemm",
@@ -64,6 +65,37 @@ class Layer(ctypes.Structure):
     ]
 
 
+class LayerJob(ctypes.Structure):
+    """Mirror of ``gptq_layer_job``."""
+
+    _fields_ = [
+        ("X", ctypes.c_void_p),
+        ("x_dtype", ctypes.c_int32),
+        ("w_dtype", ctypes.c_int32),
+        ("n_tok", ctypes.c_int64),
+        ("ld_x", ctypes.c_int64),
+        ("W", ctypes.c_void_p),
+        ("d_out", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("ld_w", ctypes.c_int64),
+        ("H", ctypes.c_void_p),
+        ("U", ctypes.c_void_p),
+        ("perm", ctypes.c_void_p),
+        ("dead_mask", ctypes.c_void_p),
+        ("qweight", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("zeros", ctypes.c_void_p),
+        ("W_hat", ctypes.c_void_p),
+        ("g_idx", ctypes.c_void_p),
+        ("row_loss", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
+        ("status", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("info", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -95,6 +127,8 @@ def lib() -> ctypes.CDLL:
     L.gptq_quantize_layers.argtypes = [_int, ctypes.POINTER(Layer), _i64, _vp, _vp, _vp, _pp, _vp,
                                        _vp, _sz, _vp]
     L.gptq_quantize_layers.restype = _int
+    L.gptq_quantize_independent.argtypes = [_int, ctypes.POINTER(LayerJob), _pp, _vp]
+    L.gptq_quantize_independent.restype = _int
     L.gptq_obq_layer.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _pp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _sz, _vp]
     L.gptq_obq_layer.restype = _int

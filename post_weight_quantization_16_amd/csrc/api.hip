@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -74,6 +76,46 @@ int check_ws(void* ws, size_t have, size_t need, const char* what) {
   return GPTQ_OK;
 }
 
+// One job of gptq_quantize_independent: the Hessian uses the whole workspace
+// (as much as gptq_hessian_accumulate would), the preparation its first part
+// and the quantization the part after it, so the preparation's status words
+// are still there when the job is done.
+size_t layer_prep_bytes(int64_t d) { return (gq::prepare_ws_bytes(d) + 255) / 256 * 256; }
+size_t layer_ws_bytes(int64_t m, int64_t d, int64_t n_tok) {
+  const size_t h = n_tok > 0 ? gq::hessian_ws_bytes(d, n_tok) : 0;
+  const size_t pq = layer_prep_bytes(d) + gq::quantize_ws_bytes(m, d);
+  return h > pq ? h : pq;
+}
+
+// Streams the independent jobs run on, per device, created on first use and
+// kept until the process ends (default priority, not synchronizing with the
+// null stream), with an event to fork from the caller's stream and one per
+// stream to join back.  A call holds the device's lock while it enqueues.
+constexpr int kJobStreams = 8;
+struct JobStreams {
+  hipStream_t s[kJobStreams] = {};
+  hipEvent_t fork = nullptr, join[kJobStreams] = {};
+  std::mutex mu;
+  hipError_t err = hipSuccess;
+};
+
+JobStreams* job_streams(int dev) {
+  static std::mutex map_mu;
+  static std::map<int, JobStreams*> pools;
+  std::lock_guard<std::mutex> g(map_mu);
+  auto it = pools.find(dev);
+  if (it != pools.end()) return it->second;
+  JobStreams* js = new JobStreams();
+  hipError_t e = hipEventCreateWithFlags(&js->fork, hipEventDisableTiming);
+  for (int i = 0; i < kJobStreams && e == hipSuccess; ++i) {
+    e = hipStreamCreateWithFlags(&js->s[i], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&js->join[i], hipEventDisableTiming);
+  }
+  js->err = e;
+  pools[dev] = js;
+  return js;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +140,9 @@ size_t gptq_workspace_bytes(int which, int64_t d_out, int64_t d_in, int64_t n_to
     case GPTQ_WS_OBQ:
       if (d_in > gq::obq_max_din()) return 0;
       return gq::obq_ws_bytes(d_in);
+    case GPTQ_WS_LAYER:
+      if (d_out <= 0 || d_out > kMaxDout || n_tok < 0) return 0;
+      return layer_ws_bytes(d_out, d_in, n_tok);
     case GPTQ_WS_W4A16:   // d_out = N, d_in = K, n_tok = M
       if (d_out <= 0 || d_out > kMaxDout || n_tok <= 0 || n_tok > kMaxDout) return 0;
       return gq::w4a16_ws_bytes(n_tok, d_out, d_in);
@@ -248,6 +293,92 @@ int gptq_quantize_layers(int n_layers, const gptq_layer* layers, int64_t d_in, c
   hipError_t e = gq::quantize_layers_launch(io.data(), n_layers, d_in, U, perm, dead_mask, *p, g_idx,
                                             ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("quantize_layers", e);
+  return GPTQ_OK;
+}
+
+int gptq_quantize_independent(int n_jobs, gptq_layer_job* jobs, const gptq_params* p,
+                              gptq_stream stream) {
+  if (n_jobs < 1 || n_jobs > 1024)
+    return fail(GPTQ_ERR_INVALID_ARG, "n_jobs must be in [1, 1024] (got %d)", n_jobs);
+  if (!jobs) return fail(GPTQ_ERR_INVALID_ARG, "jobs is NULL");
+  for (int i = 0; i < n_jobs; ++i) {
+    const gptq_layer_job& J = jobs[i];
+    if (!J.W || !J.H || !J.U || !J.qweight || !J.scales || !J.zeros)
+      return fail(GPTQ_ERR_INVALID_ARG, "job %d: W, H, U, qweight, scales and zeros must not be NULL", i);
+    if (!valid_dtype(J.w_dtype) || !valid_dtype(J.x_dtype))
+      return fail(GPTQ_ERR_INVALID_ARG, "job %d: unknown x_dtype or w_dtype", i);
+    if (J.d_in <= 0 || J.d_in > kMaxDin)
+      return fail(GPTQ_ERR_INVALID_ARG, "job %d: d_in must be in [1, %lld]", i, (long long)kMaxDin);
+    if (J.d_out <= 0 || J.d_out > kMaxDout)
+      return fail(GPTQ_ERR_INVALID_ARG, "job %d: d_out must be in [1, %lld]", i, (long long)kMaxDout);
+    if (J.ld_w < J.d_in) return fail(GPTQ_ERR_INVALID_ARG, "job %d: ld_w < d_in", i);
+    if (J.n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "job %d: n_tok must be >= 0", i);
+    if (J.n_tok > 0 && !J.X) return fail(GPTQ_ERR_INVALID_ARG, "job %d: X is NULL", i);
+    if (J.n_tok > 0 && J.ld_x < J.d_in) return fail(GPTQ_ERR_INVALID_ARG, "job %d: ld_x < d_in", i);
+    int rc = check_params(p, J.d_in);
+    if (rc) return rc;
+    if (p->act_order && !J.perm)
+      return fail(GPTQ_ERR_INVALID_ARG, "job %d: act_order needs a perm output", i);
+    rc = check_ws(J.ws, J.ws_bytes, layer_ws_bytes(J.d_out, J.d_in, J.n_tok), "quantize_independent");
+    if (rc) return fail(rc, "job %d: %s", i, g_err.c_str());
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("quantize_independent", e);
+  JobStreams* js = job_streams(dev);
+  if (js->err != hipSuccess) return hip_fail("quantize_independent (streams)", js->err);
+  hipStream_t s = (hipStream_t)stream;
+  const int ns = n_jobs < kJobStreams ? n_jobs : kJobStreams;
+  std::vector<int32_t*> status_dev((size_t)n_jobs, nullptr);
+  {
+    std::lock_guard<std::mutex> lock(js->mu);
+    if ((e = hipEventRecord(js->fork, s)) != hipSuccess) return hip_fail("quantize_independent", e);
+    for (int k = 0; k < ns; ++k)
+      if ((e = hipStreamWaitEvent(js->s[k], js->fork, 0)) != hipSuccess)
+        return hip_fail("quantize_independent", e);
+    for (int i = 0; i < n_jobs; ++i) {
+      const gptq_layer_job& J = jobs[i];
+      hipStream_t sj = js->s[i % ns];
+      char* ws = static_cast<char*>(J.ws);
+      if (J.n_tok > 0) {
+        e = gq::hessian_launch(J.H, J.d_in, J.X, J.x_dtype, J.n_tok, J.ld_x, ws,
+                               gq::hessian_ws_bytes(J.d_in, J.n_tok), sj);
+        if (e != hipSuccess) return hip_fail("quantize_independent (Hessian)", e);
+      }
+      e = gq::prepare_launch(J.H, J.d_in, p->percdamp, p->act_order, J.U, J.perm, J.dead_mask, ws,
+                             &status_dev[(size_t)i], sj);
+      if (e != hipSuccess) return hip_fail("quantize_independent (prepare)", e);
+      e = gq::quantize_launch(J.W, J.w_dtype, J.d_out, J.d_in, J.ld_w, J.U,
+                              p->act_order ? J.perm : nullptr, J.dead_mask, *p, J.qweight, J.scales,
+                              J.zeros, J.W_hat, J.g_idx, J.row_loss, ws + layer_prep_bytes(J.d_in), sj);
+      if (e != hipSuccess) return hip_fail("quantize_independent (quantize)", e);
+    }
+    for (int k = 0; k < ns; ++k) {
+      if ((e = hipEventRecord(js->join[k], js->s[k])) != hipSuccess ||
+          (e = hipStreamWaitEvent(s, js->join[k], 0)) != hipSuccess)
+        return hip_fail("quantize_independent", e);
+    }
+  }
+  std::vector<int32_t> st((size_t)n_jobs * 2, 0);
+  for (int i = 0; i < n_jobs && e == hipSuccess; ++i)
+    e = hipMemcpyAsync(&st[(size_t)i * 2], status_dev[(size_t)i], 2 * sizeof(int32_t),
+                       hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail("quantize_independent (status read-back)", e);
+  int first = GPTQ_OK, first_job = -1;
+  for (int i = 0; i < n_jobs; ++i) {
+    int64_t piv = -1;
+    const int rc = gq::prepare_status(st[(size_t)i * 2], st[(size_t)i * 2 + 1], jobs[i].d_in, &piv);
+    jobs[i].status = rc;
+    jobs[i].info = rc == GPTQ_ERR_NOT_SPD ? piv : -1;
+    if (rc != GPTQ_OK && first == GPTQ_OK) { first = rc; first_job = i; }
+  }
+  if (first == GPTQ_ERR_NOT_SPD)
+    return fail(first, "job %d: damped Hessian is not positive definite (pivot %lld); raise percdamp",
+                first_job, (long long)jobs[first_job].info);
+  if (first != GPTQ_OK)
+    return fail(first, "job %d: a factorization wave ran out of its bounded wait; outputs undefined",
+                first_job);
   return GPTQ_OK;
 }
 

@@ -33,19 +33,15 @@ def test_library_loads_and_exports_every_declared_call():
         assert re.search(rf"\bT {name}\b", out.stdout), name
 
 
-def test_header_is_c_and_struct_layout_matches_binding():
-    prog = r"""
-#include <stdio.h>
-#include <stddef.h>
-#include "gptq.h"
-int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(gptq_params), offsetof(gptq_params, bits),
-         offsetof(gptq_params, group_size), offsetof(gptq_params, block_size),
-         offsetof(gptq_params, percdamp), offsetof(gptq_params, act_order),
-         offsetof(gptq_params, sym));
-  return 0;
-}
-"""
+@pytest.mark.parametrize("cname,py", [("gptq_params", n.Params), ("gptq_layer", n.Layer),
+                                      ("gptq_layer_job", n.LayerJob)])
+def test_header_is_c_and_struct_layout_matches_binding(cname, py):
+    fields = [f for f, _ in py._fields_]
+    prog = "#include <stdio.h>\n#include <stddef.h>\n#include \"gptq.h\"\nint main(void) {\n"
+    prog += f'  printf("%zu\\n", sizeof({cname}));\n'
+    for f in fields:
+        prog += f'  printf("%zu\\n", offsetof({cname}, {f}));\n'
+    prog += "  return 0;\n}\n"
     with tempfile.TemporaryDirectory() as td:
         c = os.path.join(td, "t.c")
         exe = os.path.join(td, "t")
@@ -53,9 +49,54 @@ int main(void) {
         subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c,
                         "-o", exe], check=True)
         got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
-    P = n.Params
-    want = [ctypes.sizeof(P)] + [getattr(P, f).offset for f, _ in P._fields_]
+    want = [ctypes.sizeof(py)] + [getattr(py, f).offset for f in fields]
     assert got == want
+
+
+def _job(**kw):
+    d = dict(X=FAKE, x_dtype=n.BF16, w_dtype=n.BF16, n_tok=1024, ld_x=256, W=FAKE, d_out=64,
+             d_in=256, ld_w=256, H=FAKE, U=FAKE, perm=FAKE, dead_mask=None, qweight=FAKE,
+             scales=FAKE, zeros=FAKE, W_hat=None, g_idx=None, row_loss=None, ws=FAKE,
+             ws_bytes=1 << 40, status=77, reserved=0, info=77)
+    d.update(kw)
+    return n.LayerJob(**d)
+
+
+def test_independent_layers_validation():
+    """Every job is checked before anything is enqueued; a rejected call
+    leaves the status fields alone."""
+    L = n.lib()
+    p = _params()
+    run = lambda jobs, pp=p: L.gptq_quantize_independent(len(jobs), (n.LayerJob * len(jobs))(*jobs),
+                                                         ctypes.byref(pp), None)
+    assert L.gptq_quantize_independent(0, None, ctypes.byref(p), None) == n.ERR_INVALID_ARG
+    assert L.gptq_quantize_independent(1, None, ctypes.byref(p), None) == n.ERR_INVALID_ARG
+    for kw in [dict(W=None), dict(H=None), dict(U=None), dict(qweight=None), dict(x_dtype=9),
+               dict(d_in=0), dict(d_out=0), dict(ld_w=100), dict(n_tok=-1), dict(X=None),
+               dict(ld_x=100)]:
+        jobs = [_job(), _job(**kw)]
+        assert run(jobs) == n.ERR_INVALID_ARG, kw
+        assert "job 1" in n.last_error(), kw
+        assert jobs[0].status == 77 and jobs[1].status == 77
+    assert run([_job(ws_bytes=4096)]) == n.ERR_WORKSPACE
+    assert run([_job(ws=ctypes.c_void_p((1 << 20) + 8))]) == n.ERR_WORKSPACE
+    assert run([_job(perm=None)], _params(act_order=1)) == n.ERR_INVALID_ARG
+    assert run([_job()], _params(bits=5)) == n.ERR_INVALID_ARG
+    assert run([_job(d_in=300, ld_x=300, ld_w=300)], _params(group_size=96)) == n.ERR_UNSUPPORTED
+    # no tokens: X may be NULL (H is used as it comes); stopped by the workspace here
+    assert run([_job(X=None, n_tok=0, ws_bytes=16)]) == n.ERR_WORKSPACE
+
+
+def test_layer_workspace_holds_each_stage():
+    L = n.lib()
+    p = _params()
+    ws = lambda k, m, d, t: L.gptq_workspace_bytes(k, m, d, t, ctypes.byref(p))
+    for m, d, t in [(64, 256, 1024), (4096, 4096, 131072), (11008, 4096, 0), (100, 1000, 5)]:
+        lay = ws(n.WS_LAYER, m, d, t)
+        assert lay >= ws(n.WS_PREPARE, 0, d, 0) + ws(n.WS_QUANTIZE, m, d, 0)
+        if t:
+            assert lay >= ws(n.WS_HESSIAN, 0, d, t)
+    assert ws(n.WS_LAYER, 0, 256, 10) == 0 and ws(n.WS_LAYER, 64, 256, -1) == 0
 
 
 def _params(**kw):

@@ -369,6 +369,86 @@ def test_prepare_repeated_with_reused_workspace():
     assert rel_fro(Us[0].astype(np.float64), ora["U"]) <= U_TOL
 
 
+# ---------------------------------------------------------------- independent layers
+_INDEP = [  # (d_out, d_in, n_tok, w dtype, x dtype)
+    (96, 256, 2048, "bf16", "bf16"), (200, 384, 4096, "f32", "bf16"), (64, 640, 3000, "bf16", "f16"),
+    (130, 1000, 2500, "bf16", "bf16"), (33, 130, 777, "f32", "f32"), (300, 512, 1024, "bf16", "bf16"),
+    (8, 64, 100, "bf16", "bf16"), (40, 2100, 4200, "bf16", "bf16"), (128, 256, 512, "f16", "f16"),
+]
+
+
+def _indep_inputs(torch, k, m, d, n_tok, wdt, xdt):
+    rng = np.random.default_rng(1000 + k)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    W = torch.from_numpy((rng.standard_normal((m, d)) * 0.02).astype(np.float32)).to(tdt[wdt]).cuda()
+    x = rng.standard_normal((n_tok, d)).astype(np.float32)
+    x[:, rng.choice(d, max(1, d // 64), replace=False)] *= 12.0
+    if k % 3 == 1:
+        x += 1.5   # a shared channel mean: the fp64 leading panel runs for this layer
+    return W, torch.from_numpy(x).to(tdt[xdt]).cuda()
+
+
+@pytest.mark.parametrize("act", [False, True])
+def test_independent_layers_match_separate_calls(act):
+    """Nine layers with their own inputs, shapes and dtypes run concurrently
+    (more layers than the library's streams): every output is bitwise what
+    hessian_accumulate + prepare_hinv + quantize_layer give for that layer
+    alone, and one layer is checked against the oracle as well."""
+    torch = torch_mod()
+    g = gq()
+    p = g.GPTQParams(act_order=act)
+    layers = [_indep_inputs(torch, k, *spec) for k, spec in enumerate(_INDEP)]
+    res = g.quantize_independent(layers, p)
+    torch.cuda.synchronize()
+    for k, ((W, X), (q, prep, Hd)) in enumerate(zip(layers, res)):
+        d = W.shape[1]
+        H = torch.zeros(d, d, dtype=torch.float32, device="cuda")
+        g.hessian_accumulate(H, X)
+        pr = g.prepare_hinv(H, p)
+        qq = g.quantize_layer(W, pr, p)
+        torch.cuda.synchronize()
+        pairs = [(Hd, H, "H_d"), (prep.U, pr.U, "U"), (prep.dead, pr.dead, "dead"),
+                 (q.qweight, qq.qweight, "qweight"), (q.scales, qq.scales, "scales"),
+                 (q.zeros, qq.zeros, "zeros"), (q.W_hat, qq.W_hat, "W_hat"),
+                 (q.g_idx, qq.g_idx, "g_idx"), (q.row_loss, qq.row_loss, "row_loss")]
+        if act:
+            pairs.append((prep.perm, pr.perm, "perm"))
+        for a, b, name in pairs:
+            assert torch.equal(a, b), (k, _INDEP[k], name)
+    # one layer against the oracle (the separate path's own parity tests cover the rest)
+    W, X = layers[3]
+    q, prep, _ = res[3]
+    H_ex = oracle.hessian(X.float().cpu().numpy(), "f32")
+    ora = oracle.prepare(H_ex, p.percdamp, act, perm=prep.perm.cpu().numpy().astype(np.int64) if act else None)
+    assert rel_fro(prep.U.cpu().numpy().astype(np.float64), ora["U"]) <= U_TOL
+    log(f"INDEPENDENT act={act}: {len(layers)} layers bitwise equal to separate calls")
+
+
+def test_independent_layers_report_a_failed_factorization():
+    """A layer whose Hessian holds NaN (natural order) fails its factorization:
+    the call raises for it and the other layers' outputs are still those of
+    separate calls."""
+    torch = torch_mod()
+    g = gq()
+    p = g.GPTQParams()
+    layers = [_indep_inputs(torch, k, *_INDEP[k]) for k in (0, 3, 5)]
+    Xbad = layers[1][1].clone()
+    Xbad[7, 11] = float("nan")
+    layers[1] = (layers[1][0], Xbad)
+    with pytest.raises(g.NotPositiveDefinite) as e:
+        g.quantize_independent(layers, p)
+    assert e.value.statuses == [g._native.OK, g._native.ERR_NOT_SPD, g._native.OK]
+    torch.cuda.synchronize()
+    for k in (0, 2):
+        (W, X), (q, prep, Hd) = layers[k], e.value.results[k]
+        d = W.shape[1]
+        H = torch.zeros(d, d, dtype=torch.float32, device="cuda")
+        g.hessian_accumulate(H, X)
+        qq = g.quantize_layer(W, g.prepare_hinv(H, p), p)
+        torch.cuda.synchronize()
+        assert torch.equal(q.qweight, qq.qweight) and torch.equal(q.scales, qq.scales)
+
+
 @pytest.mark.parametrize("bits,g,d", [(3, 128, 333), (3, 128, 1024), (2, 64, 200), (4, 128, 257),
                                       (8, 128, 300), (3, -1, 97)])
 def test_export_dense_codes_and_half_metadata(bits, g, d):
