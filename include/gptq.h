@@ -249,7 +249,7 @@ typedef struct {
 /* Independent layers -- each with its own inputs X, hence its own H and
  * factor -- quantized concurrently ("Foundations", The Layer-Wise
  * Reconstruction Problem: every layer is its own problem; "GPTQ" technology
- * card, Parallelism: layers can be processed in parallel).  For every job:
+ * card, Parallelism: layers can be processed independently).  For every job:
  * H += 2·XᵀX, the preparation of gptq_prepare_hinv, then gptq_quantize_layer
  * with that factor.  Jobs run on streams of the library's own (default
  * priority), forked from `stream` and joined back into it, so small layers
