@@ -945,7 +945,14 @@ __global__ __launch_bounds__(256) void chol_step_kernel(PanelArgs p, int nP, Til
   const int L = blockIdx.x;
   if (L < nP) panel_body(p, L, smem);
   else if (L < nP + nj.count) run_near_tile(nj, L - nP, smem);
-  else run_far_tile(fj, (L - nP - nj.count) >> 2, (L - nP - nj.count) & 3, smem);
+  else {
+    // Workgroup L runs on XCD L % 8: in every run of 32 far workgroups the
+    // four quarters of a task sit 8 apart, on one XCD, so the L rows they
+    // share come through one L2 (the last, partial run keeps index order).
+    const int f = L - nP - nj.count, b = f >> 5;
+    if (8 * b + 8 <= fj.count) run_far_tile(fj, 8 * b + (f & 7), (f & 31) >> 3, smem);
+    else run_far_tile(fj, f >> 2, f & 3, smem);
+  }
 }
 
 // U[a][b] = Linv[d-1-a][d-1-b] for b >= a, 0 below the diagonal; four
