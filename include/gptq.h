@@ -263,7 +263,9 @@ typedef struct {
  * first failed job (its `status` and `info` fields, like every job's, say
  * which); a failed job's outputs are undefined, the others' are valid.
  * Argument errors are found before anything is enqueued (no job runs then,
- * and no status field is written). */
+ * and no status field is written); after GPTQ_ERR_HIP, work enqueued before
+ * the failure may still run.  Every job's pointers must be on the current
+ * device. */
 int gptq_quantize_independent(int n_jobs, gptq_layer_job* jobs, const gptq_params* p,
                               gptq_stream stream);
 

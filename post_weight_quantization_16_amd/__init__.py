@@ -306,17 +306,22 @@ def quantize_independent(layers, params: GPTQParams, want_what: bool = True, ws=
     torch = _torch()
     if not layers:
         raise ValueError("no layers")
+    if ws is not None and len(ws) != len(layers):
+        raise ValueError("ws must hold one workspace per layer")
     L = _native.lib()
     p = params.c()
     cpw = 8 if params.bits <= 4 else 4
     jobs = (_native.LayerJob * len(layers))()
     out, keep = [], []
+    dev0 = layers[0][0].device
     for i, (W, X) in enumerate(layers):
         _matrix_rows(W, f"W[{i}]")
         _matrix_rows(X, f"X[{i}]")
         m, d = W.shape
         n_tok = X.shape[0]
         dev = W.device
+        if dev != dev0:
+            raise ValueError(f"W[{i}] is on {dev}; every layer must live on {dev0}")
         if X.shape[1] != d or X.device != dev:
             raise ValueError(f"X[{i}] must have {d} columns and live on {dev}")
         ng = params.n_groups(d)
@@ -342,8 +347,8 @@ def quantize_independent(layers, params: GPTQParams, want_what: bool = True, ws=
             _dev(q.zeros, "zeros"), _dev(q.W_hat, "W_hat"), _dev(q.g_idx, "g_idx"),
             _dev(q.row_loss, "row_loss"), _dev(w, "ws"), w.numel(), 0, 0, -1)
         out.append((q, prep, H))
-    rc = L.gptq_quantize_independent(len(layers), jobs, ctypes.byref(p),
-                                     _stream(layers[0][0].device))
+    with _torch().cuda.device(dev0):   # the library runs the jobs on the current device
+        rc = L.gptq_quantize_independent(len(layers), jobs, ctypes.byref(p), _stream(dev0))
     if rc != _native.OK:
         if rc == _native.ERR_NOT_SPD:
             bad = next(j for j in jobs if j.status == _native.ERR_NOT_SPD)
