@@ -345,14 +345,18 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
+        # the preparation is queued without its wait (its status is checked
+        # once the quantization is queued behind it), so the GPU never idles
+        # between the stages
         H.zero_()
         if ev: ev[0].record(stream)
         gq.hessian_accumulate(H, X, ws=ws_h)
         if ev: ev[1].record(stream)
-        prep = gq.prepare_hinv(H, params, ws=ws_p)
+        prep = gq.prepare_hinv(H, params, ws=ws_p, sync=False)
         if ev: ev[2].record(stream)
         out = gq.quantize_layer(W, prep, params, ws=ws_q)
         if ev: ev[3].record(stream)
+        prep.check()
         return out
 
     for _ in range(args.warmup):

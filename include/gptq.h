@@ -153,6 +153,32 @@ int gptq_prepare_hinv(float* H, int64_t d_in, const gptq_params* p, float* U,
                       int32_t* perm, uint8_t* dead_mask, void* ws, size_t ws_bytes,
                       int64_t* info, gptq_stream stream);
 
+/* gptq_prepare_hinv without its wait ("Foundations", Cholesky Decomposition
+ * and Pre-computation; the computation is the same, bit for bit): the call
+ * returns once the work is enqueued, so a pipeline can queue the
+ * quantization (and the next layer's work) right behind it and look at the
+ * outcome later, instead of leaving the GPU idle while the host reads it.
+ *  status   host, out: 2 int32 status words, written asynchronously on
+ *           `stream` after the factorization.  Use pinned memory
+ *           (hipHostMalloc) so the copy does not block the host; read the
+ *           words only once the stream, or an event recorded on it after
+ *           this call, has completed, and decode them with
+ *           gptq_prepare_status.  They must stay valid until then.
+ *  Other arguments as for gptq_prepare_hinv (no info).
+ * Returns argument errors and GPTQ_ERR_HIP only; the factorization's own
+ * outcome (GPTQ_ERR_NOT_SPD, GPTQ_ERR_INTERNAL) is in `status`, and until it
+ * has been checked U must be treated as possibly undefined.  The workspace
+ * may be reused as soon as the words have been copied (stream order). */
+int gptq_prepare_hinv_async(float* H, int64_t d_in, const gptq_params* p, float* U,
+                            int32_t* perm, uint8_t* dead_mask, void* ws, size_t ws_bytes,
+                            int32_t* status, gptq_stream stream);
+
+/* What gptq_prepare_hinv would have returned, from the status words that
+ * gptq_prepare_hinv_async copied out (host only, no HIP call).
+ *  status  host, in: the 2 words.   info  host, out (may be NULL): as for
+ *  gptq_prepare_hinv. */
+int gptq_prepare_status(const int32_t* status, int64_t d_in, int64_t* info);
+
 /* Quantize the layer ("Foundations": The GPTQ Algorithmic Innovations 1-3,
  * walkthrough step 3, Quantization Formats and Group Size; "INT4 and GPTQ
  * Quantization": Group Quantization).  Columns are taken in the order perm;

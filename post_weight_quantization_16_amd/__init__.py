@@ -62,6 +62,23 @@ class Prepared:
     perm: "object"     # [d] int32 quantization order
     dead: "object"     # [d] uint8 dead-channel mask (original order)
     natural: bool = False   # perm is the identity (prepared without act-order)
+    status: "object" = None   # prepare_hinv(sync=False): pinned host status words
+    event: "object" = None    # ... and the event recorded after their copy
+
+    def check(self) -> "Prepared":
+        """For prepare_hinv(sync=False): wait for the status words and raise
+        as prepare_hinv would have; a no-op for a synchronous preparation."""
+        if self.status is None:
+            return self
+        self.event.synchronize()
+        info = ctypes.c_int64(-1)
+        rc = _native.lib().gptq_prepare_status(ctypes.c_void_p(self.status.data_ptr()),
+                                               self.U.shape[0], ctypes.byref(info))
+        if rc == _native.ERR_NOT_SPD:
+            raise NotPositiveDefinite(rc, _native.last_error(), info.value)
+        _check(rc)
+        self.status = self.event = None
+        return self
 
 
 @dataclasses.dataclass
@@ -179,8 +196,12 @@ def hessian_accumulate_noalloc(H, X):
     return H
 
 
-def prepare_hinv(H, params: GPTQParams, ws=None) -> Prepared:
-    """Dead fix, damping, act-order and U (H is overwritten with H_d)."""
+def prepare_hinv(H, params: GPTQParams, ws=None, sync: bool = True) -> Prepared:
+    """Dead fix, damping, act-order and U (H is overwritten with H_d).
+
+    sync=False returns at once (gptq_prepare_hinv_async): the work, and the
+    quantization queued behind it, run while the host goes on; call
+    ``Prepared.check()`` later for the factorization's outcome."""
     torch = _torch()
     if H.dim() != 2:
         raise ValueError("H must be a square matrix")
@@ -195,6 +216,15 @@ def prepare_hinv(H, params: GPTQParams, ws=None) -> Prepared:
     if ws is None:
         ws = _workspace(L.gptq_workspace_bytes(_native.WS_PREPARE, 0, d, 0, ctypes.byref(p)), dev)
     _ws_check(ws, dev)
+    if not sync:
+        status = torch.empty(2, dtype=torch.int32, pin_memory=True)
+        _check(L.gptq_prepare_hinv_async(_dev(H, "H"), d, ctypes.byref(p), _dev(U, "U"),
+                                         _dev(perm, "perm"), _dev(dead, "dead"), _dev(ws, "ws"),
+                                         ws.numel(), ctypes.c_void_p(status.data_ptr()),
+                                         _stream(dev)))
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream(dev))
+        return Prepared(U, perm, dead, natural=not params.act_order, status=status, event=ev)
     info = ctypes.c_int64(-1)
     rc = L.gptq_prepare_hinv(_dev(H, "H"), d, ctypes.byref(p), _dev(U, "U"), _dev(perm, "perm"),
                              _dev(dead, "dead"), _dev(ws, "ws"), ws.numel(), ctypes.byref(info),

@@ -22,6 +22,8 @@ EXPORTS = (
     "gptq_hessian_accumulate",
     "gptq_hessian_accumulate_noalloc",
     "gptq_prepare_hinv",
+    "gptq_prepare_hinv_async",
+    "gptq_prepare_status",
     "gptq_quantize_layer",
     "gptq_quantize_layers",
     "gptq_quantize_independent",
@@ -121,6 +123,10 @@ def lib() -> ctypes.CDLL:
     L.gptq_prepare_hinv.argtypes = [_vp, _i64, _pp, _vp, _vp, _vp, _vp, _sz,
                                     ctypes.POINTER(ctypes.c_int64), _vp]
     L.gptq_prepare_hinv.restype = _int
+    L.gptq_prepare_hinv_async.argtypes = [_vp, _i64, _pp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
+    L.gptq_prepare_hinv_async.restype = _int
+    L.gptq_prepare_status.argtypes = [_vp, _i64, ctypes.POINTER(ctypes.c_int64)]
+    L.gptq_prepare_status.restype = _int
     L.gptq_quantize_layer.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _pp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     L.gptq_quantize_layer.restype = _int

@@ -118,6 +118,43 @@ JobStreams* job_streams(int dev) {
 
 }  // namespace
 
+namespace {
+// Checks and enqueues the preparation; status_dev receives the device
+// address of its two status words.
+int prepare_enqueue(float* H, int64_t d_in, const gptq_params* p, float* U, int32_t* perm,
+                    uint8_t* dead_mask, void* ws, size_t ws_bytes, int32_t** status_dev,
+                    hipStream_t s) {
+  if (!H || !U) return fail(GPTQ_ERR_INVALID_ARG, "H and U must not be NULL");
+  if (d_in <= 0 || d_in > kMaxDin)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld]", (long long)kMaxDin);
+  int rc = check_params(p, d_in);
+  if (rc) return rc;
+  if (p->act_order && !perm) return fail(GPTQ_ERR_INVALID_ARG, "act_order needs a perm output");
+  rc = check_ws(ws, ws_bytes, gq::prepare_ws_bytes(d_in), "prepare_hinv");
+  if (rc) return rc;
+  hipError_t e = gq::prepare_launch(H, d_in, p->percdamp, p->act_order, U, perm, dead_mask, ws,
+                                    status_dev, s);
+  if (e != hipSuccess) return hip_fail("prepare_hinv", e);
+  return GPTQ_OK;
+}
+
+int status_result(const int32_t* st, int64_t d_in, int64_t* info) {
+  int64_t piv = -1;
+  const int rc = gq::prepare_status(st[0], st[1], d_in, &piv);
+  if (info) *info = piv;
+  if (rc == GPTQ_ERR_NOT_SPD)
+    return fail(GPTQ_ERR_NOT_SPD,
+                "damped Hessian is not positive definite (pivot %lld of the quantization order); "
+                "raise percdamp",
+                (long long)piv);
+  if (rc != GPTQ_OK)
+    return fail(rc, "prepare_hinv: a factorization wave ran out of its bounded wait for "
+                    "another wave (status words %d, %d); the outputs are undefined",
+                (int)st[0], (int)st[1]);
+  return GPTQ_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* gptq_last_error(void) { return g_err.c_str(); }
@@ -200,36 +237,36 @@ int gptq_prepare_hinv(float* H, int64_t d_in, const gptq_params* p, float* U, in
                       uint8_t* dead_mask, void* ws, size_t ws_bytes, int64_t* info,
                       gptq_stream stream) {
   if (info) *info = -1;
-  if (!H || !U) return fail(GPTQ_ERR_INVALID_ARG, "H and U must not be NULL");
-  if (d_in <= 0 || d_in > kMaxDin)
-    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld]", (long long)kMaxDin);
-  int rc = check_params(p, d_in);
-  if (rc) return rc;
-  if (p->act_order && !perm) return fail(GPTQ_ERR_INVALID_ARG, "act_order needs a perm output");
-  rc = check_ws(ws, ws_bytes, gq::prepare_ws_bytes(d_in), "prepare_hinv");
-  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   int32_t* status_dev = nullptr;
-  hipError_t e = gq::prepare_launch(H, d_in, p->percdamp, p->act_order, U, perm, dead_mask, ws,
-                                    &status_dev, s);
-  if (e != hipSuccess) return hip_fail("prepare_hinv", e);
+  int rc = prepare_enqueue(H, d_in, p, U, perm, dead_mask, ws, ws_bytes, &status_dev, s);
+  if (rc) return rc;
   int32_t st[2] = {0, 0};   // failing pivot (or INT_MAX), stall flag
-  e = hipMemcpyAsync(st, status_dev, sizeof st, hipMemcpyDeviceToHost, s);
+  hipError_t e = hipMemcpyAsync(st, status_dev, sizeof st, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail("prepare_hinv (status read-back)", e);
-  int64_t piv = -1;
-  rc = gq::prepare_status(st[0], st[1], d_in, &piv);
-  if (info) *info = piv;
-  if (rc == GPTQ_ERR_NOT_SPD)
-    return fail(GPTQ_ERR_NOT_SPD,
-                "damped Hessian is not positive definite (pivot %lld of the quantization order); "
-                "raise percdamp",
-                (long long)piv);
-  if (rc != GPTQ_OK)
-    return fail(rc, "prepare_hinv: a factorization wave ran out of its bounded wait for "
-                    "another wave (status words %d, %d); the outputs are undefined",
-                (int)st[0], (int)st[1]);
+  return status_result(st, d_in, info);
+}
+
+int gptq_prepare_hinv_async(float* H, int64_t d_in, const gptq_params* p, float* U,
+                            int32_t* perm, uint8_t* dead_mask, void* ws, size_t ws_bytes,
+                            int32_t* status, gptq_stream stream) {
+  if (!status) return fail(GPTQ_ERR_INVALID_ARG, "status must not be NULL");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* status_dev = nullptr;
+  int rc = prepare_enqueue(H, d_in, p, U, perm, dead_mask, ws, ws_bytes, &status_dev, s);
+  if (rc) return rc;
+  hipError_t e = hipMemcpyAsync(status, status_dev, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail("prepare_hinv_async (status copy)", e);
   return GPTQ_OK;
+}
+
+int gptq_prepare_status(const int32_t* status, int64_t d_in, int64_t* info) {
+  if (info) *info = -1;
+  if (!status) return fail(GPTQ_ERR_INVALID_ARG, "status must not be NULL");
+  if (d_in <= 0 || d_in > kMaxDin)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld]", (long long)kMaxDin);
+  return status_result(status, d_in, info);
 }
 
 int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,

@@ -325,3 +325,27 @@ def test_w4a16_validation():
     assert need >= 64 * 64 * 4 * 2
     assert f(*ok(M=64, K=1024, lda=1024, ng=8, ws=FAKE, ws_bytes=need - 4)) == n.ERR_WORKSPACE
     assert L.gptq_workspace_bytes(n.WS_W4A16, 64, 256, 0, None) == 0
+
+
+def test_async_prepare_validation_and_status_decoding():
+    """The asynchronous preparation checks its arguments like the synchronous
+    one (and needs the host status words); the decoder maps the two words to
+    the synchronous call's result without touching the device."""
+    L = n.lib()
+    p = _params()
+    st = (ctypes.c_int32 * 2)()
+    pa = L.gptq_prepare_hinv_async
+    assert pa(FAKE, 64, ctypes.byref(p), FAKE, FAKE, None, FAKE, 1 << 40, None, None) == n.ERR_INVALID_ARG
+    assert pa(None, 64, ctypes.byref(p), FAKE, FAKE, None, FAKE, 1 << 40, st, None) == n.ERR_INVALID_ARG
+    assert pa(FAKE, 64, ctypes.byref(_params(act_order=1)), FAKE, None, None, FAKE, 1 << 40, st,
+              None) == n.ERR_INVALID_ARG
+    assert pa(FAKE, 64, ctypes.byref(p), FAKE, FAKE, None, FAKE, 8, st, None) == n.ERR_WORKSPACE
+    dec = L.gptq_prepare_status
+    info = ctypes.c_int64(7)
+    words = lambda a, b: (ctypes.c_int32 * 2)(a, b)
+    assert dec(words(2**31 - 1, 0), 100, ctypes.byref(info)) == n.OK and info.value == -1
+    assert dec(words(5, 0), 100, ctypes.byref(info)) == n.ERR_NOT_SPD and info.value == 94
+    assert dec(words(2**31 - 1, 1), 100, ctypes.byref(info)) == n.ERR_INTERNAL and info.value == -1
+    assert dec(words(100, 0), 100, None) == n.ERR_INTERNAL      # no such pivot
+    assert dec(None, 100, None) == n.ERR_INVALID_ARG
+    assert dec(words(0, 0), 0, None) == n.ERR_INVALID_ARG

@@ -369,6 +369,41 @@ def test_prepare_repeated_with_reused_workspace():
     assert rel_fro(Us[0].astype(np.float64), ora["U"]) <= U_TOL
 
 
+@pytest.mark.parametrize("act", [False, True])
+def test_async_prepare_matches_prepare(act):
+    """gptq_prepare_hinv_async queues the same work without waiting: the
+    factor, H_d and the quantization queued right behind it are bitwise those
+    of the synchronous call, and the status words decode to OK."""
+    torch = torch_mod()
+    g = gq()
+    wl = synth.WORKLOADS["llama7b-attn"].scaled(d_out=192, d_in=1500, n_tok=6000, act_order=act)
+    W, X = _inputs(wl)
+    p = g.GPTQParams(act_order=act)
+    H0 = torch.from_numpy(oracle.hessian(X, "bf16").astype(np.float32)).cuda()
+    Wd = to_dev(W, wl.w_dtype)
+    Ha, Hs = H0.clone(), H0.clone()
+    pa = g.prepare_hinv(Ha, p, sync=False)
+    qa = g.quantize_layer(Wd, pa, p)
+    pa.check()
+    ps = g.prepare_hinv(Hs, p)
+    qs = g.quantize_layer(Wd, ps, p)
+    torch.cuda.synchronize()
+    assert pa.status is None
+    for a, b in [(Ha, Hs), (pa.U, ps.U), (pa.perm, ps.perm), (pa.dead, ps.dead), (qa.qweight, qs.qweight),
+                 (qa.scales, qs.scales), (qa.zeros, qs.zeros), (qa.W_hat, qs.W_hat)]:
+        assert torch.equal(a, b)
+
+
+def test_async_prepare_reports_not_positive_definite():
+    torch = torch_mod()
+    g = gq()
+    H = torch.from_numpy(np.diag(np.r_[np.ones(50), -5.0, np.ones(49)]).astype(np.float32)).cuda()
+    prep = g.prepare_hinv(H, g.GPTQParams(percdamp=0.0), sync=False)
+    with pytest.raises(g.NotPositiveDefinite) as e:
+        prep.check()
+    assert 0 <= e.value.pivot < 100
+
+
 # ---------------------------------------------------------------- independent layers
 _INDEP = [  # (d_out, d_in, n_tok, w dtype, x dtype)
     (96, 256, 2048, "bf16", "bf16"), (200, 384, 4096, "f32", "bf16"), (64, 640, 3000, "bf16", "f16"),
