@@ -128,6 +128,15 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
 int gptq_hessian_accumulate_noalloc(float* H, int64_t d_in, const void* X, int x_dtype,
                                     int64_t n_tok, int64_t ld_x, gptq_stream stream);
 
+/* H = 2·Xᵀ·X: gptq_hessian_accumulate for a Hessian started from zero, in one
+ * call ("Foundations", Second-Order Taylor Expansion and the Hessian).  H is
+ * only written (the accumulating call reads it too); the arithmetic of every
+ * element is that of gptq_hessian_accumulate on a zeroed H, bit for bit.
+ * n_tok == 0 sets H to zeros (X may then be NULL).  Arguments, workspace and
+ * errors as for gptq_hessian_accumulate.  Asynchronous. */
+int gptq_hessian(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tok, int64_t ld_x,
+                 void* ws, size_t ws_bytes, gptq_stream stream);
+
 /* Prepare the inverse-Hessian factor ("Foundations": walkthrough steps 1-2,
  * Hessian Damping, Activation Ordering, Cholesky Decomposition):
  *   dead_i = (H_ii == 0) -> H_ii := 1;  λ = percdamp·mean(diag H);

@@ -182,6 +182,23 @@ def hessian_accumulate(H, X, ws=None):
     return H
 
 
+def hessian(H, X, ws=None):
+    """H = 2·XᵀX (X token-major [n_tok, d_in]): hessian_accumulate on a zeroed
+    H in one call, without reading H."""
+    torch = _torch()
+    _matrix_rows(X, "X")
+    n_tok, d = X.shape
+    xdt = _dtype_code(X)
+    _require(H, "H", torch.float32, (d, d), X.device)
+    L = _native.lib()
+    if ws is None:
+        ws = _workspace(L.gptq_workspace_bytes(_native.WS_HESSIAN, 0, d, n_tok, None), X.device)
+    _ws_check(ws, X.device)
+    _check(L.gptq_hessian(_dev(H, "H"), d, _dev(X, "X"), xdt, n_tok, X.stride(0), _dev(ws, "ws"),
+                          ws.numel(), _stream(X.device)))
+    return H
+
+
 def hessian_accumulate_noalloc(H, X):
     """H += 2·XᵀX without a workspace: the library's static device scratch
     (for callers that cannot allocate; d_in <= 4096; calls that overlap on

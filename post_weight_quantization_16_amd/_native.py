@@ -20,6 +20,7 @@ WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_OBQ, WS_W4A16, WS_LAYER = 0, 1, 2, 3, 4,
 EXPORTS = (
     "gptq_workspace_bytes",
     "gptq_hessian_accumulate",
+    "gptq_hessian",
     "gptq_hessian_accumulate_noalloc",
     "gptq_prepare_hinv",
     "gptq_prepare_hinv_async",
@@ -118,6 +119,8 @@ def lib() -> ctypes.CDLL:
     L.gptq_workspace_bytes.restype = _sz
     L.gptq_hessian_accumulate.argtypes = [_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp]
     L.gptq_hessian_accumulate.restype = _int
+    L.gptq_hessian.argtypes = [_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp]
+    L.gptq_hessian.restype = _int
     L.gptq_hessian_accumulate_noalloc.argtypes = [_vp, _i64, _vp, _int, _i64, _i64, _vp]
     L.gptq_hessian_accumulate_noalloc.restype = _int
     L.gptq_prepare_hinv.argtypes = [_vp, _i64, _pp, _vp, _vp, _vp, _vp, _sz,

@@ -155,6 +155,37 @@ int status_result(const int32_t* st, int64_t d_in, int64_t* info) {
 }
 }  // namespace
 
+namespace {
+int hessian_call(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tok, int64_t ld_x,
+                 void* ws, size_t ws_bytes, gptq_stream stream, bool overwrite) {
+  if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
+  if (d_in <= 0 || d_in > kMaxDin)
+    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld] (got %lld)", (long long)kMaxDin,
+                (long long)d_in);
+  if (n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "n_tok must be >= 0");
+  if (!valid_dtype(x_dtype)) return fail(GPTQ_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
+  if (n_tok == 0 && !overwrite) return GPTQ_OK;
+  if (n_tok == 0) {   // H = 0
+    const hipError_t e = gq::hessian_launch(H, d_in, nullptr, x_dtype, 0, d_in, nullptr, 0,
+                                            (hipStream_t)stream, true);
+    return e == hipSuccess ? GPTQ_OK : hip_fail("hessian", e);
+  }
+  if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
+  if (ld_x < d_in) return fail(GPTQ_ERR_INVALID_ARG, "ld_x (%lld) < d_in (%lld)", (long long)ld_x,
+                               (long long)d_in);
+  int rc = check_ws(ws, ws_bytes, gq::hessian_ws_bytes(d_in, n_tok), "hessian_accumulate");
+  if (rc) return rc;
+  hipError_t e;
+  {
+    gq::TimerScope ts(gq::kTimerHessian, (hipStream_t)stream);
+    e = gq::hessian_launch(H, d_in, X, x_dtype, n_tok, ld_x, ws, ws_bytes, (hipStream_t)stream,
+                           overwrite);
+  }
+  if (e != hipSuccess) return hip_fail("hessian_accumulate", e);
+  return GPTQ_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* gptq_last_error(void) { return g_err.c_str(); }
@@ -190,25 +221,12 @@ size_t gptq_workspace_bytes(int which, int64_t d_out, int64_t d_in, int64_t n_to
 
 int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tok,
                             int64_t ld_x, void* ws, size_t ws_bytes, gptq_stream stream) {
-  if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
-  if (d_in <= 0 || d_in > kMaxDin)
-    return fail(GPTQ_ERR_INVALID_ARG, "d_in must be in [1, %lld] (got %lld)", (long long)kMaxDin,
-                (long long)d_in);
-  if (n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "n_tok must be >= 0");
-  if (!valid_dtype(x_dtype)) return fail(GPTQ_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
-  if (n_tok == 0) return GPTQ_OK;
-  if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
-  if (ld_x < d_in) return fail(GPTQ_ERR_INVALID_ARG, "ld_x (%lld) < d_in (%lld)", (long long)ld_x,
-                               (long long)d_in);
-  int rc = check_ws(ws, ws_bytes, gq::hessian_ws_bytes(d_in, n_tok), "hessian_accumulate");
-  if (rc) return rc;
-  hipError_t e;
-  {
-    gq::TimerScope ts(gq::kTimerHessian, (hipStream_t)stream);
-    e = gq::hessian_launch(H, d_in, X, x_dtype, n_tok, ld_x, ws, ws_bytes, (hipStream_t)stream);
-  }
-  if (e != hipSuccess) return hip_fail("hessian_accumulate", e);
-  return GPTQ_OK;
+  return hessian_call(H, d_in, X, x_dtype, n_tok, ld_x, ws, ws_bytes, stream, false);
+}
+
+int gptq_hessian(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tok, int64_t ld_x,
+                 void* ws, size_t ws_bytes, gptq_stream stream) {
+  return hessian_call(H, d_in, X, x_dtype, n_tok, ld_x, ws, ws_bytes, stream, true);
 }
 
 int gptq_hessian_accumulate_noalloc(float* H, int64_t d_in, const void* X, int x_dtype,

@@ -69,8 +69,10 @@ int hessian_splits(int64_t d, int64_t n_tok);
 size_t hessian_ws_bytes(int64_t d, int64_t n_tok);
 // smallest workspace the Hessian runs with (one partial Hessian)
 size_t hessian_min_ws_bytes(int64_t d);
+// overwrite: H = 2·XᵀX instead of H += 2·XᵀX (H is not read)
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
-                          int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s);
+                          int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s,
+                          bool overwrite = false);
 // the same with the library's static device scratch as the workspace (no
 // allocation); ERR: hipErrorInvalidValue when d needs more than it holds
 constexpr size_t kScratchBytes = (size_t)65 << 20;

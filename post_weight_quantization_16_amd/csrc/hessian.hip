@@ -568,12 +568,19 @@ __global__ __launch_bounds__(64) void zero_chunk_kernel(uint32_t* __restrict__ z
 // trip); the finished strip goes through LDS to be written transposed, so
 // both writes are coalesced.
 constexpr int RS = 32;   // strip rows
+
+// H = 0 (d² floats), for a Hessian set from no tokens.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ H, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    H[i] = 0.f;
+}
 template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ H, int d,
                                                             const float* __restrict__ P,
                                                             int64_t dp, ReducePlan rp, int nt,
                                                             int vec_h,
-                                                            const uint16_t* __restrict__ mu) {
+                                                            const uint16_t* __restrict__ mu,
+                                                            int acc_h) {
   int ti, tj;
   tile_of(blockIdx.x >> 2, nt, ti, tj);
   const bool hi = reduce_tile_hi(rp, ti, tj);
@@ -630,7 +637,8 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
 #pragma unroll
     for (int it = 0; it < NR; ++it) {
       const int e = t + 256 * it, a = e >> 5, b4 = (e & 31) * 4;
-      h[it] = *reinterpret_cast<const f32x4*>(H + (int64_t)(i0 + a) * d + tj * HT + b4);
+      h[it] = acc_h ? *reinterpret_cast<const f32x4*>(H + (int64_t)(i0 + a) * d + tj * HT + b4)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int it = 0; it < NR; ++it) {
@@ -650,7 +658,7 @@ __global__ __launch_bounds__(256) void reduce_mirror_kernel(float* __restrict__ 
         const int jq = tj * HT + b4 + q;
         float v = 0.f;
         if (i < d && jq < d && jq >= i) {
-          v = (float)fma(2.0, acc[it][q], (double)H[(int64_t)i * d + jq]);
+          v = (float)fma(2.0, acc[it][q], acc_h ? (double)H[(int64_t)i * d + jq] : 0.0);
           H[(int64_t)i * d + jq] = v;
         }
         T[a][b4 + q] = v;
@@ -728,8 +736,14 @@ size_t hessian_min_ws_bytes(int64_t d) {
 // Workspace layout: S partial Hessians (S as the path wants, at most what
 // ws_bytes holds), then μ (dp 16-bit values), then the 256-byte zero chunk.
 hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
-                          int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (n_tok <= 0) return hipSuccess;
+                          int64_t ld_x, void* ws, size_t ws_bytes, hipStream_t s, bool overwrite) {
+  if (n_tok <= 0) {
+    if (overwrite) {   // H = 2·XᵀX over no tokens: zeros (a fill kernel, no memset)
+      fill_zero_kernel<<<(unsigned)std::min<int64_t>(ceil_div(d * d, 1024), 4096), 256, 0, s>>>(H, d * d);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
   const int64_t dp = ceil_div(d, FT) * FT;   // partial Hessians are dp x dp
   float* P = static_cast<float*>(ws);
   const size_t part = (size_t)dp * dp * 4;
@@ -815,9 +829,11 @@ hipError_t hessian_launch(float* H, int64_t d, const void* X, int x_dtype, int64
   const uint16_t* mu_r = x_dtype == GPTQ_F32 ? nullptr : mu;
   rp.shift_lo = shift_tok;
   if (bf || x_dtype == GPTQ_F32)
-    reduce_mirror_kernel<true><<<gr, 256, 0, s>>>(H, (int)d, P, dp, rp, nt128, vec_h, mu_r);
+    reduce_mirror_kernel<true><<<gr, 256, 0, s>>>(H, (int)d, P, dp, rp, nt128, vec_h, mu_r,
+                                                  overwrite ? 0 : 1);
   else
-    reduce_mirror_kernel<false><<<gr, 256, 0, s>>>(H, (int)d, P, dp, rp, nt128, vec_h, mu_r);
+    reduce_mirror_kernel<false><<<gr, 256, 0, s>>>(H, (int)d, P, dp, rp, nt128, vec_h, mu_r,
+                                                   overwrite ? 0 : 1);
   return hipGetLastError();
 }
 

@@ -164,6 +164,15 @@ def test_hessian_validation():
     assert acc(FAKE, 64, FAKE, n.BF16, 10, 64, FAKE, 16, None) == n.ERR_WORKSPACE
     # zero tokens is a no-op that touches nothing
     assert acc(FAKE, 64, None, n.BF16, 0, 64, None, 0, None) == n.OK
+    # the setting call validates the same way (before any HIP call)
+    hs = L.gptq_hessian
+    assert hs(None, 64, FAKE, n.BF16, 10, 64, FAKE, 1 << 40, None) == n.ERR_INVALID_ARG
+    assert hs(FAKE, 0, FAKE, n.BF16, 10, 64, FAKE, 1 << 40, None) == n.ERR_INVALID_ARG
+    assert hs(FAKE, 64, FAKE, 9, 10, 64, FAKE, 1 << 40, None) == n.ERR_INVALID_ARG
+    assert hs(FAKE, 64, FAKE, n.BF16, -1, 64, FAKE, 1 << 40, None) == n.ERR_INVALID_ARG
+    assert hs(FAKE, 64, FAKE, n.BF16, 10, 32, FAKE, 1 << 40, None) == n.ERR_INVALID_ARG
+    assert hs(FAKE, 64, None, n.BF16, 10, 64, FAKE, 1 << 40, None) == n.ERR_INVALID_ARG
+    assert hs(FAKE, 64, FAKE, n.BF16, 10, 64, FAKE, 16, None) == n.ERR_WORKSPACE
 
 
 def test_prepare_validation():

@@ -63,6 +63,30 @@ def test_hessian_matches_oracle(d, n_tok, dtype, ld_pad):
         assert rel_fro(H3.cpu().numpy().astype(np.float64), H_ex) <= 1e-5
 
 
+@pytest.mark.parametrize("d,n_tok,dtype,pad", [(1024, 5000, "bf16", 0), (100, 3000, "bf16", 0),
+                                              (96, 2000, "f32", 0), (256, 4096, "f16", 8),
+                                              (512, 0, "bf16", 0)])
+def test_hessian_set_equals_zero_then_accumulate(d, n_tok, dtype, pad):
+    """gptq_hessian (H = 2·XᵀX, H not read) gives bitwise what
+    gptq_hessian_accumulate gives on a zeroed H, on the fast bf16/fp16 path,
+    the generic path (d not a multiple of 8), the fp32 path and with no
+    tokens (H becomes zeros whatever it held)."""
+    torch = torch_mod()
+    g = gq()
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    rng = np.random.default_rng(d + n_tok)
+    x = torch.from_numpy(rng.standard_normal((max(n_tok, 1), d + pad)).astype(np.float32)).to(tdt).cuda()
+    X = x[:n_tok, :d]
+    H1 = torch.full((d, d), 7.0, device="cuda")       # stale contents: must not be read
+    H2 = torch.zeros(d, d, device="cuda")
+    g.hessian(H1, X)
+    g.hessian_accumulate(H2, X)
+    torch.cuda.synchronize()
+    assert torch.equal(H1, H2)
+    if n_tok == 0:
+        assert not torch.any(H1)
+
+
 def test_hessian_of_hadamard_columns_is_exact():
     """±1 inputs: every partial sum is an exact integer in fp32."""
     torch = torch_mod()
