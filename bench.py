@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the GPTQ layer-quantization path on one MI355X.
 
-One step = the whole path for one layer: zero H, H += 2·XᵀX over all
-calibration tokens, prepare (dead fix, damping, factor U of H_d⁻¹), and the
-blocked sweep with lazy updates, packing and Ŵ.  Inputs (W, X) are synthetic,
+One step = the whole path for one layer: H = 2·XᵀX over all calibration
+tokens, prepare (dead fix, damping, factor U of H_d⁻¹), and the blocked
+sweep with lazy updates, packing and Ŵ.  Inputs (W, X) are synthetic,
 seeded, and resident in HBM before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--workload llama7b-attn]
